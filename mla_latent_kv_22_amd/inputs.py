@@ -1,0 +1,194 @@
+"""Seeded synthetic inputs for the MLA latent-cache path.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic (no projection, no RoPE, no attention).  Both the CPU
+oracle and the HIP path receive exactly the arrays built here: bf16 values are
+carried as their raw 16-bit patterns (numpy ``uint16``), fp32 values as
+``float32``.
+
+Workloads follow the shapes of the pages' running example (DeepSeek-V2/V3 MLA:
+latent width d_c = kv_lora_rank = 512, decoupled rotary key width d_R =
+qk_rope_head_dim = 64; LLMScale page, section "Multi-head latent attention
+(MLA)") and the five decode / prefill workloads this library is measured on.
+
+Draw order (fixed, one ``numpy.random.default_rng(seed)`` stream):
+  1. sequence lengths (ragged workload only)
+  2. page permutation (paged workloads only)
+  3. W_DKV, W_KR, W_UK, W_UV           ~ N(0, 0.02^2)
+  4. hidden states h                    ~ N(0, 1)
+  5. pre-written latent rows            ~ N(0, 1)   (decode-only workloads)
+  6. queries q = [q_C | q_R] per head   ~ N(0, 0.02^2 * hidden)
+The query projection W_Q.h is the caller's GEMM and sits outside the library,
+so q is drawn directly with the variance W_Q.h has under the stated init.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from typing import Dict, Optional
+
+import numpy as np
+
+PAGE_SIZE = 64
+WEIGHT_STD = 0.02
+ROPE_BASE = 10000.0
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    hidden: int
+    num_heads: int
+    d_c: int
+    d_r: int
+    qk_nope: int
+    v_head: int
+    dtype: str            # "f32" or "bf16"
+    batch: int
+    seq_len: int          # context length T (max length for ragged)
+    min_seq_len: int = 0  # >0 selects ragged lengths U{min_seq_len .. seq_len}
+    paged: bool = False   # random page permutation instead of contiguous pages
+    prefill: bool = False
+    page_size: int = PAGE_SIZE
+    rope_base: float = ROPE_BASE
+    weight_std: float = WEIGHT_STD
+
+    @property
+    def row_width(self) -> int:
+        return self.d_c + self.d_r
+
+    @property
+    def qk_head(self) -> int:
+        return self.qk_nope + self.d_r
+
+    @property
+    def softmax_scale(self) -> float:
+        # 1/sqrt of the per-head score width of the non-absorbed form.
+        return 1.0 / float(np.sqrt(self.qk_nope + self.d_r))
+
+
+TINY = Config("tiny_f32", 256, 8, 64, 16, 32, 32, "f32", 2, 256)
+V2LITE = Config("v2lite_decode", 2048, 16, 512, 64, 128, 128, "bf16", 16, 4096)
+V3 = Config("v3_decode", 7168, 128, 512, 64, 128, 128, "bf16", 64, 8192)
+RAGGED = Config("v3_paged_ragged", 7168, 128, 512, 64, 128, 128, "bf16", 128, 32768,
+                min_seq_len=512, paged=True)
+PREFILL = Config("v3_prefill", 7168, 128, 512, 64, 128, 128, "bf16", 4, 4096,
+                 paged=True, prefill=True)
+CONFIGS: Dict[str, Config] = {c.name: c for c in (TINY, V2LITE, V3, RAGGED, PREFILL)}
+
+
+def scaled(cfg: Config, **kw) -> Config:
+    """A copy of ``cfg`` with some fields replaced (smaller parity cases)."""
+    return dataclasses.replace(cfg, **kw)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even float32 -> bf16 bit pattern (storage conversion)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str, chunk: int = 1 << 24) -> np.ndarray:
+    """N(0, std^2) drawn in float32 chunks (bounded host memory), stored as dtype."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        v = rng.standard_normal(e - s, dtype=np.float32)
+        if std != 1.0:
+            v *= np.float32(std)
+        out[s:e] = _store(v, dtype)
+    return out.reshape(shape)
+
+
+def seq_lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
+    if cfg.min_seq_len > 0:
+        return rng.integers(cfg.min_seq_len, cfg.seq_len, size=cfg.batch, endpoint=True).astype(np.int32)
+    return np.full(cfg.batch, cfg.seq_len, dtype=np.int32)
+
+
+def make(cfg: Config, seed: int = 0, with_rows: bool = True) -> Dict[str, np.ndarray]:
+    """Build every input of one step of ``cfg``.
+
+    Returns a dict with:
+      seq_lens   int32 [B]          context length per sequence (decode) / tokens per sequence (prefill)
+      block_table int32 [B, max_pages]  page holding tokens i*P .. i*P+P-1 of sequence b
+      num_pages  int                pool size in pages
+      w_dkr      [R, D]             rows 0..d_c-1 = W_DKV, rows d_c..R-1 = W_KR
+      w_uk       [H, d_n, d_c]      K_C,h = W_UK,h . c
+      w_uv       [H, d_v, d_c]      V_h   = W_UV,h . c
+      h          [N, D]             hidden states of the tokens written this step
+      positions  int32 [N]          their positions
+      slots      int64 [N]          their cache slots (page * P + offset)
+      rows       [num_pages, P, R]  pre-written latent rows (decode workloads; zero rows elsewhere)
+      q          [Nq, H, d_n+d_R]   pre-RoPE queries ([q_C | q_R] per head)
+      q_positions int32 [Nq]
+    """
+    rng = np.random.default_rng(seed)
+    P = cfg.page_size
+    lens = seq_lengths(cfg, rng)
+    pages_per_seq = (lens.astype(np.int64) + P - 1) // P
+    num_pages = int(pages_per_seq.sum())
+    max_pages = int(pages_per_seq.max())
+    if cfg.paged:
+        perm = rng.permutation(num_pages).astype(np.int32)
+    else:
+        perm = np.arange(num_pages, dtype=np.int32)
+    block_table = np.zeros((cfg.batch, max_pages), dtype=np.int32)
+    start = 0
+    for b in range(cfg.batch):
+        n = int(pages_per_seq[b])
+        block_table[b, :n] = perm[start:start + n]
+        start += n
+
+    R, D, H = cfg.row_width, cfg.hidden, cfg.num_heads
+    w_dkv = _normal(rng, (cfg.d_c, D), cfg.weight_std, cfg.dtype)
+    w_kr = _normal(rng, (cfg.d_r, D), cfg.weight_std, cfg.dtype)
+    w_uk = _normal(rng, (H, cfg.qk_nope, cfg.d_c), cfg.weight_std, cfg.dtype)
+    w_uv = _normal(rng, (H, cfg.v_head, cfg.d_c), cfg.weight_std, cfg.dtype)
+    w_dkr = np.concatenate([w_dkv, w_kr], axis=0)
+
+    full_path = cfg.prefill or cfg.dtype == "f32"
+    if full_path:
+        # every context token is projected and written by the cache-write step
+        positions = np.concatenate([np.arange(int(L), dtype=np.int32) for L in lens])
+        seq_of_tok = np.repeat(np.arange(cfg.batch), lens)
+    else:
+        # decode: the newest token of each sequence is written this step
+        positions = (lens - 1).astype(np.int32)
+        seq_of_tok = np.arange(cfg.batch)
+    slots = (block_table[seq_of_tok, positions // P].astype(np.int64) * P + positions % P).astype(np.int64)
+    h = _normal(rng, (positions.shape[0], D), 1.0, cfg.dtype)
+
+    if with_rows and not full_path:
+        rows = _normal(rng, (num_pages, P, R), 1.0, cfg.dtype)
+    else:
+        rows = np.zeros((num_pages, P, R), dtype=np.uint16 if cfg.dtype == "bf16" else np.float32)
+
+    q_std = cfg.weight_std * float(np.sqrt(D))
+    if cfg.prefill:
+        q_positions = positions.copy()
+    else:
+        q_positions = (lens - 1).astype(np.int32)
+    q = _normal(rng, (q_positions.shape[0], H, cfg.qk_head), q_std, cfg.dtype)
+    cu = np.zeros(cfg.batch + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    return dict(seq_lens=lens, block_table=block_table, num_pages=num_pages, w_dkr=w_dkr,
+                w_uk=w_uk, w_uv=w_uv, h=h, positions=positions, slots=slots, rows=rows,
+                q=q, q_positions=q_positions, cu_seqlens=cu)
+
+
+def digest(arrays: Dict[str, np.ndarray]) -> str:
+    """sha256 over the raw bytes of every array (determinism check)."""
+    m = hashlib.sha256()
+    for k in sorted(arrays):
+        v = arrays[k]
+        m.update(k.encode())
+        m.update(np.ascontiguousarray(np.asarray(v)).tobytes())
+    return m.hexdigest()

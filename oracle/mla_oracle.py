@@ -1,0 +1,317 @@
+"""Plain float64 CPU oracle of Multi-head Latent Attention over a latent cache.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run this module.  It shares
+no code with the HIP library: it has its own bf16 decoding and rounding, its
+own RoPE, its own page addressing and its own softmax.  It is deliberately
+slow and obvious: per-head K and V are materialised from the latent exactly as
+the non-absorbed description reads, and every step is a plain NumPy
+expression.
+
+Sources (the pages carry no code; each function names the passage it follows):
+  [blog]  yapayzekasozluk.tr, "Multi-head Latent Attention (MLA) Nedir?"
+          sections "MLA nasil calisir?" (compression, decompression,
+          decoupled RoPE) and "MLA'nin avantajlari ve hesap maliyeti".
+  [scale] LLMScale, "GQA, MQA ve MLA: attention KV cache'i nasil belirler",
+          sections "Multi-head attention (MHA)", "Grouped-query attention
+          (GQA)", "Multi-head latent attention (MLA)".
+  [arch]  openarchlab, "MLA - latent KV, decoupled RoPE va matrix
+          absorption", sections 1 (definition), 2 (flow), 3 (solution:
+          cache formulas), 4 (profiling), 5 (examples), 6 (terms).
+
+Readings where the pages leave a step open (all pinned by tests/test_oracle_*):
+  * RoPE (named, not written out, in [blog] "Decoupled RoPE" and [arch] 1):
+    the rotary embedding of RoFormer with adjacent pairs (2i, 2i+1),
+    theta_i = base^(-2i/d), position p as a float64 angle p*theta_i.
+  * One rotary key k_R per token, shared by all heads ([scale] MLA: the head
+    count drops out of the per-token cache size); one rotary query part q_R
+    per head.
+  * V is up-projected from the content latent c only ([arch] 1: only the
+    position branch is kept apart from the latent).
+  * Score of head h against token t:  sigma * (q_C,h . K_C,h,t + q_R,h . k_R,t),
+    softmax over t, natural-log LSE.  sigma is an input.
+  * Decode: the query sits at position seq_len-1 and sees all seq_len rows,
+    including its own row written in the same step ([arch] 2: project, then
+    write, then read).
+  * Prefill: query i of a fresh sequence sees rows t <= i.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# storage formats
+# --------------------------------------------------------------------------
+
+
+def from_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Decode stored values to float64.  bf16 arrives as raw uint16 patterns:
+    the value is the float32 whose upper 16 bits are the pattern."""
+    if dtype == "bf16":
+        u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return u.view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 to the nearest bf16 value (8 significant bits), ties to even.
+
+    Single rounding straight from float64: scale each value by a power of two
+    so its 8 significant bits sit left of the binary point, round half-even,
+    scale back (both scalings are exact)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def round_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_bf16(x)
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# cache-size formulas ([scale] MHA / GQA / MLA; [arch] 3 and 5)
+# --------------------------------------------------------------------------
+
+
+def mla_cache_bytes_per_token(layers: int, d_c: int, d_r: int, elem_bytes: int) -> int:
+    """Per-token MLA cache: layers x (latent width + rotary key width) x bytes.
+    The head count does not enter ([scale] MLA; [arch] 3)."""
+    return layers * (d_c + d_r) * elem_bytes
+
+
+def mla_cache_bytes(layers: int, tokens: int, d_c: int, d_r: int, elem_bytes: int) -> int:
+    """Ideal MLA cache of one sequence: L x T x (d_c + d_R) x b ([arch] 3)."""
+    return tokens * mla_cache_bytes_per_token(layers, d_c, d_r, elem_bytes)
+
+
+def gqa_cache_bytes_per_token(layers: int, kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """Uniform GQA: 2 x L x H_KV x d_h x b per token ([arch] 3).  With
+    kv_heads equal to the query heads this is the MHA formula ([scale] MHA)."""
+    return 2 * layers * kv_heads * head_dim * elem_bytes
+
+
+def gqa_equivalent_groups(d_c: int, d_r: int, head_dim: int) -> float:
+    """Number of K/V head pairs whose cache equals one MLA latent row."""
+    return (d_c + d_r) / (2.0 * head_dim)
+
+
+# --------------------------------------------------------------------------
+# rotary embedding ([blog] "Decoupled RoPE"; [arch] 1 and 6)
+# --------------------------------------------------------------------------
+
+
+def rope(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """Rotate adjacent pairs (x_2i, x_2i+1) of the last axis by angle pos*theta_i,
+    theta_i = base^(-2i/d).  ``pos`` broadcasts against x.shape[:-1]."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    assert d % 2 == 0
+    i = np.arange(d // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * i / d)
+    p = np.asarray(pos, dtype=np.float64)
+    p = np.broadcast_to(p, x.shape[:-1])
+    ang = p[..., None] * theta
+    cs, sn = np.cos(ang), np.sin(ang)
+    ev, od = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = ev * cs - od * sn
+    out[..., 1::2] = ev * sn + od * cs
+    return out
+
+
+# --------------------------------------------------------------------------
+# step 1: project the hidden state to the cached row ([arch] 2 step 1;
+#         [blog] compression + decoupled RoPE)
+# --------------------------------------------------------------------------
+
+
+def latent_rows(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray, positions, base: float) -> np.ndarray:
+    """row_n = [c_KV,n | k_R,n] with c_KV,n = W_DKV h_n and
+    k_R,n = RoPE(W_KR h_n, p_n).  float64, unrounded.  Shapes: h [N, D],
+    w_dkv [d_c, D], w_kr [d_R, D] -> [N, d_c + d_R]."""
+    c = h @ w_dkv.T
+    kr = rope(h @ w_kr.T, np.asarray(positions), base)
+    return np.concatenate([c, kr], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# step 2: write the cache in the engine's layout ([arch] 2 step 2;
+#         paged cache: [blog] "MLA ve diger optimizasyonlarla iliskisi")
+# --------------------------------------------------------------------------
+
+
+def scatter_rows(pool: np.ndarray, rows: np.ndarray, slots: np.ndarray) -> np.ndarray:
+    """Return a copy of ``pool`` [num_pages, P, R] with row n stored at slot
+    slots[n] (page slots[n] // P, offset slots[n] % P); slot -1 is skipped."""
+    out = np.array(pool, copy=True)
+    P = out.shape[1]
+    for n, s in enumerate(np.asarray(slots).tolist()):
+        if s < 0:
+            continue
+        out[s // P, s % P, :] = rows[n]
+    return out
+
+
+def gather_rows(pool: np.ndarray, block_table_row: np.ndarray, length: int) -> np.ndarray:
+    """Rows 0..length-1 of one sequence: token t lives in page
+    block_table_row[t // P] at offset t % P."""
+    P = pool.shape[1]
+    out = np.empty((length, pool.shape[2]), dtype=pool.dtype)
+    for t in range(length):
+        out[t] = pool[int(block_table_row[t // P]), t % P]
+    return out
+
+
+# --------------------------------------------------------------------------
+# step 3: read -- the plain, non-absorbed form ([blog] decompression:
+#         K and V are regenerated from c_KV per head)
+# --------------------------------------------------------------------------
+
+
+def _attend(scores: np.ndarray, values: np.ndarray) -> Tuple[np.ndarray, float]:
+    """Softmax over the last axis of ``scores`` [T], weighted sum of
+    ``values`` [T, d]; returns (output [d], natural-log LSE)."""
+    m = float(np.max(scores))
+    w = np.exp(scores - m)
+    l = float(np.sum(w))
+    return (w @ values) / l, m + math.log(l)
+
+
+def decode_one(q: np.ndarray, rows: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray,
+               q_pos: int, d_c: int, sigma: float, base: float,
+               heads: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """One decode query of one sequence, every head, non-absorbed.
+
+    q    [H, d_n + d_R]  pre-RoPE query per head ([q_C | q_R])
+    rows [T, d_c + d_R]  the sequence's cached rows, float64
+    w_uk [H, d_n, d_c], w_uv [H, d_v, d_c]
+    Returns o [H, d_v], lse [H] (only ``heads`` filled if given, others NaN).
+    """
+    H, dq = q.shape
+    d_n = w_uk.shape[1]
+    d_v = w_uv.shape[1]
+    C = rows[:, :d_c]
+    KR = rows[:, d_c:]
+    o = np.full((H, d_v), np.nan)
+    lse = np.full(H, np.nan)
+    if rows.shape[0] == 0:
+        o[:] = 0.0
+        lse[:] = -np.inf
+        return o, lse
+    for h in (range(H) if heads is None else heads):
+        q_c = q[h, :d_n]
+        q_r = rope(q[h, d_n:], q_pos, base)
+        K_c = C @ w_uk[h].T            # [T, d_n]   K_C,h,t = W_UK,h c_t
+        V = C @ w_uv[h].T              # [T, d_v]   V_h,t   = W_UV,h c_t
+        s = sigma * (K_c @ q_c + KR @ q_r)
+        o[h], lse[h] = _attend(s, V)
+    return o, lse
+
+
+def decode(q: np.ndarray, pool: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
+           w_uk: np.ndarray, w_uv: np.ndarray, d_c: int, sigma: float, base: float,
+           seqs: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None):
+    """Batched decode: sequence b's query q[b] at position seq_lens[b]-1 over
+    its seq_lens[b] cached rows.  Returns o [B, H, d_v], lse [B, H] (NaN for
+    sequences not in ``seqs``)."""
+    B, H, _ = q.shape
+    d_v = w_uv.shape[1]
+    o = np.full((B, H, d_v), np.nan)
+    lse = np.full((B, H), np.nan)
+    for b in (range(B) if seqs is None else seqs):
+        L = int(seq_lens[b])
+        rows = gather_rows(pool, block_table[b], L)
+        o[b], lse[b] = decode_one(q[b], rows, w_uk, w_uv, L - 1, d_c, sigma, base, heads)
+    return o, lse
+
+
+def prefill_one(q: np.ndarray, rows: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray,
+                d_c: int, sigma: float, base: float,
+                queries: Optional[Sequence[int]] = None,
+                heads: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Causal prefill of one fresh sequence: query i (position i) sees rows
+    t <= i.  q [T, H, d_n + d_R], rows [T, R].  Returns o [T, H, d_v] and
+    lse [T, H]; entries outside ``queries`` x ``heads`` are NaN."""
+    T, H, _ = q.shape
+    d_n = w_uk.shape[1]
+    d_v = w_uv.shape[1]
+    C = rows[:, :d_c]
+    KR = rows[:, d_c:]
+    qi = np.arange(T) if queries is None else np.asarray(queries)
+    o = np.full((T, H, d_v), np.nan)
+    lse = np.full((T, H), np.nan)
+    for h in (range(H) if heads is None else heads):
+        K_c = C @ w_uk[h].T
+        V = C @ w_uv[h].T
+        for i in qi.tolist():
+            q_c = q[i, h, :d_n]
+            q_r = rope(q[i, h, d_n:], i, base)
+            s = sigma * (K_c[: i + 1] @ q_c + KR[: i + 1] @ q_r)
+            o[i, h], lse[i, h] = _attend(s, V[: i + 1])
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# absorbed order ([arch] 1 and 6: fold W_UK into the query, apply W_UV
+# after the weighted latent sum -- same function, different order)
+# --------------------------------------------------------------------------
+
+
+def absorb_query(q: np.ndarray, w_uk: np.ndarray, q_pos, d_n: int, base: float) -> np.ndarray:
+    """q~[..., h, :d_c] = W_UK,h^T q_C,h ;  q~[..., h, d_c:] = RoPE(q_R,h, p).
+    q [N, H, d_n + d_R], q_pos [N] -> [N, H, d_c + d_R]."""
+    q_c = q[..., :d_n]
+    q_r = rope(q[..., d_n:], np.asarray(q_pos)[..., None], base)
+    q_lat = np.einsum("nhj,hjc->nhc", q_c, w_uk)
+    return np.concatenate([q_lat, q_r], axis=-1)
+
+
+def absorbed_logits(q_abs: np.ndarray, rows: np.ndarray, sigma: float) -> np.ndarray:
+    """Scores of absorbed queries q_abs [H, R] against cached rows [T, R]:
+    sigma * q~_h . row_t  -> [H, T]."""
+    return sigma * (q_abs @ rows.T)
+
+
+def nonabsorbed_logits(q: np.ndarray, rows: np.ndarray, w_uk: np.ndarray, q_pos: int,
+                       d_c: int, sigma: float, base: float) -> np.ndarray:
+    """The same scores computed with per-head K materialised -> [H, T]."""
+    H = q.shape[0]
+    d_n = w_uk.shape[1]
+    C, KR = rows[:, :d_c], rows[:, d_c:]
+    out = np.empty((H, rows.shape[0]))
+    for h in range(H):
+        out[h] = sigma * ((C @ w_uk[h].T) @ q[h, :d_n] + KR @ rope(q[h, d_n:], q_pos, base))
+    return out
+
+
+# --------------------------------------------------------------------------
+# merging partial softmax results over disjoint token ranges
+# --------------------------------------------------------------------------
+
+
+def partial_softmax(scores: np.ndarray, latents: np.ndarray):
+    """(m, l, acc) of one token range: m = max s, l = sum e^(s-m),
+    acc = sum e^(s-m) latent.  An empty range gives (-inf, 0, 0)."""
+    if scores.shape[0] == 0:
+        return -np.inf, 0.0, np.zeros(latents.shape[1])
+    m = float(np.max(scores))
+    w = np.exp(scores - m)
+    return m, float(np.sum(w)), w @ latents
+
+
+def merge_partials(parts) -> Tuple[np.ndarray, float]:
+    """Combine (m_s, l_s, acc_s): m* = max m_s, weights e^(m_s - m*), normalised
+    latent sum and natural-log LSE.  Empty parts carry weight 0."""
+    ms = np.array([p[0] for p in parts], dtype=np.float64)
+    m_star = float(np.max(ms))
+    if m_star == -np.inf:
+        return np.zeros_like(parts[0][2]), -np.inf
+    wts = np.array([0.0 if p[0] == -np.inf else math.exp(p[0] - m_star) for p in parts])
+    l_star = float(sum(w * p[1] for w, p in zip(wts, parts)))
+    acc = sum(w * p[2] for w, p in zip(wts, parts))
+    return acc / l_star, m_star + math.log(l_star)
