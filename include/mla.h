@@ -1,0 +1,197 @@
+/*
+ * mla.h -- C ABI of libmla.so: Multi-head Latent Attention over a paged
+ * latent cache, hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are the pages this library is built from):
+ *   - Per token, the hidden state h is projected to a small latent
+ *     c_KV = W_DKV h and a separate rotary key k_R = RoPE(W_KR h, p); only the
+ *     row [c_KV | k_R] is cached, one per token per layer, shared by every head
+ *     (yapayzekasozluk.tr "Multi-head Latent Attention (MLA) Nedir?", section
+ *     "MLA nasil calisir?"; LLMScale "GQA, MQA ve MLA", section "Multi-head
+ *     latent attention (MLA)").
+ *   - The step order is: project to the latent, write the cache in the
+ *     engine's layout, read it with merged matrices or an equivalent kernel
+ *     (openarchlab "MLA - latent KV, decoupled RoPE va matrix absorption",
+ *     section 2).
+ *   - Reading uses matrix absorption: W_UK is folded into the query and W_UV
+ *     is applied after the softmax-weighted latent sum, changing the order of
+ *     computation but not the function (same page, sections 1 and 6).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *     and the call returns at once.  Scalar/struct pointers (dims, out
+ *     parameters of the size helpers) are HOST pointers.
+ *   - All tensors are dense row-major with the shapes written below.
+ *     `dtype` selects fp32 or bf16 storage for every floating tensor except
+ *     `lse` (always fp32) and workspaces (library-defined).  Arithmetic is
+ *     fp32 (bf16 operands, fp32 accumulation) in either case.
+ *   - Argument errors are detected on the host before anything is launched
+ *     and return a negative mla_status; nothing is written.  A failed kernel
+ *     launch returns MLA_ERR_HIP.  Device-side preconditions (block-table
+ *     entries < num_pages, positions >= 0) are the caller's duty and are not
+ *     checked on the device, except that decode lengths are clamped to
+ *     max_seq_len, which the host checks against the block-table capacity,
+ *     so no read leaves the caller's pages.
+ *   - Calls on one stream are ordered; calls that share an output or a
+ *     workspace on different streams race.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,      /* a required pointer is NULL                        */
+  MLA_ERR_DIMS = -2,      /* unsupported or inconsistent dimensions            */
+  MLA_ERR_DTYPE = -3,     /* unknown dtype code                                */
+  MLA_ERR_WORKSPACE = -4, /* workspace smaller than the *_workspace_size value */
+  MLA_ERR_CAPACITY = -5,  /* max_seq_len exceeds max_pages_per_seq * page_size */
+  MLA_ERR_HIP = -6,       /* a HIP launch or device query failed               */
+  MLA_ERR_ARG = -7        /* other invalid argument (negative count, bad flag) */
+} mla_status;
+
+enum { MLA_F32 = 0, MLA_BF16 = 1 };
+
+/* flags: MLA_FLAG_GENERIC forces the plain (VALU, any-shape) kernels even
+ * where the MFMA kernels apply; used to cross-check the two on one input. */
+enum { MLA_FLAG_GENERIC = 1 };
+
+typedef struct {
+  int32_t hidden;      /* D: width of h                                         */
+  int32_t num_heads;   /* H: query heads                                        */
+  int32_t d_c;         /* latent width (kv_lora_rank), even                     */
+  int32_t d_r;         /* rotary key width (qk_rope_head_dim), even             */
+  int32_t qk_nope;     /* d_n: per-head non-rotary query/key width              */
+  int32_t v_head;      /* d_v: per-head value width                             */
+  int32_t page_size;   /* P: tokens per cache page                              */
+  int32_t dtype;       /* MLA_F32 or MLA_BF16                                   */
+  float rope_base;     /* RoPE base (10000 in the pages' models)                */
+  float softmax_scale; /* sigma, multiplies every score                         */
+  int32_t flags;       /* 0 or MLA_FLAG_GENERIC                                 */
+} mla_dims_t;
+
+/*
+ * Step 1 + 2: project and write the cache (openarchlab section 2, steps 1-2;
+ * compression and decoupled RoPE as in yapayzekasozluk.tr "MLA nasil calisir?").
+ *
+ * For n < n_tokens with slot_mapping[n] >= 0:
+ *   row = [ W_DKV h_n  |  RoPE(W_KR h_n, positions[n]) ]      (fp32, then dtype, RNE)
+ *   pool[slot / P][slot % P][0 : d_c + d_r] = row
+ * RoPE rotates adjacent pairs (2i, 2i+1) by positions[n] * rope_base^(-2i/d_r).
+ *
+ *   h            [n_tokens, D]                 dtype
+ *   w_dkr        [d_c + d_r, D]                dtype  rows 0..d_c-1 = W_DKV, rest = W_KR
+ *   positions    [n_tokens]                    int32
+ *   slot_mapping [n_tokens]                    int64  page * P + offset, -1 = skip
+ *   pool         [num_pages, P, d_c + d_r]     dtype  updated in place
+ * Slots must be distinct and < num_pages * P (unchecked on the device).
+ * n_tokens == 0 is a no-op.
+ */
+int mla_write_cache(const mla_dims_t* dims, const void* h, const void* w_dkr,
+                    const int32_t* positions, const int64_t* slot_mapping, int32_t n_tokens,
+                    void* pool, int32_t num_pages, hipStream_t stream);
+
+/*
+ * Query absorption (openarchlab sections 1 and 6: W_UK folded into the query).
+ *   q_abs[n][h][0 : d_c]       = W_UK,h^T q[n][h][0 : d_n]
+ *   q_abs[n][h][d_c : d_c+d_r] = RoPE(q[n][h][d_n : d_n + d_r], positions[n])
+ *
+ *   q      [n_tokens, H, d_n + d_r]  dtype  pre-RoPE query, per head [q_C | q_R]
+ *   w_uk   [H, d_n, d_c]             dtype  K_C,h = W_UK,h c
+ *   q_abs  [n_tokens, H, d_c + d_r]  dtype  output
+ */
+int mla_absorb_q(const mla_dims_t* dims, const void* q, const void* w_uk,
+                 const int32_t* positions, int32_t n_tokens, void* q_abs, hipStream_t stream);
+
+/* Bytes of workspace mla_decode needs for `batch` sequences of at most
+ * max_seq_len tokens (0 on invalid arguments or when no device is present). */
+size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t max_seq_len);
+
+/*
+ * Step 3, decode (openarchlab section 2 step 3; absorption, sections 1 and 6).
+ * Sequence b has seq_lens[b] cached rows; token t lives at
+ * pool[block_table[b][t / P]][t % P].  Its query q_abs[b] attends to all of
+ * them (it sits at position seq_lens[b]-1, its own row already written):
+ *   s_h,t  = softmax_scale * q_abs[b][h] . row_t              (all d_c + d_r)
+ *   lat_h  = sum_t softmax_t(s_h) row_t[0 : d_c]
+ *   out[b][h] = W_UV,h lat_h,   lse[b][h] = ln sum_t exp(s_h,t)
+ * Empty sequences give out = 0, lse = -inf.
+ *
+ *   q_abs       [batch, H, d_c + d_r]           dtype
+ *   pool        [num_pages, P, d_c + d_r]       dtype
+ *   block_table [batch, max_pages_per_seq]      int32
+ *   seq_lens    [batch]                         int32 (device); lengths above
+ *                                                max_seq_len are clamped to it
+ *   w_uv        [H, d_v, d_c]                   dtype
+ *   out         [batch, H, d_v]                 dtype
+ *   lse         [batch, H]                      fp32, may be NULL
+ *   workspace   >= mla_decode_workspace_size(dims, batch, max_seq_len) bytes
+ * max_seq_len is a host-side bound on seq_lens: it must not exceed
+ * max_pages_per_seq * P (MLA_ERR_CAPACITY) and it sizes the workspace.
+ * Results do not depend on the page permutation (token-space split
+ * boundaries, fixed merge order): two calls on permuted pools give identical
+ * bits.
+ */
+int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int32_t num_pages,
+               const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+               int32_t batch, int32_t max_seq_len, const void* w_uv, void* out, float* lse,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace mla_prefill needs for `total_tokens` query tokens. */
+size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t total_tokens);
+
+/*
+ * Causal prefill of fresh sequences (openarchlab section 4 asks for prefill
+ * and decode to be measured on the target kernel; decompression of K and V
+ * from c_KV, yapayzekasozluk.tr "MLA nasil calisir?").  Sequence i holds
+ * tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 of q/out, at positions
+ * 0 .. len-1, and its rows are already in the pool.  For each head h:
+ *   K_h,t = [W_UK,h c_t | k_R,t],  V_h,t = W_UV,h c_t,
+ *   Q_h,i = [q_C | RoPE(q_R, i)],  out[i][h] = softmax_{t<=i}(sigma Q.K) V,
+ *   lse[i][h] = ln sum_{t<=i} exp(sigma Q.K).
+ *
+ *   q           [total_tokens, H, d_n + d_r]   dtype  pre-RoPE
+ *   cu_seqlens  [num_seqs + 1]                  int32 (device), cu[0] = 0,
+ *                                               cu[num_seqs] = total_tokens
+ *   out         [total_tokens, H, d_v]          dtype
+ *   lse         [total_tokens, H]               fp32, may be NULL
+ * max_seq_len bounds every sequence length (capacity check and tiling).
+ */
+int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t num_pages,
+                const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* cu_seqlens,
+                int32_t num_seqs, int32_t total_tokens, int32_t max_seq_len, const void* w_uk,
+                const void* w_uv, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
+ * Ideal cache bytes of `tokens` tokens over `layers` layers:
+ * layers x tokens x (d_c + d_r) x element bytes (openarchlab section 3;
+ * LLMScale "Multi-head latent attention (MLA)": the head count drops out).
+ * Returns 0 for invalid dims.
+ */
+size_t mla_cache_bytes(const mla_dims_t* dims, int64_t tokens, int32_t layers);
+
+/* Static string naming a status code. */
+const char* mla_status_string(int status);
+
+/*
+ * Which kernels a call with these dims would use: 1 = MFMA fast path,
+ * 0 = generic path, negative = invalid dims.  `op` is 0 write_cache,
+ * 1 absorb_q, 2 decode, 3 prefill.
+ */
+int mla_uses_fast_path(const mla_dims_t* dims, int32_t op);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,160 @@
+// Device helpers shared by the HIP kernels of libmla (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- storage
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ld(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+
+// ---------------------------------------------------------------- RoPE
+// Rotation of pair i of a d-wide vector at position pos: angle pos * base^(-2i/d).
+// The angle and its sine/cosine are taken in double so that large positions
+// (tens of thousands of radians for pair 0) keep full fp32 accuracy.
+__device__ __forceinline__ void rope_cs(int pos, int i, int d, float base, float& c, float& s) {
+  const double theta = exp(-(2.0 * (double)i / (double)d) * log((double)base));
+  const double ang = (double)pos * theta;
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// ---------------------------------------------------------------- block reductions
+__device__ __forceinline__ int block_sum_int(int v, int* red) {
+  // red: >= blockDim.x/64 ints of LDS
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  int s = 0;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+// Exclusive prefix sum of one int per thread over the work-group.
+// red: >= blockDim.x/64 ints of LDS.  Returns the prefix, writes the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) red[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int r = red[i];
+    if (i < w) base += r;
+    tot += r;
+  }
+  total = tot;
+  return base + x - v;
+}
+
+// ---------------------------------------------------------------- decode work split
+// The token axis of every sequence is cut into chunks of `chunk` tokens
+// (a multiple of 32); chunk k of sequence b is work item s_items[b] + k.  The
+// plan is a pure function of the clamped lengths, the slot count and the
+// overhead estimate, so every work-group (and the combine kernel) computes
+// the same plan without a host round trip, and the split points never depend
+// on where pages live.
+struct DecodePlan {
+  int chunk;
+  int n_items;
+};
+
+__device__ __forceinline__ int clamp_len(int len, int cap) { return len < 0 ? 0 : (len > cap ? cap : len); }
+
+// Candidate chunk sizes: the total token count spread over k * slots items
+// for k = 1, 2, 4, rounded up to 32 and clamped to [min_chunk, max_chunk].  The chosen one
+// minimises (rounds of `slots` items) * chunk + the partial-result overhead
+// (ovh_tokens token-equivalents per item, spread over the slots).
+// s_len, s_items: LDS, >= batch + 1 ints; red: LDS, >= 16 ints.  All threads call.
+__device__ inline DecodePlan make_decode_plan(const int32_t* __restrict__ seq_lens, int batch, int cap,
+                                              int slots, int min_chunk, int max_chunk, int ovh_tokens, int* s_len,
+                                              int* s_items, int* red) {
+  int part = 0;
+  for (int b = threadIdx.x; b < batch; b += blockDim.x) {
+    const int L = clamp_len(seq_lens[b], cap);
+    s_len[b] = L;
+    part += L;
+  }
+  const int total = block_sum_int(part, red);  // (barriers inside publish s_len)
+  int best_chunk = 0;
+  long long best_cost = -1;
+  for (int k = 1; k <= 4; k <<= 1) {
+    const long long denom = (long long)k * slots;
+    int ch = (int)((total + denom - 1) / denom);
+    ch = ((ch + 31) / 32) * 32;
+    if (ch < min_chunk) ch = min_chunk;
+    if (ch > max_chunk) ch = max_chunk;
+    int it = 0;
+    for (int b = threadIdx.x; b < batch; b += blockDim.x) it += (s_len[b] + ch - 1) / ch;
+    it = block_sum_int(it, red);
+    const long long rounds = (it + slots - 1) / slots;
+    const long long cost = rounds * ch + ((long long)it * ovh_tokens) / slots;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_chunk = ch;
+    }
+  }
+  // exclusive prefix of item counts: thread t owns a contiguous run of sequences
+  const int per = (batch + blockDim.x - 1) / blockDim.x;
+  const int b0 = threadIdx.x * per;
+  const int b1 = min(batch, b0 + per);
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) mine += (s_len[b] + best_chunk - 1) / best_chunk;
+  int n_items = 0;
+  int pre = block_exclusive_scan(mine, red, n_items);
+  for (int b = b0; b < b1; ++b) {
+    s_items[b] = pre;
+    pre += (s_len[b] + best_chunk - 1) / best_chunk;
+  }
+  if (threadIdx.x == 0) s_items[batch] = n_items;
+  __syncthreads();
+  DecodePlan p;
+  p.chunk = best_chunk;
+  p.n_items = n_items;
+  return p;
+}
+
+// Sequence owning work item `item` (s_items ascending, s_items[batch] > item).
+__device__ __forceinline__ int item_seq(const int* s_items, int batch, int item) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_items[mid] <= item) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace mla

@@ -1,0 +1,83 @@
+// Internal interface between the C ABI (mla_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+// Largest batch the decode kernels plan for (two int arrays of this size sit in LDS).
+constexpr int kMaxDecodeBatch = 4096;
+// Decode split: k in {1,2,4} chunks per slot, so items <= 4 * slots + batch.
+constexpr int kMaxChunksPerSlot = 4;
+// Longest token range of one decode work item, and the pages it can touch.
+constexpr int kMaxChunk = 8192;
+constexpr int kMaxItemPages = kMaxChunk / 32 + 2;
+
+struct WriteCacheArgs {
+  const void* h;
+  const void* w_dkr;
+  const int32_t* positions;
+  const int64_t* slots;
+  void* pool;
+  int n_tokens, D, d_c, d_r, P;
+  float rope_base;
+};
+
+struct AbsorbArgs {
+  const void* q;
+  const void* w_uk;
+  const int32_t* positions;
+  void* q_abs;
+  int n_tokens, H, d_n, d_c, d_r;
+  float rope_base;
+};
+
+struct DecodeArgs {
+  const void* q_abs;
+  const void* pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const void* w_uv;
+  void* out;
+  float* lse;
+  float* part_acc;  // [max_items, H, d_c]
+  float* part_ml;   // [max_items, H, 2]  (running max in log2 units, sum)
+  int batch, H, d_c, d_r, d_v, P, max_pages_per_seq;
+  int len_cap;      // lengths are clamped to min(max_seq_len, block-table capacity)
+  int slots;        // concurrent work-groups the split kernel can hold
+  int max_items;    // capacity of the partial buffers
+  int min_chunk, ovh_tokens;
+  float scale_log2; // softmax_scale * log2(e)
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* pool;
+  const int32_t* block_table;
+  const int32_t* cu_seqlens;
+  const void* w_uk;
+  const void* w_uv;
+  void* out;
+  float* lse;
+  void* ws_k;  // up-projected K_C  [total, H, d_n]
+  void* ws_v;  // up-projected V    [total, H, d_v]
+  int num_seqs, total, max_seq_len, H, d_n, d_r, d_c, d_v, P, max_pages_per_seq;
+  float rope_base, scale;
+};
+
+// generic kernels (any shape, fp32 or bf16 storage)
+hipError_t write_cache_generic(const WriteCacheArgs& a, bool bf16, hipStream_t s);
+hipError_t absorb_generic(const AbsorbArgs& a, bool bf16, hipStream_t s);
+hipError_t decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s);
+hipError_t prefill_generic(const PrefillArgs& a, bool bf16, hipStream_t s);
+
+// MFMA kernels (bf16, latent width 512, rotary width 64)
+bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch);
+int decode_mfma_slots(int H, int cus);
+hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace mla

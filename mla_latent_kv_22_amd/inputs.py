@@ -113,7 +113,8 @@ def seq_lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
     return np.full(cfg.batch, cfg.seq_len, dtype=np.int32)
 
 
-def make(cfg: Config, seed: int = 0, with_rows: bool = True) -> Dict[str, np.ndarray]:
+def make(cfg: Config, seed: int = 0, with_rows: bool = True,
+         lengths=None) -> Dict[str, np.ndarray]:
     """Build every input of one step of ``cfg``.
 
     Returns a dict with:
@@ -132,7 +133,11 @@ def make(cfg: Config, seed: int = 0, with_rows: bool = True) -> Dict[str, np.nda
     """
     rng = np.random.default_rng(seed)
     P = cfg.page_size
-    lens = seq_lengths(cfg, rng)
+    if lengths is not None:
+        lens = np.asarray(lengths, dtype=np.int32)
+        assert lens.shape == (cfg.batch,)
+    else:
+        lens = seq_lengths(cfg, rng)
     pages_per_seq = (lens.astype(np.int64) + P - 1) // P
     num_pages = int(pages_per_seq.sum())
     max_pages = int(pages_per_seq.max())
@@ -161,9 +166,12 @@ def make(cfg: Config, seed: int = 0, with_rows: bool = True) -> Dict[str, np.nda
         seq_of_tok = np.repeat(np.arange(cfg.batch), lens)
     else:
         # decode: the newest token of each sequence is written this step
-        positions = (lens - 1).astype(np.int32)
+        # (an empty sequence writes nothing: slot -1)
+        positions = np.maximum(lens - 1, 0).astype(np.int32)
         seq_of_tok = np.arange(cfg.batch)
     slots = (block_table[seq_of_tok, positions // P].astype(np.int64) * P + positions % P).astype(np.int64)
+    if not full_path:
+        slots[lens == 0] = -1
     h = _normal(rng, (positions.shape[0], D), 1.0, cfg.dtype)
 
     if with_rows and not full_path:
@@ -175,7 +183,7 @@ def make(cfg: Config, seed: int = 0, with_rows: bool = True) -> Dict[str, np.nda
     if cfg.prefill:
         q_positions = positions.copy()
     else:
-        q_positions = (lens - 1).astype(np.int32)
+        q_positions = np.maximum(lens - 1, 0).astype(np.int32)
     q = _normal(rng, (q_positions.shape[0], H, cfg.qk_head), q_std, cfg.dtype)
     cu = np.zeros(cfg.batch + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lens)

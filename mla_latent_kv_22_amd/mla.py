@@ -1,0 +1,168 @@
+"""ctypes binding of libmla.so (C ABI in include/mla.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the HIP stream, and a negative status becomes an exception.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback.  Importing this module does not load the library; the first call
+does, and raises if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+F32, BF16 = 0, 1
+FLAG_GENERIC = 1
+OP_WRITE_CACHE, OP_ABSORB_Q, OP_DECODE, OP_PREFILL = 0, 1, 2, 3
+
+_SYMBOLS = ("mla_write_cache", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode",
+            "mla_prefill_workspace_size", "mla_prefill", "mla_cache_bytes", "mla_status_string",
+            "mla_uses_fast_path")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("d_c", ctypes.c_int32),
+                ("d_r", ctypes.c_int32), ("qk_nope", ctypes.c_int32), ("v_head", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_int32)]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mla_latent_kv_22_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        dp = ctypes.POINTER(Dims)
+        L.mla_write_cache.argtypes = [dp, vp, vp, vp, vp, i32, vp, i32, vp]
+        L.mla_absorb_q.argtypes = [dp, vp, vp, vp, i32, vp, vp]
+        L.mla_decode_workspace_size.argtypes = [dp, i32, i32]
+        L.mla_decode_workspace_size.restype = sz
+        L.mla_decode.argtypes = [dp, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.mla_prefill_workspace_size.argtypes = [dp, i32]
+        L.mla_prefill_workspace_size.restype = sz
+        L.mla_prefill.argtypes = [dp, vp, vp, i32, vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.mla_cache_bytes.argtypes = [dp, i64, i32]
+        L.mla_cache_bytes.restype = sz
+        L.mla_status_string.argtypes = [ctypes.c_int]
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_uses_fast_path.argtypes = [dp, i32]
+        for f in ("mla_write_cache", "mla_absorb_q", "mla_decode", "mla_prefill", "mla_uses_fast_path"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mla_status_string(int(status)).decode()
+
+
+def make_dims(hidden, num_heads, d_c, d_r, qk_nope, v_head, page_size, dtype, rope_base, softmax_scale,
+              flags=0) -> Dims:
+    return Dims(hidden, num_heads, d_c, d_r, qk_nope, v_head, page_size,
+                BF16 if dtype in ("bf16", BF16, torch.bfloat16) else F32, rope_base, softmax_scale, flags)
+
+
+# --------------------------------------------------------------------------- helpers
+
+def _torch_dtype(d: Dims):
+    return torch.bfloat16 if d.dtype == BF16 else torch.float32
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise MLAError(status, what)
+
+
+# --------------------------------------------------------------------------- calls
+
+def write_cache(d: Dims, h, w_dkr, positions, slot_mapping, pool, stream=None) -> None:
+    dt = _torch_dtype(d)
+    n = 0 if h is None else int(h.shape[0])
+    num_pages = int(pool.shape[0])
+    _check(lib().mla_write_cache(ctypes.byref(d), _ptr(h, "h", dt), _ptr(w_dkr, "w_dkr", dt),
+                                 _ptr(positions, "positions", torch.int32),
+                                 _ptr(slot_mapping, "slot_mapping", torch.int64), n,
+                                 _ptr(pool, "pool", dt), num_pages, _stream(stream)), "mla_write_cache")
+
+
+def absorb_q(d: Dims, q, w_uk, positions, q_abs, stream=None) -> None:
+    dt = _torch_dtype(d)
+    _check(lib().mla_absorb_q(ctypes.byref(d), _ptr(q, "q", dt), _ptr(w_uk, "w_uk", dt),
+                              _ptr(positions, "positions", torch.int32), int(q.shape[0]),
+                              _ptr(q_abs, "q_abs", dt), _stream(stream)), "mla_absorb_q")
+
+
+def decode_workspace_size(d: Dims, batch: int, max_seq_len: int) -> int:
+    return int(lib().mla_decode_workspace_size(ctypes.byref(d), int(batch), int(max_seq_len)))
+
+
+def decode(d: Dims, q_abs, pool, block_table, seq_lens, max_seq_len: int, w_uv, out, lse, workspace,
+           stream=None) -> None:
+    dt = _torch_dtype(d)
+    _check(lib().mla_decode(ctypes.byref(d), _ptr(q_abs, "q_abs", dt), _ptr(pool, "pool", dt),
+                            int(pool.shape[0]), _ptr(block_table, "block_table", torch.int32),
+                            int(block_table.shape[1]), _ptr(seq_lens, "seq_lens", torch.int32),
+                            int(seq_lens.shape[0]), int(max_seq_len), _ptr(w_uv, "w_uv", dt),
+                            _ptr(out, "out", dt), _ptr(lse, "lse", torch.float32),
+                            _ptr(workspace, "workspace", torch.uint8),
+                            0 if workspace is None else workspace.numel(), _stream(stream)), "mla_decode")
+
+
+def prefill_workspace_size(d: Dims, total_tokens: int) -> int:
+    return int(lib().mla_prefill_workspace_size(ctypes.byref(d), int(total_tokens)))
+
+
+def prefill(d: Dims, q, pool, block_table, cu_seqlens, max_seq_len: int, w_uk, w_uv, out, lse, workspace,
+            stream=None) -> None:
+    dt = _torch_dtype(d)
+    _check(lib().mla_prefill(ctypes.byref(d), _ptr(q, "q", dt), _ptr(pool, "pool", dt), int(pool.shape[0]),
+                             _ptr(block_table, "block_table", torch.int32), int(block_table.shape[1]),
+                             _ptr(cu_seqlens, "cu_seqlens", torch.int32), int(cu_seqlens.shape[0]) - 1,
+                             int(q.shape[0]), int(max_seq_len), _ptr(w_uk, "w_uk", dt), _ptr(w_uv, "w_uv", dt),
+                             _ptr(out, "out", dt), _ptr(lse, "lse", torch.float32),
+                             _ptr(workspace, "workspace", torch.uint8),
+                             0 if workspace is None else workspace.numel(), _stream(stream)), "mla_prefill")
+
+
+def cache_bytes(d: Dims, tokens: int, layers: int) -> int:
+    return int(lib().mla_cache_bytes(ctypes.byref(d), int(tokens), int(layers)))
+
+
+def uses_fast_path(d: Dims, op: int) -> int:
+    return int(lib().mla_uses_fast_path(ctypes.byref(d), int(op)))

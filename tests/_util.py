@@ -1,0 +1,84 @@
+"""Shared helpers of the test suite: tolerances, oracle runs over the seeded
+inputs (the oracle reads the same stored values the GPU reads)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+# max relative error per output tensor: ||g - o||_inf / ||o||_inf
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def rel_err(g, o) -> float:
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    assert g.shape == o.shape, (g.shape, o.shape)
+    if np.isnan(g).any():
+        return float("inf")
+    den = np.max(np.abs(o))
+    return float(np.max(np.abs(g - o)) / (den if den > 0 else 1.0))
+
+
+def lse_err(g, o) -> float:
+    """LSE compared on its own scale (values of order log T): absolute error
+    divided by max(1, max |o|)."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    both_inf = np.isneginf(g) & np.isneginf(o)
+    if np.any(np.isneginf(g) != np.isneginf(o)) or np.isnan(g).any():
+        return float("inf")
+    d = np.where(both_inf, 0.0, np.abs(g - o))
+    return float(np.max(d) / max(1.0, float(np.max(np.abs(np.where(both_inf, 0.0, o))))))
+
+
+def full_path(cfg) -> bool:
+    """Workloads whose every cached row is written from h in the step (the
+    same rule the input builder uses)."""
+    return cfg.prefill or cfg.dtype == "f32"
+
+
+def _weights(cfg, inp):
+    w = O.from_storage(inp["w_dkr"], cfg.dtype)
+    return w[: cfg.d_c], w[cfg.d_c:]
+
+
+def seq_rows(cfg, inp, b):
+    """float64 rows [L, R] of sequence b as the oracle sees them after this
+    step's cache write: rows computed by the oracle from h are rounded to the
+    storage type; pre-written rows are the stored values, gathered through the
+    block table by the oracle's own page addressing."""
+    L = int(inp["seq_lens"][b])
+    w_dkv, w_kr = _weights(cfg, inp)
+    if full_path(cfg):
+        c0, c1 = int(inp["cu_seqlens"][b]), int(inp["cu_seqlens"][b + 1])
+        h = O.from_storage(inp["h"][c0:c1], cfg.dtype)
+        return O.round_storage(O.latent_rows(h, w_dkv, w_kr, inp["positions"][c0:c1], cfg.rope_base), cfg.dtype)
+    rows = O.from_storage(O.gather_rows(inp["rows"], inp["block_table"][b], L), cfg.dtype)
+    if L > 0:
+        h = O.from_storage(inp["h"][b: b + 1], cfg.dtype)
+        new = O.latent_rows(h, w_dkv, w_kr, inp["positions"][b: b + 1], cfg.rope_base)
+        rows[L - 1] = O.round_storage(new, cfg.dtype)[0]
+    return rows
+
+
+def oracle_decode(cfg, inp, seqs, heads=None):
+    """o [len(seqs), H, d_v], lse [len(seqs), H] for the listed sequences."""
+    q = O.from_storage(inp["q"], cfg.dtype)
+    w_uk = O.from_storage(inp["w_uk"], cfg.dtype)
+    w_uv = O.from_storage(inp["w_uv"], cfg.dtype)
+    os_, ls_ = [], []
+    for b in seqs:
+        rows = seq_rows(cfg, inp, b)
+        o, l = O.decode_one(q[b], rows, w_uk, w_uv, int(inp["seq_lens"][b]) - 1, cfg.d_c, cfg.softmax_scale,
+                            cfg.rope_base, heads=heads)
+        os_.append(o)
+        ls_.append(l)
+    return np.stack(os_), np.stack(ls_)
+
+
+def need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a GPU")

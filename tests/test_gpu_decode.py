@@ -1,0 +1,244 @@
+"""GPU parity of the decode path (cache write, query absorption, split-T
+decode + combine) against the CPU oracle, through the C ABI, plus the
+bit-exact properties: untouched cache slots, one-hot projections, page-
+permutation invariance and run-to-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mla_latent_kv_22_amd import harness, inputs as I, mla
+from tests._util import TOL, lse_err, need_gpu, oracle_decode, rel_err, seq_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(label):
+    print(f"[case] {label}", flush=True)
+
+
+# ---------------------------------------------------------------------------- cache write
+
+@pytest.mark.parametrize("cfg", [I.TINY, I.scaled(I.V3, hidden=512, batch=3, seq_len=150, paged=True)],
+                         ids=["tiny_f32", "v3dims_bf16"])
+def test_write_cache_parity_and_untouched_slots(cfg):
+    need_gpu()
+    _case(f"write_cache {cfg.name}")
+    inp = I.make(cfg, 1)
+    dt = cfg.dtype
+    # sentinel pool: every slot holds a recognisable pattern
+    if dt == "bf16":
+        sentinel = np.full(inp["rows"].shape, 0xC0E8, dtype=np.uint16)  # -7.25
+    else:
+        sentinel = np.full(inp["rows"].shape, -7.25, dtype=np.float32)
+    slots = inp["slots"].copy()
+    slots[::5] = -1  # skipped tokens leave their slots untouched
+    inp2 = dict(inp, slots=slots)
+    st = harness.DecodeStep(cfg, inp2, pool=harness.to_device(sentinel, dt))
+    st.write()
+    torch.cuda.synchronize()
+    got = harness.to_host_bits(st.pool)
+    P, R = cfg.page_size, cfg.row_width
+    written = {int(s) for s in slots if s >= 0}
+    g = got.reshape(-1, R)
+    sen = sentinel.reshape(-1, R)
+    untouched = np.array([i for i in range(g.shape[0]) if i not in written], dtype=np.int64)
+    assert np.array_equal(g[untouched], sen[untouched]), "a slot outside slot_mapping changed"
+    w = O.from_storage(inp["w_dkr"], dt)
+    h = O.from_storage(inp["h"], dt)
+    ref = O.latent_rows(h, w[: cfg.d_c], w[cfg.d_c:], inp["positions"], cfg.rope_base)
+    keep = slots >= 0
+    gw = O.from_storage(g[slots[keep]], dt)
+    assert rel_err(gw, ref[keep]) < TOL[dt]
+    # per element: within one storage ulp of the float64 row (plus a small
+    # absolute floor for entries that cancel to near zero) nearly everywhere
+    r = ref[keep]
+    ulp = 2.0 ** -8 if dt == "bf16" else 2.0 ** -20
+    ok = np.abs(gw - r) <= ulp * np.abs(r) + 1e-3 * np.sqrt(np.mean(r * r))
+    assert np.mean(ok) > 0.999
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_write_cache_one_hot_is_exact(dt):
+    """Selection rows in W_DKR and position 0 (RoPE is the identity): the
+    written row is exactly the selected hidden values."""
+    need_gpu()
+    _case(f"write_cache one-hot {dt}")
+    cfg = I.scaled(I.V3, hidden=640, batch=2, seq_len=64, dtype=dt)
+    inp = I.make(cfg, 2)
+    rng = np.random.default_rng(3)
+    sel = rng.permutation(cfg.hidden)[: cfg.row_width]
+    w = np.zeros((cfg.row_width, cfg.hidden), dtype=np.float32)
+    w[np.arange(cfg.row_width), sel] = 1.0
+    inp["w_dkr"] = I.f32_to_bf16_bits(w) if dt == "bf16" else w
+    inp["positions"] = np.zeros_like(inp["positions"])
+    st = harness.DecodeStep(cfg, inp)
+    st.write()
+    torch.cuda.synchronize()
+    got = harness.to_host_bits(st.pool).reshape(-1, cfg.row_width)[inp["slots"]]
+    assert np.array_equal(got, inp["h"][:, sel])
+
+
+# ---------------------------------------------------------------------------- absorption
+
+@pytest.mark.parametrize("cfg", [I.TINY, I.scaled(I.V3, batch=5)], ids=["tiny_f32", "v3_bf16"])
+def test_absorb_q_parity(cfg):
+    need_gpu()
+    _case(f"absorb_q {cfg.name}")
+    inp = I.make(cfg, 4, with_rows=False)
+    st = harness.DecodeStep(cfg, inp)
+    st.absorb()
+    torch.cuda.synchronize()
+    got = O.from_storage(harness.to_host_bits(st.q_abs), cfg.dtype)
+    q = O.from_storage(inp["q"], cfg.dtype)
+    ref = O.absorb_query(q, O.from_storage(inp["w_uk"], cfg.dtype), inp["q_positions"], cfg.qk_nope, cfg.rope_base)
+    assert rel_err(got[..., : cfg.d_c], ref[..., : cfg.d_c]) < TOL[cfg.dtype]
+    assert rel_err(got[..., cfg.d_c:], ref[..., cfg.d_c:]) < TOL[cfg.dtype]
+
+
+# ---------------------------------------------------------------------------- decode
+
+def _run_step(cfg, inp, flags=0):
+    st = harness.DecodeStep(cfg, inp, flags=flags)
+    st.step()
+    torch.cuda.synchronize()
+    return st
+
+
+def _check(cfg, inp, st, seqs, heads=None):
+    o_ref, l_ref = oracle_decode(cfg, inp, seqs, heads)
+    out = O.from_storage(harness.to_host_bits(st.out), cfg.dtype)[seqs]
+    lse = st.lse.cpu().numpy().astype(np.float64)[seqs]
+    if heads is not None:
+        out, lse, o_ref, l_ref = out[:, heads], lse[:, heads], o_ref[:, heads], l_ref[:, heads]
+    e_o, e_l = rel_err(out, o_ref), lse_err(lse, l_ref)
+    print(f"  out rel err {e_o:.3e}  lse err {e_l:.3e}", flush=True)
+    assert e_o < TOL[cfg.dtype]
+    assert e_l < TOL[cfg.dtype]
+
+
+def test_decode_tiny_f32_full_path():
+    """Tiny fp32 step: all 512 rows written by the GPU from h, then absorb and
+    decode; the oracle runs the non-absorbed form from the same h."""
+    need_gpu()
+    _case("decode tiny_f32 full path")
+    cfg = I.TINY
+    inp = I.make(cfg, 0)
+    st = _run_step(cfg, inp)
+    _check(cfg, inp, st, list(range(cfg.batch)))
+
+
+def test_decode_tiny_sharp_softmax():
+    """Weights 10x larger: a peaked softmax that is sensitive to score errors."""
+    need_gpu()
+    _case("decode tiny sharp")
+    cfg = I.scaled(I.TINY, weight_std=0.2)
+    inp = I.make(cfg, 7)
+    st = _run_step(cfg, inp)
+    _check(cfg, inp, st, list(range(cfg.batch)))
+
+
+@pytest.mark.parametrize("flags", [0, mla.FLAG_GENERIC], ids=["mfma", "generic"])
+def test_decode_v2lite(flags):
+    need_gpu()
+    cfg = I.V2LITE
+    _case(f"decode v2lite flags={flags}")
+    inp = I.make(cfg, 0)
+    st = _run_step(cfg, inp, flags)
+    assert mla.uses_fast_path(st.d, mla.OP_DECODE) == (0 if flags else 1)
+    _check(cfg, inp, st, [0, 7, 15])
+
+
+@pytest.mark.parametrize("lens", [[1, 2, 31, 32, 33, 63, 64, 65], [0, 257, 300, 1000, 5, 4097, 128, 96]],
+                         ids=["short", "mixed_with_empty"])
+@pytest.mark.parametrize("heads", [128, 16, 40])
+def test_decode_ragged_edges(lens, heads):
+    """Lengths around tile (32) and page (64) boundaries, an empty sequence,
+    head counts that fill 4, 1 and 2 waves; random page permutation."""
+    need_gpu()
+    _case(f"decode ragged edges lens={lens} H={heads}")
+    cfg = I.scaled(I.RAGGED, hidden=512, num_heads=heads, batch=len(lens), seq_len=max(lens), min_seq_len=1)
+    inp = I.make(cfg, 11, lengths=lens)
+    lens = np.array(lens, dtype=np.int32)
+    st = _run_step(cfg, inp)
+    nz = [b for b in range(len(lens)) if lens[b] > 0]
+    _check(cfg, inp, st, nz)
+    z = [b for b in range(len(lens)) if lens[b] == 0]
+    for b in z:
+        assert np.all(harness.to_host_bits(st.out)[b].astype(np.uint16) == 0)
+        assert np.all(np.isneginf(st.lse.cpu().numpy()[b]))
+
+
+@pytest.mark.parametrize("flags", [0, mla.FLAG_GENERIC], ids=["mfma", "generic"])
+def test_page_permutation_bit_invariance_and_determinism(flags):
+    need_gpu()
+    _case(f"page permutation invariance flags={flags}")
+    cfg = I.scaled(I.RAGGED, hidden=512, batch=6, seq_len=3000, min_seq_len=200)
+    inp = I.make(cfg, 5)
+    st = _run_step(cfg, inp, flags)
+    out1, lse1 = harness.to_host_bits(st.out).copy(), st.lse.cpu().numpy().copy()
+    st.attend()
+    torch.cuda.synchronize()
+    assert np.array_equal(harness.to_host_bits(st.out), out1), "two runs differ"
+    assert np.array_equal(st.lse.cpu().numpy(), lse1)
+    # move every page to a new place and rewrite the block table
+    pool = harness.to_host_bits(st.pool)
+    perm = np.random.default_rng(9).permutation(pool.shape[0])
+    moved = np.empty_like(pool)
+    moved[perm] = pool
+    bt = inp["block_table"].copy()
+    used = bt >= 0
+    bt = np.where(used, perm[bt], bt).astype(np.int32)
+    st.block_table = harness.to_device(bt, "i32")
+    st.attend(pool=harness.to_device(moved, cfg.dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(harness.to_host_bits(st.out), out1), "page placement changed the result"
+    assert np.array_equal(st.lse.cpu().numpy(), lse1)
+
+
+def test_position_branch_matters_on_gpu():
+    """Zeroing the rotary half of the stored rows changes the GPU output far
+    beyond the tolerance (the position branch is really read)."""
+    need_gpu()
+    _case("position branch")
+    cfg = I.scaled(I.V2LITE, batch=2, seq_len=512)
+    inp = I.make(cfg, 13)
+    st = _run_step(cfg, inp)
+    o1 = O.from_storage(harness.to_host_bits(st.out), "bf16")
+    rows = inp["rows"].copy()
+    rows[..., cfg.d_c:] = 0
+    st2 = harness.DecodeStep(cfg, dict(inp, rows=rows))
+    st2.absorb()
+    st2.attend()
+    torch.cuda.synchronize()
+    o2 = O.from_storage(harness.to_host_bits(st2.out), "bf16")
+    assert rel_err(o2, o1) > 20 * TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------- full-size cases
+
+@pytest.mark.slow
+def test_decode_v3_full_size():
+    """B=64, T=8192, H=128 in the launch configuration the benchmark times;
+    the oracle checks two sequences over all heads and two more over 16 heads."""
+    need_gpu()
+    _case("decode v3 full size")
+    cfg = I.V3
+    inp = I.make(cfg, 0)
+    st = _run_step(cfg, inp)
+    _check(cfg, inp, st, [0, 41])
+    _check(cfg, inp, st, [17, 63], heads=list(range(0, 128, 8)))
+
+
+@pytest.mark.slow
+def test_decode_ragged_paged_full_size():
+    """B=128, lengths U{512..32768}, random page permutation: the longest, the
+    shortest and two seeded sequences, 12 heads each."""
+    need_gpu()
+    _case("decode ragged paged full size")
+    cfg = I.RAGGED
+    inp = I.make(cfg, 0)
+    st = _run_step(cfg, inp)
+    lens = inp["seq_lens"]
+    seqs = [int(np.argmax(lens)), int(np.argmin(lens))] + [int(x) for x in np.random.default_rng(1).choice(128, 2)]
+    _check(cfg, inp, st, seqs, heads=[0, 1, 31, 32, 63, 64, 65, 95, 96, 100, 126, 127])
