@@ -1,0 +1,179 @@
+"""Benchmark of one MLA decode step on one MI355X.
+
+A step is the whole decode hot path on one batch: write the newest latent row
+of every sequence (mla_write_cache), absorb W_UK into the queries
+(mla_absorb_q), then split-T decode + LSE-merge combine with W_UV
+(mla_decode).  Default workload: DeepSeek-V3 attention shapes, B=64 sequences
+of T=8192 cached tokens, H=128 heads, d_c=512, d_R=64, bf16, page size 64.
+
+Prints one JSON line.  `value` is latent-cache GB/s of the step: the
+algorithmic bytes (sum of sequence lengths x 576 values x 2 bytes) divided by
+the step time; tokens/s (sequences decoded per second, per layer) rides along.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload v3_decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_v3_counters.json")
+DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_22_amd", "csrc", "k_decode_mfma.hip")
+
+
+def _src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(n_steps_note=""):
+    """HBM bytes per decode call from committed rocprofv3 counter runs, or None
+    when the counters are absent or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != _src_hash(DECODE_SRC):
+        return None
+    return t.get("bytes_per_decode_call")
+
+
+def cpu_baseline(cfg, inp):
+    """Time the float64 oracle on a bounded sample of the same workload: one
+    sequence over 16 of its heads (the oracle's cost is linear in both)."""
+    import numpy as np
+    import oracle as O
+    from tests._util import oracle_decode
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    heads = list(range(0, cfg.num_heads, max(1, cfg.num_heads // 16)))[:16]
+    t0 = time.perf_counter()
+    oracle_decode(cfg, inp, [0], heads)
+    dt = time.perf_counter() - t0
+    frac = (1.0 / cfg.batch) * (len(heads) / cfg.num_heads)
+    total_bytes = float(np.sum(inp["seq_lens"].astype(np.int64))) * cfg.row_width * 2
+    return {"value": round(total_bytes * frac / dt / 1e9, 9), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"sequence 0 ({int(inp['seq_lens'][0])} tokens) x {len(heads)} of {cfg.num_heads} heads, "
+                      f"float64 NumPy, non-absorbed; scaled to the full workload by the sample fraction {frac:.6f}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="v3_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); multi-GPU runs are not part of this "
+              f"library's measurements", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mla_latent_kv_22_amd import harness, inputs as I, mla
+
+    mla.lib()
+    cfg = I.CONFIGS[args.workload]
+    if cfg.prefill:
+        raise SystemExit("use the decode workloads here; prefill is timed in the prefill block")
+    print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
+    inp = I.make(cfg, 0)
+    st = harness.DecodeStep(cfg, inp)
+    # two pool copies, alternated per step, so no step finds the cache warm in
+    # the 256 MB Infinity Cache from the step before
+    pools = [st.pool, st.pool.clone()]
+    stream = torch.cuda.current_stream()
+    algo_bytes = int(np.sum(inp["seq_lens"].astype(np.int64))) * cfg.row_width * 2
+
+    def step(i):
+        st.step(pool=pools[i % 2])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print("[bench] warm", file=sys.stderr, flush=True)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-phase timing: each phase alone, same stream, per-call events
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            evs[i][0].record(stream)
+            fn(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    t_write = timed(lambda i: mla.write_cache(st.d, st.h, st.w_dkr, st.positions, st.slots, pools[i % 2]),
+                    args.steps)
+    t_absorb = timed(lambda i: st.absorb(), args.steps)
+    t_decode = timed(lambda i: st.attend(pool=pools[i % 2]), args.steps)
+    dec_ms = float(np.mean(t_decode))
+
+    flops = 2.0 * cfg.num_heads * (cfg.row_width + cfg.d_c) * float(np.sum(inp["seq_lens"]))
+    achieved = algo_bytes / (dec_ms * 1e-3) / 1e9
+    res = {
+        "metric": "MLA decode latent-cache GB/s (% HBM peak) + tokens/s at B=64,T=8k,H=128",
+        "value": round(algo_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latent rows and hidden states, N(0,0.02^2) weights)",
+        "config": {"workload": f"{cfg.name}: B={cfg.batch} T={cfg.seq_len}{' (max, ragged)' if cfg.min_seq_len else ''} "
+                               f"H={cfg.num_heads} d_c={cfg.d_c} d_R={cfg.d_r} d_v={cfg.v_head} bf16 page={cfg.page_size}",
+                   "batch": cfg.batch, "context": cfg.seq_len, "heads": cfg.num_heads,
+                   "step": "write_cache(B rows) + absorb_q + decode(split + combine)",
+                   "cache_copies_rotated": 2},
+        "pct_hbm_peak": round(100.0 * algo_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(cfg.batch / (ms_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": algo_bytes,
+        "phases_ms": {"write_cache": round(float(np.mean(t_write)), 5), "absorb_q": round(float(np.mean(t_absorb)), 5),
+                      "decode": round(dec_ms, 5),
+                      "decode_p50_p95_p99": [round(float(np.percentile(t_decode, p)), 5) for p in (50, 95, 99)]},
+        "roofline": {"kernel": "mla_decode (split-T pass + combine, one stream)", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(),
+                     "mfma_tflops": round(flops / (dec_ms * 1e-3) / 1e12, 1),
+                     "mfma_frac_of_bf16_peak": round(flops / (dec_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

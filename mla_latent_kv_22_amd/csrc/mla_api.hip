@@ -42,6 +42,14 @@ int current_cus() {
   return cus;
 }
 
+bool bf16_fast(const mla_dims_t* d) { return d->dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC); }
+
+bool write_fast(const mla_dims_t* d) { return bf16_fast(d) && write_mfma_supported(d->hidden, d->d_c, d->d_r); }
+
+bool absorb_fast(const mla_dims_t* d) {
+  return bf16_fast(d) && absorb_mfma_supported(d->num_heads, d->qk_nope, d->d_c, d->d_r);
+}
+
 bool decode_fast(const mla_dims_t* d, int batch) {
   return d->dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC) &&
          decode_mfma_supported(d->num_heads, d->d_c, d->d_r, d->v_head, d->page_size, batch);
@@ -101,9 +109,13 @@ size_t mla_cache_bytes(const mla_dims_t* dims, int64_t tokens, int32_t layers) {
 int mla_uses_fast_path(const mla_dims_t* dims, int32_t op) {
   const int st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (op == 2) return decode_fast(dims, 1) ? 1 : 0;
-  if (op < 0 || op > 3) return MLA_ERR_ARG;
-  return 0;
+  switch (op) {
+    case 0: return write_fast(dims) ? 1 : 0;
+    case 1: return absorb_fast(dims) ? 1 : 0;
+    case 2: return decode_fast(dims, 1) ? 1 : 0;
+    case 3: return 0;
+    default: return MLA_ERR_ARG;
+  }
 }
 
 int mla_write_cache(const mla_dims_t* dims, const void* h, const void* w_dkr, const int32_t* positions,
@@ -116,6 +128,7 @@ int mla_write_cache(const mla_dims_t* dims, const void* h, const void* w_dkr, co
   if (!h || !w_dkr || !positions || !slot_mapping || !pool) return MLA_ERR_NULL;
   WriteCacheArgs a{h, w_dkr, positions, slot_mapping, pool, n_tokens, dims->hidden, dims->d_c, dims->d_r,
                    dims->page_size, dims->rope_base};
+  if (write_fast(dims)) return launched(write_cache_mfma(a, stream));
   return launched(write_cache_generic(a, dims->dtype == MLA_BF16, stream));
 }
 
@@ -128,6 +141,7 @@ int mla_absorb_q(const mla_dims_t* dims, const void* q, const void* w_uk, const 
   if (!q || !w_uk || !positions || !q_abs) return MLA_ERR_NULL;
   AbsorbArgs a{q, w_uk, positions, q_abs, n_tokens, dims->num_heads, dims->qk_nope, dims->d_c, dims->d_r,
                dims->rope_base};
+  if (absorb_fast(dims)) return launched(absorb_mfma(a, stream));
   return launched(absorb_generic(a, dims->dtype == MLA_BF16, stream));
 }
 

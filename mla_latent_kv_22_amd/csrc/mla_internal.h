@@ -75,7 +75,13 @@ hipError_t absorb_generic(const AbsorbArgs& a, bool bf16, hipStream_t s);
 hipError_t decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s);
 hipError_t prefill_generic(const PrefillArgs& a, bool bf16, hipStream_t s);
 
-// MFMA kernels (bf16, latent width 512, rotary width 64)
+// MFMA projection kernels (bf16)
+bool write_mfma_supported(int D, int d_c, int d_r);
+hipError_t write_cache_mfma(const WriteCacheArgs& a, hipStream_t s);
+bool absorb_mfma_supported(int H, int d_n, int d_c, int d_r);
+hipError_t absorb_mfma(const AbsorbArgs& a, hipStream_t s);
+
+// MFMA decode kernels (bf16, latent width 512, rotary width 64)
 bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch);
 int decode_mfma_slots(int H, int cus);
 hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s);

@@ -19,11 +19,15 @@ def _case(label):
 
 # ---------------------------------------------------------------------------- cache write
 
-@pytest.mark.parametrize("cfg", [I.TINY, I.scaled(I.V3, hidden=512, batch=3, seq_len=150, paged=True)],
-                         ids=["tiny_f32", "v3dims_bf16"])
-def test_write_cache_parity_and_untouched_slots(cfg):
+@pytest.mark.parametrize("cfg,flags", [
+    (I.TINY, 0),
+    (I.scaled(I.V3, hidden=512, batch=3, seq_len=150, paged=True), 0),
+    (I.scaled(I.V3, hidden=512, batch=3, seq_len=150, paged=True), mla.FLAG_GENERIC),
+    (I.scaled(I.PREFILL, hidden=512, batch=3, seq_len=700), 0),   # > 1024 tokens: wide token blocks
+], ids=["tiny_f32", "v3dims_bf16_mfma", "v3dims_bf16_generic", "prefill_rows_mfma"])
+def test_write_cache_parity_and_untouched_slots(cfg, flags):
     need_gpu()
-    _case(f"write_cache {cfg.name}")
+    _case(f"write_cache {cfg.name} flags={flags}")
     inp = I.make(cfg, 1)
     dt = cfg.dtype
     # sentinel pool: every slot holds a recognisable pattern
@@ -34,7 +38,9 @@ def test_write_cache_parity_and_untouched_slots(cfg):
     slots = inp["slots"].copy()
     slots[::5] = -1  # skipped tokens leave their slots untouched
     inp2 = dict(inp, slots=slots)
-    st = harness.DecodeStep(cfg, inp2, pool=harness.to_device(sentinel, dt))
+    st = harness.DecodeStep(cfg, inp2, flags=flags, pool=harness.to_device(sentinel, dt))
+    if dt == "bf16":
+        assert mla.uses_fast_path(st.d, mla.OP_WRITE_CACHE) == (0 if flags else 1)
     st.write()
     torch.cuda.synchronize()
     got = harness.to_host_bits(st.pool)
@@ -81,12 +87,16 @@ def test_write_cache_one_hot_is_exact(dt):
 
 # ---------------------------------------------------------------------------- absorption
 
-@pytest.mark.parametrize("cfg", [I.TINY, I.scaled(I.V3, batch=5)], ids=["tiny_f32", "v3_bf16"])
-def test_absorb_q_parity(cfg):
+@pytest.mark.parametrize("cfg,flags", [(I.TINY, 0), (I.scaled(I.V3, batch=5), 0),
+                                       (I.scaled(I.V3, batch=5), mla.FLAG_GENERIC), (I.scaled(I.V3, batch=70), 0)],
+                         ids=["tiny_f32", "v3_bf16_mfma", "v3_bf16_generic", "v3_bf16_mfma_70tok"])
+def test_absorb_q_parity(cfg, flags):
     need_gpu()
-    _case(f"absorb_q {cfg.name}")
+    _case(f"absorb_q {cfg.name} flags={flags}")
     inp = I.make(cfg, 4, with_rows=False)
-    st = harness.DecodeStep(cfg, inp)
+    st = harness.DecodeStep(cfg, inp, flags=flags)
+    if cfg.dtype == "bf16":
+        assert mla.uses_fast_path(st.d, mla.OP_ABSORB_Q) == (0 if flags else 1)
     st.absorb()
     torch.cuda.synchronize()
     got = O.from_storage(harness.to_host_bits(st.q_abs), cfg.dtype)
