@@ -24,10 +24,8 @@ FLAGS = [
 ]
 
 
-# per-file extra flags: the split-decode kernel keeps its 32x512 fp32
-# accumulator in the MFMA VGPR form, which lets the register allocator place
-# it beside the query fragments without spilling
-EXTRA = {"k_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# per-file extra flags (none at present)
+EXTRA = {}
 
 
 def _compile(src: str, verbose: bool) -> str:

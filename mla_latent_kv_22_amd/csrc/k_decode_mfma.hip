@@ -8,10 +8,11 @@
 //   scores  S^T[t][h] = row_t . q~_h          (MFMA 32x32x16, k = 576 features)
 //   latent  O^T[f][h] += C^T[f][t] P^T[t][h]  (MFMA 32x32x16, k = 32 tokens)
 // The C^T operand comes straight from the row-major tile through the LDS
-// transpose read (ds_read_b64_tr_b16), so no transposed copy is staged.  The
-// softmax is online with a lazily moved reference maximum: the accumulator is
-// rescaled only when a head's running maximum grows by more than 8 (log2
-// units), which keeps every exp2 below 256 and leaves the result exact.
+// transpose read (ds_read_b64_tr_b16), so no transposed copy is staged.  Each
+// item fixes its per-head reference maximum on its first tile and never
+// rescales the accumulator (the merge stays exact: every partial carries its
+// own reference); a score more than 2^64 above the reference would overflow,
+// so such an (item, head) is flagged and recomputed exactly by the combine.
 // Pass 2 (combine): per (head, 32 sequences): LSE-merge of the items in a
 // fixed order, the merged latent split into bf16 hi + lo parts, and W_UV
 // applied with MFMA (so the fp32 latent reaches the product intact to ~2^-17).
@@ -30,7 +31,7 @@ constexpr int TILE_BYTES = TILE_CHUNKS * 16;  // 36864
 constexpr int LOADS_PER_TILE = TILE_CHUNKS / 64;  // 36 wave-wide 16-byte loads
 constexpr int KS = RW / 16;        // 36 k-steps of the score MFMA
 constexpr int FB = DC / 32;        // 16 f-blocks of the latent accumulator
-constexpr float kLazy = 8.f;       // rescale threshold, log2 units
+constexpr float kHeadroom = 64.f;  // largest score above the item's reference, log2 units
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -51,45 +52,78 @@ __device__ __forceinline__ constexpr int waitcnt_vm(int n) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Wave-wide load i (0..35) of a tile fills LDS bytes [1024 i, 1024 i + 1024):
-// column group cg = i / 4, rows 8 (i % 4) .. +7.  Lane l takes row
-// r = 8 (i % 4) + l / 8 and the chunk whose swizzled slot is l % 8, so its
-// global byte offset is lane_off(l, i % 2) + 9216 (i % 4) + 128 (i / 4): the
-// swizzle of row r depends on bit 3 of r, which is the parity of i % 4.
-__device__ __forceinline__ uint32_t load_lane_off(int lane, int odd) {
-  const int r = lane >> 3;
-  return (uint32_t)(r * (RW * 2) + (((lane & 7) ^ swz(r + 8 * odd)) << 4));
+// two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
-// One wave-wide 16-byte direct-to-LDS load: lane l's 16 bytes at
-// sbase + voff land at LDS byte lds_addr + 16 l.  Written as inline asm so the
-// compiler does not add its own conservative wait for every load in flight
-// before each LDS read; the tile loop waits explicitly (s_waitcnt vmcnt +
-// barrier) for exactly the tile it reads.  The instruction writes no VGPR.
+// The score chain keeps its accumulator in VGPRs (inline asm) while the
+// latent accumulator owns the AGPRs (compiler MFMA form).  Hazards the
+// compiler cannot see for the asm chain are covered here: its operands come
+// from LDS reads or global loads (waited for by the compiler through the asm
+// inputs), and score_drain() puts 20 wait states between the last MFMA and
+// the first VALU read of the scores (a 16-pass MFMA needs 18).
+__device__ __forceinline__ void score_first(f32x16& acc, const u32x4& a, const u32x4& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void score_next(f32x16& acc, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void score_drain(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc));
+}
+__device__ __forceinline__ void latent_mfma(f32x16& acc, const u32x4& a, const u32x4& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
+}
+
+// Direct-to-LDS loads of one tile.  Wave w of NW issues loads i = w, w+NW, ...
+// of the 36; load i fills LDS bytes [1024 i, +1024) = column group i / 4,
+// rows 8 (i % 4) .. +7, lane l taking row 8 (i % 4) + l / 8 and the chunk
+// whose swizzled slot is l % 8.  Its global byte offset is
+// lane_off(l, i % 4) + 128 (i / 4); with NW = 4 the row block i % 4 = w is
+// fixed per wave, so one lane offset serves all nine loads.  Written as inline asm so the compiler adds no wait of its own
+// before LDS reads; the tile loop waits explicitly for exactly the tile it
+// reads.  The instruction writes no VGPR.
+__device__ __forceinline__ uint32_t load_lane_off(int lane, int rb) {
+  const int r = 8 * rb + (lane >> 3);
+  return (uint32_t)(r * (RW * 2) + (((lane & 7) ^ swz(r)) << 4));
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+template <int COL>
 __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
+      "global_load_lds_dwordx4 %0, %1 offset:%3"
       :
-      : "v"(voff), "s"(sbase), "s"(lds_addr)
+      : "v"(voff), "s"(sbase), "s"(lds_addr), "i"(COL)
       : "memory", "m0");
 }
 
-__device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+template <int NW, int I0>
+__device__ __forceinline__ void issue_full(const char* tile_base, uint32_t lds0, int w, const uint32_t* lane_off) {
+  if constexpr (I0 < LOADS_PER_TILE) {
+    const int i = I0 + w;
+    // column offset 128 * (i / 4) goes into the scalar base (the instruction's
+    // immediate offset would move the LDS destination as well)
+    if constexpr (NW == 4) {
+      dma16<0>(tile_base + 32 * I0, lane_off[0], lds0 + 1024 * i);
+    } else {
+      dma16<0>(tile_base + 128 * (i >> 2), lane_off[i & 3], lds0 + 1024 * i);
+    }
+    issue_full<NW, I0 + NW>(tile_base, lds0, w, lane_off);
+  }
 }
 
 template <int NW>
-__device__ __forceinline__ void issue_tile(const char* __restrict__ tile_base, int nvalid, char* stage, int w,
-                                           int lane, uint32_t lane_off0, uint32_t lane_off1) {
-  const uint32_t lds0 = lds_addr_of(stage);
+__device__ __forceinline__ void issue_tile(const char* __restrict__ tile_base, int nvalid, uint32_t lds0, int w,
+                                           int lane, const uint32_t* lane_off) {
   if (nvalid == TT) {
-#pragma unroll
-    for (int i0 = 0; i0 < LOADS_PER_TILE; i0 += NW) {
-      const int i = i0 + w;
-      dma16(tile_base + (9216 * (i & 3) + 128 * (i >> 2)), (i & 1) ? lane_off1 : lane_off0, lds0 + 1024 * i);
-    }
+    issue_full<NW, 0>(tile_base, lds0, w, lane_off);
   } else {
     // ragged tail: rows past the last valid token repeat it (their p is 0)
 #pragma unroll
@@ -98,27 +132,140 @@ __device__ __forceinline__ void issue_tile(const char* __restrict__ tile_base, i
       const int r = 8 * (i & 3) + (lane >> 3);
       const int rr = r < nvalid ? r : nvalid - 1;
       const int c = 8 * (i >> 2) + ((lane & 7) ^ swz(r));
-      dma16(tile_base, (uint32_t)(rr * (RW * 2) + c * 16), lds0 + 1024 * i);
+      dma16<0>(tile_base, (uint32_t)(rr * (RW * 2) + c * 16), lds0 + 1024 * i);
     }
   }
 }
 
-// Three stage buffers as separate LDS objects: the compiler can then tell the
-// direct-to-LDS loads of one stage from reads of another and waits only for
-// the tile being read instead of every load in flight.
+// Per-lane LDS byte offsets of the operand reads, relative to a stage base.
+struct ReadOffsets {
+  int s[4];     // score A operand (row = lane % 32, chunk 2 ks + g): + 4096 (ks / 4)
+  int t[2][2];  // transpose reads [fb parity][upper 8 rows]: + 4096 (fb / 2) + 2048 kk
+};
+
+// Scores of one tile: S^T[t][h] = sum_f row_t[f] q~_h[f], chained MFMAs with
+// K fragments read 3 ahead; optionally interleaved one-for-one with the 32
+// latent MFMAs O^T += C^T P^T of the previous tile (transpose reads 2 ahead).
+template <bool WITH_LATENT>
+__device__ __forceinline__ void tile_mfma(f32x16& sacc, const char* ts, const u32x4* qf, f32x16* acc,
+                                          const char* tp, const u32x4* pb, const ReadOffsets& o) {
+  constexpr int PF = 3, PF2 = 2, NPC = 2 * FB;
+  u32x4 kf[PF];
+#pragma unroll
+  for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x4*)(ts + o.s[ks & 3] + 4096 * (ks >> 2));
+  auto tr_a = [&](int idx) {
+    const int kk = idx / FB, fb = idx % FB;
+    const int imm = 4096 * (fb >> 1) + 2048 * kk;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][0] + imm));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][1] + imm + 1024));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
+  u32x4 av[PF2];
+  if constexpr (WITH_LATENT) {
+#pragma unroll
+    for (int i = 0; i < PF2; ++i) av[i] = tr_a(i);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 cur = kf[ks % PF];
+    if (ks + PF < KS) kf[ks % PF] = *(const u32x4*)(ts + o.s[(ks + PF) & 3] + 4096 * ((ks + PF) >> 2));
+    if (ks == 0) score_first(sacc, cur, qf[ks]);
+    else score_next(sacc, cur, qf[ks]);
+    if constexpr (WITH_LATENT) {
+      if (ks < NPC) {
+        const u32x4 ca = av[ks % PF2];
+        if (ks + PF2 < NPC) av[ks % PF2] = tr_a(ks + PF2);
+        latent_mfma(acc[ks % FB], ca, pb[ks / FB]);
+      }
+    }
+  }
+  score_drain(sacc);
+}
+
+// The 32 latent MFMAs of the last tile (no next tile to score).
+__device__ __forceinline__ void latent_only(f32x16* acc, const char* tp, const u32x4* pb, const ReadOffsets& o) {
+  constexpr int PF2 = 2, NPC = 2 * FB;
+  auto tr_a = [&](int idx) {
+    const int kk = idx / FB, fb = idx % FB;
+    const int imm = 4096 * (fb >> 1) + 2048 * kk;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][0] + imm));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][1] + imm + 1024));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
+  u32x4 av[PF2];
+#pragma unroll
+  for (int i = 0; i < PF2; ++i) av[i] = tr_a(i);
+#pragma unroll
+  for (int i = 0; i < NPC; ++i) {
+    const u32x4 ca = av[i % PF2];
+    if (i + PF2 < NPC) av[i % PF2] = tr_a(i + PF2);
+    latent_mfma(acc[i % FB], ca, pb[i / FB]);
+  }
+}
+
+// Softmax numerators of one tile for head lane % 32: p = 2^(s sl2 - m_ref)
+// rounded to bf16 (the P operand of the latent MFMA), their sum in lsum.
+// Tokens at or past t1 (only in a ragged last tile) get p = 0.
+__device__ __forceinline__ void tile_softmax(const f32x16& sacc, int tok0, int t1, int g, float sl2, float m_ref,
+                                             u32x4* pb, float& lsum) {
+  const bool full = tok0 + TT <= t1;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    uint32_t wds[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int j = 8 * kk + e;
+      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], sl2, -m_ref));
+      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j + 1], sl2, -m_ref));
+      if (!full) {
+        const int t = 8 * (j >> 2) + 4 * g + (j & 3);  // tokens of j and j + 1 are t and t + 1
+        if (tok0 + t >= t1) p0 = 0.f;
+        if (tok0 + t + 1 >= t1) p1 = 0.f;
+      }
+      const uint32_t pk = pack_bf16x2(p0, p1);  // hardware round-to-nearest-even
+      lsum += __uint_as_float(pk << 16) + __uint_as_float(pk & 0xffff0000u);
+      wds[e >> 1] = pk;
+    }
+    pb[kk] = u32x4{wds[0], wds[1], wds[2], wds[3]};
+  }
+}
+
+// Largest score of the tile for this lane's head (both lane halves), raw units.
+__device__ __forceinline__ float tile_max(const f32x16& sacc, int tok0, int t1, int g) {
+  float mt = -INFINITY;
+  if (tok0 + TT <= t1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int t = 8 * (j >> 2) + 4 * g + (j & 3);
+      if (tok0 + t < t1) mt = fmaxf(mt, sacc[j]);
+    }
+  }
+  return fmaxf(mt, __shfl_xor(mt, 32));
+}
+
+// Four stage buffers of one tile each.  The planner's two per-sequence arrays
+// live in stage 3 until the first load into it (every read of them happens
+// before the barrier that precedes that load).
+constexpr int NSTAGE = 4;
+constexpr int PLAN_INTS = 2 * (kMaxDecodeBatch + 1);
+static_assert(PLAN_INTS * 4 <= TILE_BYTES, "planner arrays must fit in one stage");
+
 template <int NW>
 __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char tile0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char tile1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char tile2[TILE_BYTES];
-  __shared__ int s_len[kMaxDecodeBatch + 1];
-  __shared__ int s_items[kMaxDecodeBatch + 1];
+  __shared__ __attribute__((aligned(16))) char tiles[NSTAGE * TILE_BYTES];
   __shared__ int red[16];
   __shared__ int s_pages[kMaxItemPages];
+  int* s_len = (int*)(tiles + 3 * TILE_BYTES);
+  int* s_items = s_len + (kMaxDecodeBatch + 1);
 
   const int cap = a.len_cap;
-  const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk, a.ovh_tokens,
-                                           s_len, s_items, red);
+  const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
+                                           a.ovh_tokens, s_len, s_items, red);
   const int n_items = plan.n_items;
   if ((int)blockIdx.x >= n_items) return;
   // consecutive items (same sequence) share an XCD: work-group i runs on XCD i % 8
@@ -126,7 +273,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
   if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
 
   // wave-uniform values read from LDS are moved to scalar registers so that
-  // block-table reads and tile addresses stay scalar
+  // page lookups and tile addresses stay scalar
   const int b = __builtin_amdgcn_readfirstlane(item_seq(s_items, a.batch, item));
   const int chunk = __builtin_amdgcn_readfirstlane(plan.chunk);
   const int t0 = (item - __builtin_amdgcn_readfirstlane(s_items[b])) * chunk;
@@ -135,40 +282,29 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
   const int g = lane >> 5, hl = lane & 31;
   const int hq = w * 32 + hl;
   const bool hvalid = hq < a.H;
-
+  const int P = a.P;
   const char* __restrict__ pool = (const char*)a.pool;
   const int ntiles = (t1 - t0 + TT - 1) / TT;
-  const uint32_t lane_off0 = load_lane_off(lane, 0), lane_off1 = load_lane_off(lane, 1);
-  const int P = a.P;
-  // the item's pages, staged once so the tile loop reads them from LDS
   {
     const int32_t* __restrict__ bt = a.block_table + (size_t)b * a.max_pages_per_seq;
     const int p0 = t0 / P, np = (t1 - 1) / P - p0 + 1;
     for (int i = threadIdx.x; i < np; i += blockDim.x) s_pages[i] = bt[p0 + i];
-    __syncthreads();
   }
+  __syncthreads();  // pages staged; planner arrays no longer read
   const int page0 = t0 / P;
-
   auto tile_ptr = [&](int tile, int& nvalid) {
     const int tok0 = t0 + tile * TT;
     nvalid = min(TT, t1 - tok0);
     const int page = __builtin_amdgcn_readfirstlane(s_pages[tok0 / P - page0]);
     return pool + ((size_t)page * P + (tok0 % P)) * (RW * 2);
   };
+  const uint32_t lds_tiles = lds_addr_of(tiles);
+  uint32_t lane_off[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) lane_off[rb] = load_lane_off(lane, NW == 4 ? w : rb);
 
-  // prologue: the first two tiles in flight
-  if (0 < ntiles) {
-    int nv;
-    const char* tp = tile_ptr(0, nv);
-    issue_tile<NW>(tp, nv, tile0, w, lane, lane_off0, lane_off1);
-  }
-  if (1 < ntiles) {
-    int nv;
-    const char* tp = tile_ptr(1, nv);
-    issue_tile<NW>(tp, nv, tile1, w, lane, lane_off0, lane_off1);
-  }
-
-  // absorbed query fragments: B operand of the score MFMA, k = features
+  // absorbed query fragments (B operand of the score MFMA), loaded before the
+  // first tiles so the tile waits below count only tile loads after them
   u32x4 qf[KS];
   {
     const uint16_t* qp = (const uint16_t*)a.q_abs + ((size_t)b * a.H + (hvalid ? hq : 0)) * RW + 8 * g;
@@ -178,21 +314,21 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
       qf[ks] = hvalid ? v : u32x4{0, 0, 0, 0};
     }
   }
-
-  f32x16 acc[FB];
+  // prologue: tiles 0, 1, 2 in flight
 #pragma unroll
-  for (int fb = 0; fb < FB; ++fb) acc[fb] = f32x16{};
-  float m_ref = -INFINITY, lsum = 0.f;
+  for (int st = 0; st < 3; ++st) {
+    if (st < ntiles) {
+      int nv;
+      const char* tp = tile_ptr(st, nv);
+      issue_tile<NW>(tp, nv, lds_tiles + st * TILE_BYTES, w, lane, lane_off);
+    }
+  }
 
-  // per-lane LDS byte offsets of the operand reads (the rest is an immediate)
-  int sbase[4];  // score A operand: row = lane % 32, chunk 2 ks + g
+  ReadOffsets ro;
   {
     const int sw = swz(hl);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sbase[q] = 128 * hl + 16 * ((2 * q + g) ^ sw);
-  }
-  int tbase[2][2];  // transpose reads: [fb parity][upper 8 rows]
-  {
+    for (int q = 0; q < 4; ++q) ro.s[q] = 128 * hl + 16 * ((2 * q + g) ^ sw);
     const int grp = lane >> 4, jl = lane & 15;
     const int trow = 4 * g + (jl >> 2);
     const int tchunk = 2 * (grp & 1) + ((jl >> 1) & 1);
@@ -200,93 +336,51 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
     for (int par = 0; par < 2; ++par)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        tbase[par][hf] = 128 * trow + 16 * ((4 * par + tchunk) ^ swz(trow + 8 * hf)) + 8 * (jl & 1);
+        ro.t[par][hf] = 128 * trow + 16 * ((4 * par + tchunk) ^ swz(trow + 8 * hf)) + 8 * (jl & 1);
   }
   const float sl2 = a.scale_log2;
+  constexpr int LPW = LOADS_PER_TILE / NW;  // loads per wave per tile
 
-  // One tile step: `cur` holds tile it, `nxt2` receives tile it + 2.
-  auto step = [&](int it, char* cur, char* nxt2) {
-    // this wave's loads of tile `it` are done once at most the next tile's remain
-    if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS_PER_TILE / NW));
+  f32x16 acc[FB];
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb) acc[fb] = f32x16{};
+  float lsum = 0.f;
+  bool overflow = false;
+
+  // tile 0: scores, reference maximum, numerators
+  if (ntiles >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW));
+  else if (ntiles == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  f32x16 sacc;
+  u32x4 pb[2];
+  tile_mfma<false>(sacc, tiles, qf, acc, tiles, pb, ro);
+  const float m_ref = tile_max(sacc, t0, t1, g) * sl2;  // fixed for the whole item
+  tile_softmax(sacc, t0, t1, g, sl2, m_ref, pb, lsum);
+
+  // step it: scores of tile it+1 interleaved with the latent update of tile it
+  for (int it = 0; it + 1 < ntiles; ++it) {
+    // this wave's loads of tile it+1 are done once only tile it+2's remain
+    if (it + 2 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    // plain barrier: every wave has waited for its own loads of tile `it`, and
-    // every wave is done reading the stage that the next loads overwrite
+    // every wave has its share of tile it+1 in LDS and is done with tile it-1
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (it + 2 < ntiles) {
+    if (it + 3 < ntiles) {
       int nv;
-      const char* tp = tile_ptr(it + 2, nv);
-      issue_tile<NW>(tp, nv, nxt2, w, lane, lane_off0, lane_off1);
+      const char* tp = tile_ptr(it + 3, nv);
+      issue_tile<NW>(tp, nv, lds_tiles + ((it + 3) & 3) * TILE_BYTES, w, lane, lane_off);
     }
-    const char* tl = cur;
-    const int tok0 = t0 + it * TT;
-
-    // ---- scores: S^T[t][h], A = K rows (token = lane%32), B = q~
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 kf = *(const u32x4*)(tl + sbase[ks & 3] + 4096 * (ks >> 2));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), sacc, 0, 0, 0);
-    }
-
-    // ---- online softmax for head hl (this lane and lane^32 share it)
-    float s[16];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int t = 8 * (j >> 2) + 4 * g + (j & 3);
-      const float v = sacc[j] * sl2;
-      s[j] = (tok0 + t < t1) ? v : -INFINITY;
-      mt = fmaxf(mt, s[j]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool need = mt > m_ref + kLazy;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = need ? mt : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-#pragma unroll
-      for (int fb = 0; fb < FB; ++fb) acc[fb] *= alpha;
-      lsum *= alpha;
-      m_ref = m_new;
-    }
-    u32x4 pb[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      uint32_t wds[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(s[8 * kk + e] - m_ref);
-        const float p1 = __builtin_amdgcn_exp2f(s[8 * kk + e + 1] - m_ref);
-        const uint16_t b0 = f32_to_bf16(p0), b1 = f32_to_bf16(p1);
-        lsum += bf16_to_f32(b0) + bf16_to_f32(b1);
-        wds[e >> 1] = (uint32_t)b0 | ((uint32_t)b1 << 16);
-      }
-      pb[kk] = u32x4{wds[0], wds[1], wds[2], wds[3]};
-    }
-
-    // ---- latent: O^T[f][h] += C^T[f][t] P^T[t][h]; A via LDS transpose reads
-    //      rows 16 kk + 4 g + j/4 (+8), chunk 4 fb + ..., see tbase
-#pragma unroll
-    for (int fb = 0; fb < FB; ++fb) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int imm = 4096 * (fb >> 1) + 128 * 16 * kk;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(tl + tbase[fb & 1][0] + imm));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(tl + tbase[fb & 1][1] + imm + 128 * 8));
-        const s16x8 av = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                          as_bf16x8(pb[kk]), acc[fb], 0, 0, 0);
-      }
-    }
-    };
-
-  for (int it = 0; it < ntiles; it += 3) {
-    step(it, tile0, tile2);
-    if (it + 1 < ntiles) step(it + 1, tile1, tile0);
-    if (it + 2 < ntiles) step(it + 2, tile2, tile1);
+    const char* cur = tiles + (it & 3) * TILE_BYTES;
+    const char* nxt = tiles + ((it + 1) & 3) * TILE_BYTES;
+    tile_mfma<true>(sacc, nxt, qf, acc, cur, pb, ro);
+    const int tok1 = t0 + (it + 1) * TT;
+    overflow |= tile_max(sacc, tok1, t1, g) * sl2 > m_ref + kHeadroom;
+    tile_softmax(sacc, tok1, t1, g, sl2, m_ref, pb, lsum);
   }
+  // latent update of the last tile (its scores were taken in the last step)
+  latent_only(acc, tiles + ((ntiles - 1) & 3) * TILE_BYTES, pb, ro);
 
   lsum += __shfl_xor(lsum, 32);
   if (hvalid) {
@@ -298,10 +392,64 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
         *(f32x4*)(pa + 32 * fb + 8 * q4) =
             f32x4{acc[fb][4 * q4], acc[fb][4 * q4 + 1], acc[fb][4 * q4 + 2], acc[fb][4 * q4 + 3]};
     if (g == 0) {
-      a.part_ml[((size_t)item * a.H + hq) * 2 + 0] = m_ref;
+      // +inf marks a partial the combine pass must recompute
+      a.part_ml[((size_t)item * a.H + hq) * 2 + 0] = overflow ? INFINITY : m_ref;
       a.part_ml[((size_t)item * a.H + hq) * 2 + 1] = lsum;
     }
   }
+}
+
+// --------------------------------------------------------------------------
+// Exact two-pass partial (m, l, acc) of one (item, head) in fp32, used only for
+// partials the split pass flagged.  scratch: >= 576 + 256 floats of LDS.
+__device__ __noinline__ void recompute_partial(const DecodeArgs& a, int item, int b, int h, int t0, int t1,
+                                               float* scratch, int* red) {
+  float* q = scratch;          // 576
+  float* p = scratch + RW;     // 256
+  const int tid = threadIdx.x;
+  const uint16_t* pool = (const uint16_t*)a.pool;
+  const int32_t* bt = a.block_table + (size_t)b * a.max_pages_per_seq;
+  const uint16_t* qa = (const uint16_t*)a.q_abs + ((size_t)b * a.H + h) * RW;
+  __syncthreads();
+  for (int f = tid; f < RW; f += blockDim.x) q[f] = bf16_to_f32(qa[f]);
+  __syncthreads();
+  auto score = [&](int t) {
+    const uint16_t* row = pool + ((size_t)bt[t / a.P] * a.P + t % a.P) * RW;
+    float d = 0.f;
+    for (int f = 0; f < RW; ++f) d += q[f] * bf16_to_f32(row[f]);
+    return d * a.scale_log2;
+  };
+  float m = -INFINITY;
+  for (int t = t0 + tid; t < t1; t += blockDim.x) m = fmaxf(m, score(t));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) red[tid >> 6] = __float_as_int(m);
+  __syncthreads();
+  m = -INFINITY;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, __int_as_float(red[w]));
+  float acc0 = 0.f, acc1 = 0.f, l = 0.f;
+  for (int tb = t0; tb < t1; tb += blockDim.x) {
+    __syncthreads();
+    const int t = tb + tid;
+    p[tid] = (t < t1) ? exp2f(score(t) - m) : 0.f;
+    __syncthreads();
+    const int nt = min((int)blockDim.x, t1 - tb);
+    for (int k = 0; k < nt; ++k) {
+      const int tt = tb + k;
+      const uint16_t* row = pool + ((size_t)bt[tt / a.P] * a.P + tt % a.P) * RW;
+      const float pk = p[k];
+      l += pk;  // every thread keeps the full sum
+      acc0 += pk * bf16_to_f32(row[tid]);
+      acc1 += pk * bf16_to_f32(row[tid + 256]);
+    }
+  }
+  float* pa = a.part_acc + ((size_t)item * a.H + h) * DC;
+  pa[tid] = acc0;
+  pa[tid + 256] = acc1;
+  if (tid == 0) {
+    a.part_ml[((size_t)item * a.H + h) * 2 + 0] = m;
+    a.part_ml[((size_t)item * a.H + h) * 2 + 1] = l;
+  }
+  __syncthreads();
 }
 
 // --------------------------------------------------------------------------
@@ -316,9 +464,22 @@ __global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
   __shared__ float s_m[CB], s_invl[CB];
 
   const int cap = a.len_cap;
-  make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk, a.ovh_tokens, s_len, s_items, red);
+  const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
+                                           a.ovh_tokens, s_len, s_items, red);
   const int h = blockIdx.x, b0 = blockIdx.y * CB;
   const int tid = threadIdx.x;
+
+  // rare path: partials flagged by the split pass are recomputed here, exactly
+  for (int bl = 0; bl < CB && b0 + bl < a.batch; ++bl) {
+    const int b = b0 + bl;
+    for (int i = s_items[b]; i < s_items[b + 1]; ++i) {
+      if (a.part_ml[((size_t)i * a.H + h) * 2] != INFINITY) continue;  // same value in every thread
+      const int t0 = (i - s_items[b]) * plan.chunk;
+      const int t1 = min(s_len[b], t0 + plan.chunk);
+      recompute_partial(a, i, b, h, t0, t1, (float*)lat_hi, red);
+    }
+  }
+  __syncthreads();
 
   // per-sequence merge statistics (fixed item order)
   if (tid < CB) {

@@ -252,3 +252,25 @@ def test_decode_ragged_paged_full_size():
     lens = inp["seq_lens"]
     seqs = [int(np.argmax(lens)), int(np.argmin(lens))] + [int(x) for x in np.random.default_rng(1).choice(128, 2)]
     _check(cfg, inp, st, seqs, heads=[0, 1, 31, 32, 63, 64, 65, 95, 96, 100, 126, 127])
+
+
+@pytest.mark.parametrize("flags", [0, mla.FLAG_GENERIC], ids=["mfma", "generic"])
+def test_decode_score_spike_far_above_first_tile(flags):
+    """One row of sequence 1 aligned with head 0's absorbed query and scaled so
+    its score exceeds the rest of its work item by ~500 (natural log units):
+    the MFMA split pass must hand this (item, head) to the exact recompute
+    path; the output is then W_UV,0 c_spike for head 0."""
+    need_gpu()
+    _case(f"score spike flags={flags}")
+    cfg = I.scaled(I.RAGGED, hidden=512, batch=3, seq_len=2100, min_seq_len=1)
+    inp = I.make(cfg, 21, lengths=[700, 2100, 64])
+    q = O.from_storage(inp["q"], "bf16")
+    qa = O.absorb_query(q, O.from_storage(inp["w_uk"], "bf16"), inp["q_positions"], cfg.qk_nope, cfg.rope_base)
+    spike = np.where(qa[1, 0] >= 0, 40.0, -40.0).astype(np.float32)
+    t_spike = 1000  # inside a work item, past its first tile
+    P = cfg.page_size
+    rows = inp["rows"].copy()
+    rows[inp["block_table"][1, t_spike // P], t_spike % P] = I.f32_to_bf16_bits(spike)
+    inp["rows"] = rows
+    st = _run_step(cfg, inp, flags)
+    _check(cfg, inp, st, [0, 1, 2])
