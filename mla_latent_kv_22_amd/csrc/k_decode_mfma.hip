@@ -72,9 +72,6 @@ __device__ __forceinline__ void score_next(f32x16& acc, const u32x4& a, const u3
 __device__ __forceinline__ void score_drain(f32x16& acc) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc));
 }
-__device__ __forceinline__ void latent_mfma(f32x16& acc, const u32x4& a, const u32x4& b) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
-}
 
 // Direct-to-LDS loads of one tile.  Wave w of NW issues loads i = w, w+NW, ...
 // of the 36; load i fills LDS bytes [1024 i, +1024) = column group i / 4,
@@ -137,79 +134,23 @@ __device__ __forceinline__ void issue_tile(const char* __restrict__ tile_base, i
   }
 }
 
-// Per-lane LDS byte offsets of the operand reads, relative to a stage base.
+// Per-lane LDS byte offsets of the operand reads, relative to a buffer base.
 struct ReadOffsets {
   int s[4];     // score A operand (row = lane % 32, chunk 2 ks + g): + 4096 (ks / 4)
   int t[2][2];  // transpose reads [fb parity][upper 8 rows]: + 4096 (fb / 2) + 2048 kk
+  int p[2];     // P^T fragment of head lane % 32, [kk]: + 2048 hb
 };
 
-// Scores of one tile: S^T[t][h] = sum_f row_t[f] q~_h[f], chained MFMAs with
-// K fragments read 3 ahead; optionally interleaved one-for-one with the 32
-// latent MFMAs O^T += C^T P^T of the previous tile (transpose reads 2 ahead).
-template <bool WITH_LATENT>
-__device__ __forceinline__ void tile_mfma(f32x16& sacc, const char* ts, const u32x4* qf, f32x16* acc,
-                                          const char* tp, const u32x4* pb, const ReadOffsets& o) {
-  constexpr int PF = 3, PF2 = 2, NPC = 2 * FB;
-  u32x4 kf[PF];
-#pragma unroll
-  for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x4*)(ts + o.s[ks & 3] + 4096 * (ks >> 2));
-  auto tr_a = [&](int idx) {
-    const int kk = idx / FB, fb = idx % FB;
-    const int imm = 4096 * (fb >> 1) + 2048 * kk;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][0] + imm));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][1] + imm + 1024));
-    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-    return u32x4{l2[0], l2[1], h2[0], h2[1]};
-  };
-  u32x4 av[PF2];
-  if constexpr (WITH_LATENT) {
-#pragma unroll
-    for (int i = 0; i < PF2; ++i) av[i] = tr_a(i);
-  }
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const u32x4 cur = kf[ks % PF];
-    if (ks + PF < KS) kf[ks % PF] = *(const u32x4*)(ts + o.s[(ks + PF) & 3] + 4096 * ((ks + PF) >> 2));
-    if (ks == 0) score_first(sacc, cur, qf[ks]);
-    else score_next(sacc, cur, qf[ks]);
-    if constexpr (WITH_LATENT) {
-      if (ks < NPC) {
-        const u32x4 ca = av[ks % PF2];
-        if (ks + PF2 < NPC) av[ks % PF2] = tr_a(ks + PF2);
-        latent_mfma(acc[ks % FB], ca, pb[ks / FB]);
-      }
-    }
-  }
-  score_drain(sacc);
-}
-
-// The 32 latent MFMAs of the last tile (no next tile to score).
-__device__ __forceinline__ void latent_only(f32x16* acc, const char* tp, const u32x4* pb, const ReadOffsets& o) {
-  constexpr int PF2 = 2, NPC = 2 * FB;
-  auto tr_a = [&](int idx) {
-    const int kk = idx / FB, fb = idx % FB;
-    const int imm = 4096 * (fb >> 1) + 2048 * kk;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][0] + imm));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][1] + imm + 1024));
-    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-    return u32x4{l2[0], l2[1], h2[0], h2[1]};
-  };
-  u32x4 av[PF2];
-#pragma unroll
-  for (int i = 0; i < PF2; ++i) av[i] = tr_a(i);
-#pragma unroll
-  for (int i = 0; i < NPC; ++i) {
-    const u32x4 ca = av[i % PF2];
-    if (i + PF2 < NPC) av[i % PF2] = tr_a(i + PF2);
-    latent_mfma(acc[i % FB], ca, pb[i / FB]);
-  }
-}
+// P^T in LDS, bf16: head h owns 64 bytes = [kk][half g][8 tokens]; the 16-byte
+// slot 2 kk + g is XOR-swizzled by (h >> 1) & 3 (conflict-free 16-byte reads
+// and writes of 8 consecutive heads).
+__device__ __forceinline__ int p_off(int h, int kk, int g) { return 64 * h + 16 * ((2 * kk + g) ^ ((h >> 1) & 3)); }
 
 // Softmax numerators of one tile for head lane % 32: p = 2^(s sl2 - m_ref)
-// rounded to bf16 (the P operand of the latent MFMA), their sum in lsum.
+// rounded to bf16, written to the P^T buffer; their sum goes to lsum.
 // Tokens at or past t1 (only in a ragged last tile) get p = 0.
 __device__ __forceinline__ void tile_softmax(const f32x16& sacc, int tok0, int t1, int g, float sl2, float m_ref,
-                                             u32x4* pb, float& lsum) {
+                                             char* pbuf, int head_off, float& lsum, const ReadOffsets& o) {
   const bool full = tok0 + TT <= t1;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
@@ -228,7 +169,7 @@ __device__ __forceinline__ void tile_softmax(const f32x16& sacc, int tok0, int t
       lsum += __uint_as_float(pk << 16) + __uint_as_float(pk & 0xffff0000u);
       wds[e >> 1] = pk;
     }
-    pb[kk] = u32x4{wds[0], wds[1], wds[2], wds[3]};
+    *(u32x4*)(pbuf + head_off + o.p[kk]) = u32x4{wds[0], wds[1], wds[2], wds[3]};
   }
 }
 
@@ -248,20 +189,90 @@ __device__ __forceinline__ float tile_max(const f32x16& sacc, int tok0, int t1, 
   return fmaxf(mt, __shfl_xor(mt, 32));
 }
 
-// Four stage buffers of one tile each.  The planner's two per-sequence arrays
-// live in stage 3 until the first load into it (every read of them happens
-// before the barrier that precedes that load).
+// Work split inside one work-group of NW waves: for the scores, wave w owns
+// heads [32 w, 32 w + 32) (HB = NW head blocks in all); for the latent update
+// it owns the FBW = 16 / NW feature blocks [FBW w, FBW w + FBW) of every head,
+// so each C^T fragment read from LDS serves HB MFMAs and each wave reads only
+// its share of the tile through the transpose path.
+template <int NW>
+struct Split {
+  static constexpr int HB = NW;
+  static constexpr int FBW = FB / NW;
+  static constexpr int NPC = 2 * FBW * HB;  // latent MFMAs per tile (32)
+};
+
+// Latent update of one tile, op i = (kk, fbl, hb) in that order: A = C^T
+// fragment of feature block FBW w + fbl (two transpose reads, one group
+// ahead), B = P^T fragment of head block hb (16-byte reads, reloaded as soon
+// as its last use for kk = 0 has issued).  With SCORES, the 36 chained score
+// MFMAs of the next tile are interleaved one for one.
+template <int NW, bool SCORES>
+__device__ __forceinline__ void tile_step(f32x16& sacc, const char* ts, const u32x4* qf, f32x16* acc, const char* tp,
+                                          const char* pbuf, int w, const ReadOffsets& o) {
+  using S = Split<NW>;
+  constexpr int PF = 3;
+  u32x4 kf[PF];
+  if constexpr (SCORES) {
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x4*)(ts + o.s[ks & 3] + 4096 * (ks >> 2));
+  }
+  auto tr_a = [&](int kk, int fbl) {
+    const int fb = S::FBW * w + fbl;
+    const int imm = 4096 * (fb >> 1) + 2048 * kk;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][0] + imm));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][1] + imm + 1024));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
+  auto p_frag = [&](int kk, int hb) { return *(const u32x4*)(pbuf + 2048 * hb + o.p[kk]); };
+  u32x4 af[2], pf[S::HB];
+  af[0] = tr_a(0, 0);
+#pragma unroll
+  for (int hb = 0; hb < S::HB; ++hb) pf[hb] = p_frag(0, hb);
+  constexpr int NOPS = SCORES ? KS : S::NPC;
+#pragma unroll
+  for (int op = 0; op < NOPS; ++op) {
+    if constexpr (SCORES) {
+      const u32x4 cur = kf[op % PF];
+      if (op + PF < KS) kf[op % PF] = *(const u32x4*)(ts + o.s[(op + PF) & 3] + 4096 * ((op + PF) >> 2));
+      if (op == 0) score_first(sacc, cur, qf[op]);
+      else score_next(sacc, cur, qf[op]);
+    }
+    if (op < S::NPC) {
+      const int kk = op / (S::FBW * S::HB), fbl = (op / S::HB) % S::FBW, hb = op % S::HB;
+      const int grp = op / S::HB;  // (kk, fbl) group index 0 .. 2 FBW - 1
+      if (hb == 0 && grp + 1 < 2 * S::FBW) af[(grp + 1) & 1] = tr_a((grp + 1) / S::FBW, (grp + 1) % S::FBW);
+      const u32x4 bv = pf[hb];
+      if (kk == 0 && fbl == S::FBW - 1) pf[hb] = p_frag(1, hb);  // last kk = 0 use of this slot
+      acc[fbl * S::HB + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[grp & 1]), as_bf16x8(bv),
+                                                                      acc[fbl * S::HB + hb], 0, 0, 0);
+    }
+  }
+  if constexpr (SCORES) score_drain(sacc);
+}
+
+// LDS map (160 KiB, the whole LDS of a CU):
+//   [0, 147456)        four tile stages of 36864 bytes
+//   [147456, 163840)   two P^T buffers of NW * 2048 bytes (8192 for NW = 4)
+// The planner's per-sequence arrays and its reduction scratch live in stage 3
+// until the first load into it (every read of them happens before the
+// barrier that precedes that load).
 constexpr int NSTAGE = 4;
-constexpr int PLAN_INTS = 2 * (kMaxDecodeBatch + 1);
+constexpr int PBUF_BYTES = 4 * 2048;
+constexpr int LDS_BYTES = NSTAGE * TILE_BYTES + 2 * PBUF_BYTES;
+constexpr int PLAN_INTS = 2 * (kMaxDecodeBatch + 1) + 16;
 static_assert(PLAN_INTS * 4 <= TILE_BYTES, "planner arrays must fit in one stage");
+static_assert(LDS_BYTES <= 163840, "LDS budget");
 
 template <int NW>
 __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char tiles[NSTAGE * TILE_BYTES];
-  __shared__ int red[16];
-  __shared__ int s_pages[kMaxItemPages];
+  using S = Split<NW>;
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  char* tiles = smem;
+  char* pbufs = smem + NSTAGE * TILE_BYTES;
   int* s_len = (int*)(tiles + 3 * TILE_BYTES);
   int* s_items = s_len + (kMaxDecodeBatch + 1);
+  int* red = s_items + (kMaxDecodeBatch + 1);
 
   const int cap = a.len_cap;
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
@@ -273,7 +284,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
   if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
 
   // wave-uniform values read from LDS are moved to scalar registers so that
-  // page lookups and tile addresses stay scalar
+  // page lookups (scalar loads) and tile addresses stay scalar
   const int b = __builtin_amdgcn_readfirstlane(item_seq(s_items, a.batch, item));
   const int chunk = __builtin_amdgcn_readfirstlane(plan.chunk);
   const int t0 = (item - __builtin_amdgcn_readfirstlane(s_items[b])) * chunk;
@@ -284,18 +295,12 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
   const bool hvalid = hq < a.H;
   const int P = a.P;
   const char* __restrict__ pool = (const char*)a.pool;
+  const int32_t* __restrict__ btb = a.block_table + (size_t)b * a.max_pages_per_seq;
   const int ntiles = (t1 - t0 + TT - 1) / TT;
-  {
-    const int32_t* __restrict__ bt = a.block_table + (size_t)b * a.max_pages_per_seq;
-    const int p0 = t0 / P, np = (t1 - 1) / P - p0 + 1;
-    for (int i = threadIdx.x; i < np; i += blockDim.x) s_pages[i] = bt[p0 + i];
-  }
-  __syncthreads();  // pages staged; planner arrays no longer read
-  const int page0 = t0 / P;
   auto tile_ptr = [&](int tile, int& nvalid) {
     const int tok0 = t0 + tile * TT;
     nvalid = min(TT, t1 - tok0);
-    const int page = __builtin_amdgcn_readfirstlane(s_pages[tok0 / P - page0]);
+    const int page = btb[tok0 / P];
     return pool + ((size_t)page * P + (tok0 % P)) * (RW * 2);
   };
   const uint32_t lds_tiles = lds_addr_of(tiles);
@@ -314,6 +319,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
       qf[ks] = hvalid ? v : u32x4{0, 0, 0, 0};
     }
   }
+  __syncthreads();  // planner arrays in stage 3 are no longer read
   // prologue: tiles 0, 1, 2 in flight
 #pragma unroll
   for (int st = 0; st < 3; ++st) {
@@ -337,65 +343,87 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
         ro.t[par][hf] = 128 * trow + 16 * ((4 * par + tchunk) ^ swz(trow + 8 * hf)) + 8 * (jl & 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) ro.p[kk] = p_off(hl, kk, g);  // + 2048 hb (hb keeps (h >> 1) & 3)
   }
+  const int head_off = 2048 * w;  // this wave's heads in the P^T buffer
   const float sl2 = a.scale_log2;
   constexpr int LPW = LOADS_PER_TILE / NW;  // loads per wave per tile
 
   f32x16 acc[FB];
 #pragma unroll
-  for (int fb = 0; fb < FB; ++fb) acc[fb] = f32x16{};
+  for (int i = 0; i < FB; ++i) acc[i] = f32x16{};
   float lsum = 0.f;
   bool overflow = false;
 
-  // tile 0: scores, reference maximum, numerators
+  // tile 0: scores, reference maximum, numerators into P^T buffer 0
   if (ntiles >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW));
   else if (ntiles == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   f32x16 sacc;
-  u32x4 pb[2];
-  tile_mfma<false>(sacc, tiles, qf, acc, tiles, pb, ro);
+  {
+    constexpr int PF = 3;
+    u32x4 kf[PF];
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x4*)(tiles + ro.s[ks & 3] + 4096 * (ks >> 2));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 cur = kf[ks % PF];
+      if (ks + PF < KS) kf[ks % PF] = *(const u32x4*)(tiles + ro.s[(ks + PF) & 3] + 4096 * ((ks + PF) >> 2));
+      if (ks == 0) score_first(sacc, cur, qf[ks]);
+      else score_next(sacc, cur, qf[ks]);
+    }
+    score_drain(sacc);
+  }
   const float m_ref = tile_max(sacc, t0, t1, g) * sl2;  // fixed for the whole item
-  tile_softmax(sacc, t0, t1, g, sl2, m_ref, pb, lsum);
+  tile_softmax(sacc, t0, t1, g, sl2, m_ref, pbufs, head_off, lsum, ro);
 
-  // step it: scores of tile it+1 interleaved with the latent update of tile it
+  // step it: latent update of tile it (P^T buffer it % 2) interleaved with the
+  // scores of tile it+1, whose numerators go to P^T buffer (it+1) % 2
   for (int it = 0; it + 1 < ntiles; ++it) {
+    int nv3 = 0;
+    const char* tp3 = (it + 3 < ntiles) ? tile_ptr(it + 3, nv3) : nullptr;  // scalar page load, early
     // this wave's loads of tile it+1 are done once only tile it+2's remain
     if (it + 2 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    // every wave has its share of tile it+1 in LDS and is done with tile it-1
+    // all waves: tile it+1 in LDS, P^T of tile it written, tile it-1 and
+    // P^T buffer (it+1) % 2 no longer read
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (it + 3 < ntiles) {
-      int nv;
-      const char* tp = tile_ptr(it + 3, nv);
-      issue_tile<NW>(tp, nv, lds_tiles + ((it + 3) & 3) * TILE_BYTES, w, lane, lane_off);
-    }
+    if (it + 3 < ntiles) issue_tile<NW>(tp3, nv3, lds_tiles + ((it + 3) & 3) * TILE_BYTES, w, lane, lane_off);
     const char* cur = tiles + (it & 3) * TILE_BYTES;
     const char* nxt = tiles + ((it + 1) & 3) * TILE_BYTES;
-    tile_mfma<true>(sacc, nxt, qf, acc, cur, pb, ro);
+    tile_step<NW, true>(sacc, nxt, qf, acc, cur, pbufs + (it & 1) * PBUF_BYTES, w, ro);
     const int tok1 = t0 + (it + 1) * TT;
     overflow |= tile_max(sacc, tok1, t1, g) * sl2 > m_ref + kHeadroom;
-    tile_softmax(sacc, tok1, t1, g, sl2, m_ref, pb, lsum);
+    tile_softmax(sacc, tok1, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum, ro);
   }
   // latent update of the last tile (its scores were taken in the last step)
-  latent_only(acc, tiles + ((ntiles - 1) & 3) * TILE_BYTES, pb, ro);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  tile_step<NW, false>(sacc, tiles, qf, acc, tiles + ((ntiles - 1) & 3) * TILE_BYTES,
+                       pbufs + ((ntiles - 1) & 1) * PBUF_BYTES, w, ro);
 
   lsum += __shfl_xor(lsum, 32);
-  if (hvalid) {
-    float* pa = a.part_acc + ((size_t)item * a.H + hq) * DC + 4 * g;
+  // acc[fbl * HB + hb] holds O^T rows f = 32 (FBW w + fbl) + 8 (j/4) + 4 g + j % 4
+  // of head 32 hb + lane % 32
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
+  for (int fbl = 0; fbl < S::FBW; ++fbl)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *(f32x4*)(pa + 32 * fb + 8 * q4) =
-            f32x4{acc[fb][4 * q4], acc[fb][4 * q4 + 1], acc[fb][4 * q4 + 2], acc[fb][4 * q4 + 3]};
-    if (g == 0) {
-      // +inf marks a partial the combine pass must recompute
-      a.part_ml[((size_t)item * a.H + hq) * 2 + 0] = overflow ? INFINITY : m_ref;
-      a.part_ml[((size_t)item * a.H + hq) * 2 + 1] = lsum;
+    for (int hb = 0; hb < S::HB; ++hb) {
+      const int h = 32 * hb + hl;
+      if (h >= a.H) continue;
+      float* pa = a.part_acc + ((size_t)item * a.H + h) * DC + 32 * (S::FBW * w + fbl) + 4 * g;
+      const f32x16& v = acc[fbl * S::HB + hb];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) *(f32x4*)(pa + 8 * q4) = f32x4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
     }
+  if (hvalid && g == 0) {
+    // +inf marks a partial the combine pass must recompute
+    a.part_ml[((size_t)item * a.H + hq) * 2 + 0] = overflow ? INFINITY : m_ref;
+    a.part_ml[((size_t)item * a.H + hq) * 2 + 1] = lsum;
   }
 }
 
@@ -461,76 +489,129 @@ __global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
   __shared__ int s_len[kMaxDecodeBatch + 1];
   __shared__ int s_items[kMaxDecodeBatch + 1];
   __shared__ int red[16];
-  __shared__ float s_m[CB], s_invl[CB];
+  __shared__ float s_ms[CB], s_il[CB];  // per-sequence reference max m* and 1 / L
+  __shared__ int s_maxn;
 
   const int cap = a.len_cap;
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
                                            a.ovh_tokens, s_len, s_items, red);
   const int h = blockIdx.x, b0 = blockIdx.y * CB;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, r = lane & 31;
+  const int bend = min(a.batch, b0 + CB);
+  const int i_lo = s_items[b0], i_hi = s_items[bend];
 
-  // rare path: partials flagged by the split pass are recomputed here, exactly
-  for (int bl = 0; bl < CB && b0 + bl < a.batch; ++bl) {
-    const int b = b0 + bl;
-    for (int i = s_items[b]; i < s_items[b + 1]; ++i) {
-      if (a.part_ml[((size_t)i * a.H + h) * 2] != INFINITY) continue;  // same value in every thread
-      const int t0 = (i - s_items[b]) * plan.chunk;
-      const int t1 = min(s_len[b], t0 + plan.chunk);
-      recompute_partial(a, i, b, h, t0, t1, (float*)lat_hi, red);
+  // W_UV fragments of this wave's first 32 output columns, fetched up front so
+  // their latency hides behind the merge (B operand: v = lane % 32, 8 latent
+  // values from 16 ks + 8 g)
+  const uint16_t* wuv = (const uint16_t*)a.w_uv + (size_t)h * a.d_v * DC;
+  u32x4 wf[DC / 16];
+  const bool wpre = w * 32 < a.d_v;
+  if (wpre) {
+    const uint16_t* wrow = wuv + (size_t)(w * 32 + r) * DC + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < DC / 16; ++ks) wf[ks] = *(const u32x4*)(wrow + 16 * ks);
+  }
+
+  // rare path: partials flagged by the split pass are recomputed here, exactly.
+  // The flags of this block's items are checked in parallel first.
+  {
+    int any = 0;
+    for (int i = i_lo + tid; i < i_hi; i += 256) any |= a.part_ml[((size_t)i * a.H + h) * 2] == INFINITY;
+    any = __syncthreads_or(any);
+    if (any) {
+      for (int bl = 0; bl < CB && b0 + bl < a.batch; ++bl) {
+        const int b = b0 + bl;
+        for (int i = s_items[b]; i < s_items[b + 1]; ++i) {
+          if (a.part_ml[((size_t)i * a.H + h) * 2] != INFINITY) continue;  // same value in every thread
+          const int t0 = (i - s_items[b]) * plan.chunk;
+          const int t1 = min(s_len[b], t0 + plan.chunk);
+          recompute_partial(a, i, b, h, t0, t1, (float*)lat_hi, red);
+        }
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
 
-  // per-sequence merge statistics (fixed item order)
+  // per-sequence merge statistics in a fixed item order: m* = max m_i,
+  // L = sum 2^(m_i - m*) l_i; item i then weighs 2^(m_i - m*) / L
+  if (tid == 0) s_maxn = 0;
+  __syncthreads();
   if (tid < CB) {
     const int b = b0 + tid;
-    float ms = -INFINITY, L = 0.f;
+    float ms = 0.f, il = 0.f;
     if (b < a.batch) {
       const int i0 = s_items[b], i1 = s_items[b + 1];
+      ms = -INFINITY;
+      float L = 0.f;
       for (int i = i0; i < i1; ++i) ms = fmaxf(ms, a.part_ml[((size_t)i * a.H + h) * 2]);
       for (int i = i0; i < i1; ++i)
         L += exp2f(a.part_ml[((size_t)i * a.H + h) * 2] - ms) * a.part_ml[((size_t)i * a.H + h) * 2 + 1];
       if (a.lse) a.lse[(size_t)b * a.H + h] = (i1 > i0) ? (ms + log2f(L)) * kLn2 : -INFINITY;
+      il = (L > 0.f) ? 1.f / L : 0.f;
+      atomicMax(&s_maxn, i1 - i0);
     }
-    s_m[tid] = ms;
-    s_invl[tid] = (L > 0.f) ? 1.f / L : 0.f;
+    s_ms[tid] = ms;
+    s_il[tid] = il;
   }
   __syncthreads();
 
-  // merged latent, split into bf16 hi + lo, stored with a 16-byte-chunk swizzle
-  for (int u = tid; u < CB * (DC / 4); u += 256) {
-    const int bl = u / (DC / 4), c4 = (u % (DC / 4)) * 4;
-    const int b = b0 + bl;
-    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (b < a.batch) {
-      const int i0 = s_items[b], i1 = s_items[b + 1];
-      const float ms = s_m[bl], invl = s_invl[bl];
-      for (int i = i0; i < i1; ++i) {
-        const float wgt = exp2f(a.part_ml[((size_t)i * a.H + h) * 2] - ms) * invl;
-        v += wgt * *(const f32x4*)(a.part_acc + ((size_t)i * a.H + h) * DC + c4);
+  // merged latent of sequence b0 + bl at columns 4 cq .. 4 cq + 3: the thread
+  // takes cq = tid % 128 and the sequences bl = tid / 128 + 2 k; for each item
+  // index j the loads of all its sequences are issued before any is used
+  {
+    const int cq = tid & 127, blo = tid >> 7;
+    f32x4 v[CB / 2];
+#pragma unroll
+    for (int k = 0; k < CB / 2; ++k) v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int maxn = s_maxn;
+    for (int j = 0; j < maxn; ++j) {
+      float ml[CB / 2];
+      bool ok[CB / 2];
+      f32x4 pa[CB / 2];
+#pragma unroll
+      for (int k = 0; k < CB / 2; ++k) {
+        const int bl = blo + 2 * k, b = b0 + bl;
+        const int i = (b < a.batch) ? s_items[b] + j : 0;
+        ok[k] = b < a.batch && i < s_items[b + 1];
+        const size_t ih = (size_t)(ok[k] ? i : 0) * a.H + h;
+        ml[k] = ok[k] ? a.part_ml[ih * 2] : 0.f;
+        pa[k] = ok[k] ? *(const f32x4*)(a.part_acc + ih * DC + 4 * cq) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int k = 0; k < CB / 2; ++k) {
+        const int bl = blo + 2 * k;
+        const float wgt = ok[k] ? exp2f(ml[k] - s_ms[bl]) * s_il[bl] : 0.f;
+        v[k] += wgt * pa[k];
       }
     }
-    const int chunk = c4 >> 3, within = c4 & 7;
-    const int pos = bl * (DC / 8) + (chunk ^ (bl & 7));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint16_t hb = f32_to_bf16(v[e]);
-      const uint16_t lb = f32_to_bf16(v[e] - bf16_to_f32(hb));
-      lat_hi[pos * 8 + within + e] = hb;
-      lat_lo[pos * 8 + within + e] = lb;
+    for (int k = 0; k < CB / 2; ++k) {
+      const int bl = blo + 2 * k;
+      const int chunk = cq >> 1, within = (cq & 1) * 4;
+      const int pos = bl * (DC / 8) + (chunk ^ (bl & 7));
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const uint32_t hp = pack_bf16x2(v[k][e], v[k][e + 1]);
+        const float h0 = __uint_as_float(hp << 16), h1 = __uint_as_float(hp & 0xffff0000u);
+        hw[e >> 1] = hp;
+        lw[e >> 1] = pack_bf16x2(v[k][e] - h0, v[k][e + 1] - h1);
+      }
+      *(uint2*)(lat_hi + pos * 8 + within) = make_uint2(hw[0], hw[1]);
+      *(uint2*)(lat_lo + pos * 8 + within) = make_uint2(lw[0], lw[1]);
     }
   }
   __syncthreads();
 
-  // out[b][h][v] = sum_c lat[b][c] W_UV[h][v][c]: D[b][v], A = lat (b = lane%32), B = W_UV^T
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, r = lane & 31;
-  const uint16_t* wuv = (const uint16_t*)a.w_uv + (size_t)h * a.d_v * DC;
+  // out[b][h][v] = sum_c lat[b][c] W_UV[h][v][c]: D[b][v], A = lat (b = lane%32),
+  // B = W_UV^T; lat = hi + lo carries the fp32 merge to ~2^-17
   for (int vb = w; vb * 32 < a.d_v; vb += 4) {
     f32x16 acc = f32x16{};
     const uint16_t* wrow = wuv + (size_t)(vb * 32 + r) * DC + 8 * g;
-#pragma unroll 4
+#pragma unroll
     for (int ks = 0; ks < DC / 16; ++ks) {
-      const u32x4 bw = *(const u32x4*)(wrow + 16 * ks);
+      const u32x4 bw = (vb == w) ? wf[ks] : *(const u32x4*)(wrow + 16 * ks);
       const int pos = r * (DC / 8) + ((2 * ks + g) ^ (r & 7));
       const u32x4 ah = *(const u32x4*)(lat_hi + pos * 8);
       const u32x4 al = *(const u32x4*)(lat_lo + pos * 8);
@@ -554,20 +635,20 @@ bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch) {
          batch <= kMaxDecodeBatch;
 }
 
+// waves per split work-group: 32 heads each, and 16 / NW latent feature blocks
+static int split_waves(int H) { return H <= 32 ? 1 : (H <= 64 ? 2 : 4); }
+
 int decode_mfma_slots(int H, int cus) {
-  // one 4-wave work-group per CU (registers); narrower groups pack 4 waves per CU
-  const int nw = (H + 31) / 32;
-  return cus * (4 / nw);
+  // one work-group per CU at 4 waves (registers); narrower groups pack 4 waves per CU
+  return cus * (4 / split_waves(H));
 }
 
 hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  const int nw = (a.H + 31) / 32;
   const dim3 g1(a.max_items);
-  switch (nw) {
+  switch (split_waves(a.H)) {
     case 1: hipLaunchKernelGGL(k_split<1>, g1, dim3(64), 0, s, a); break;
     case 2: hipLaunchKernelGGL(k_split<2>, g1, dim3(128), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(k_split<3>, g1, dim3(192), 0, s, a); break;
     default: hipLaunchKernelGGL(k_split<4>, g1, dim3(256), 0, s, a); break;
   }
   hipError_t e = hipGetLastError();

@@ -1,8 +1,8 @@
 // MFMA kernels for the two projections around the cache (gfx950, bf16):
 //
 // cache write   rows^T[R x N] = W_DKR[R x D] . h^T[D x N]   (16x16x32 MFMA)
-//   One work-group per (16 cached features, 16 * TB4 tokens); its 4 waves
-//   split the hidden axis and meet in LDS.  In the accumulator each lane holds
+//   One work-group per (16 cached features, 16 * TB4 tokens); its waves split
+//   the hidden axis and meet in LDS.  In the accumulator each lane holds
 //   4 consecutive features of one token, so the rotary pairs (2i, 2i+1) of
 //   the k_R branch are rotated in registers before the bf16 store to the
 //   token's slot.
@@ -23,9 +23,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------- cache write
-template <int TB4>
-__global__ void __launch_bounds__(256) k_write_mfma(WriteCacheArgs a) {
-  __shared__ f32x4 part[4][TB4][64];
+template <int TB4, int NWV>
+__global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
+  __shared__ f32x4 part[NWV][TB4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int R = a.d_c + a.d_r;
   const int r0 = blockIdx.x * 16;
@@ -47,8 +47,8 @@ __global__ void __launch_bounds__(256) k_write_mfma(WriteCacheArgs a) {
     hv[t] = n < a.n_tokens;
     hp[t] = H + (size_t)(hv[t] ? n : 0) * D + kq;
   }
-#pragma unroll 4
-  for (int ks = w; ks < ksteps; ks += 4) {
+#pragma unroll 8
+  for (int ks = w; ks < ksteps; ks += NWV) {
     const u32x4 av = *(const u32x4*)(wp + 32 * ks);
 #pragma unroll
     for (int t = 0; t < TB4; ++t) {
@@ -61,8 +61,10 @@ __global__ void __launch_bounds__(256) k_write_mfma(WriteCacheArgs a) {
   for (int t = 0; t < TB4; ++t) part[w][t][lane] = acc[t];
   __syncthreads();
   // epilogue: waves take token sub-blocks; fixed summation order over waves
-  for (int t = w; t < TB4; t += 4) {
-    const f32x4 v = part[0][t][lane] + part[1][t][lane] + part[2][t][lane] + part[3][t][lane];
+  for (int t = w; t < TB4; t += NWV) {
+    f32x4 v = part[0][t][lane];
+#pragma unroll
+    for (int k = 1; k < NWV; ++k) v += part[k][t][lane];
     const int n = n0 + 16 * t + m;  // D: lane holds token n = lane % 16, features 4 (lane / 16) + j
     if (n >= a.n_tokens) continue;
     const long long slot = a.slots[n];
@@ -99,10 +101,19 @@ __global__ void __launch_bounds__(256) k_absorb_mfma(AbsorbArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int H = a.H, dn = a.d_n, dc = a.d_c, dq = a.d_n + a.d_r, R = a.d_c + a.d_r;
   const uint16_t* __restrict__ wuk = (const uint16_t*)a.w_uk + (size_t)h * dn * dc + cb * AB_C;
-  for (int u = tid; u < dn * (AB_C / 8); u += 256) {
-    const int j = u >> 4, ch = u & 15;
-    const u32x4 v = *(const u32x4*)(wuk + (size_t)j * dc + 8 * ch);
-    *(u32x4*)(wtile + j * 256 + 16 * (ch ^ (2 * (j & 3)))) = v;
+  // staged 8 chunks per thread at a time, all loads in flight before the stores
+  for (int u0 = 0; u0 < dn * (AB_C / 8); u0 += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int u = u0 + k * 256 + tid, j = u >> 4, ch = u & 15;
+      if (u < dn * (AB_C / 8)) v[k] = *(const u32x4*)(wuk + (size_t)j * dc + 8 * ch);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int u = u0 + k * 256 + tid, j = u >> 4, ch = u & 15;
+      if (u < dn * (AB_C / 8)) *(u32x4*)(wtile + j * 256 + 16 * (ch ^ (2 * (j & 3)))) = v[k];
+    }
   }
   __syncthreads();
 
@@ -117,6 +128,7 @@ __global__ void __launch_bounds__(256) k_absorb_mfma(AbsorbArgs a) {
     const bool nv = n < a.n_tokens;
     const uint16_t* qp = Q + ((size_t)(nv ? n : 0) * H + h) * dq + 8 * g;
     f32x16 acc = f32x16{};
+#pragma unroll 8
     for (int ks = 0; ks < dn / 16; ++ks) {
       u32x4 av = *(const u32x4*)(qp + 16 * ks);
       if (!nv) av = u32x4{0, 0, 0, 0};
@@ -160,10 +172,13 @@ bool write_mfma_supported(int D, int d_c, int d_r) { return D % 32 == 0 && d_c %
 hipError_t write_cache_mfma(const WriteCacheArgs& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
   const int R = a.d_c + a.d_r;
+  // few tokens (decode): W_DKR dominates the bytes, so 16 waves per work-group
+  // split the hidden axis and keep many loads in flight; many tokens: 4 token
+  // blocks per work-group reuse each W fragment 4 times
   if (a.n_tokens <= 1024) {
-    hipLaunchKernelGGL(k_write_mfma<1>, dim3(R / 16, (a.n_tokens + 15) / 16), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_write_mfma<1, 16>), dim3(R / 16, (a.n_tokens + 15) / 16), dim3(1024), 0, s, a);
   } else {
-    hipLaunchKernelGGL(k_write_mfma<4>, dim3(R / 16, (a.n_tokens + 63) / 64), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_write_mfma<4, 4>), dim3(R / 16, (a.n_tokens + 63) / 64), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
