@@ -264,6 +264,9 @@ constexpr int PLAN_INTS = 2 * (kMaxDecodeBatch + 1) + 16;
 static_assert(PLAN_INTS * 4 <= TILE_BYTES, "planner arrays must fit in one stage");
 static_assert(LDS_BYTES <= 163840, "LDS budget");
 
+// One work-group per CU, persistent over the work items: round r of work-group
+// x takes item index x + r * gridDim.x (the host keeps rounds <= 64), so no
+// work-group is launched without work.
 template <int NW>
 __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
   using S = Split<NW>;
@@ -278,58 +281,39 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
                                            a.ovh_tokens, s_len, s_items, red);
   const int n_items = plan.n_items;
-  if ((int)blockIdx.x >= n_items) return;
-  // consecutive items (same sequence) share an XCD: work-group i runs on XCD i % 8
-  int item = blockIdx.x;
-  if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
-
-  // wave-uniform values read from LDS are moved to scalar registers so that
-  // page lookups (scalar loads) and tile addresses stay scalar
-  const int b = __builtin_amdgcn_readfirstlane(item_seq(s_items, a.batch, item));
-  const int chunk = __builtin_amdgcn_readfirstlane(plan.chunk);
-  const int t0 = (item - __builtin_amdgcn_readfirstlane(s_items[b])) * chunk;
-  const int t1 = min(__builtin_amdgcn_readfirstlane(s_len[b]), t0 + chunk);
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // work-group 0 publishes the plan for the combine pass:
+  // [0, B] first item of each sequence, [B+1, 2B] clamped lengths, [2B+1] chunk
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i <= a.batch; i += blockDim.x) a.plan[i] = s_items[i];
+    for (int i = threadIdx.x; i < a.batch; i += blockDim.x) a.plan[a.batch + 1 + i] = s_len[i];
+    if (threadIdx.x == 0) a.plan[2 * a.batch + 1] = plan.chunk;
+  }
+  // lane r of every wave holds round r's item, sequence and token range.
+  // Consecutive items (same sequence) share an XCD: work-group x runs on XCD x % 8.
+  const int G = gridDim.x;
+  const int rounds = (int)blockIdx.x < n_items ? (n_items - 1 - (int)blockIdx.x) / G + 1 : 0;
+  int d_item = 0, d_b = 0, d_t0 = 0, d_t1 = 0;
+  if (lane < rounds) {
+    const int idx = blockIdx.x + lane * G;
+    const int item = ((n_items & 7) == 0 && (G & 7) == 0) ? (idx & 7) * (n_items >> 3) + (idx >> 3) : idx;
+    const int b = item_seq(s_items, a.batch, item);
+    d_item = item;
+    d_b = b;
+    d_t0 = (item - s_items[b]) * plan.chunk;
+    d_t1 = min(s_len[b], d_t0 + plan.chunk);
+  }
+  __syncthreads();  // the planner arrays in stage 3 are not read after this point
+
   const int g = lane >> 5, hl = lane & 31;
   const int hq = w * 32 + hl;
   const bool hvalid = hq < a.H;
   const int P = a.P;
   const char* __restrict__ pool = (const char*)a.pool;
-  const int32_t* __restrict__ btb = a.block_table + (size_t)b * a.max_pages_per_seq;
-  const int ntiles = (t1 - t0 + TT - 1) / TT;
-  auto tile_ptr = [&](int tile, int& nvalid) {
-    const int tok0 = t0 + tile * TT;
-    nvalid = min(TT, t1 - tok0);
-    const int page = btb[tok0 / P];
-    return pool + ((size_t)page * P + (tok0 % P)) * (RW * 2);
-  };
   const uint32_t lds_tiles = lds_addr_of(tiles);
   uint32_t lane_off[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) lane_off[rb] = load_lane_off(lane, NW == 4 ? w : rb);
-
-  // absorbed query fragments (B operand of the score MFMA), loaded before the
-  // first tiles so the tile waits below count only tile loads after them
-  u32x4 qf[KS];
-  {
-    const uint16_t* qp = (const uint16_t*)a.q_abs + ((size_t)b * a.H + (hvalid ? hq : 0)) * RW + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = *(const u32x4*)(qp + 16 * ks);
-      qf[ks] = hvalid ? v : u32x4{0, 0, 0, 0};
-    }
-  }
-  __syncthreads();  // planner arrays in stage 3 are no longer read
-  // prologue: tiles 0, 1, 2 in flight
-#pragma unroll
-  for (int st = 0; st < 3; ++st) {
-    if (st < ntiles) {
-      int nv;
-      const char* tp = tile_ptr(st, nv);
-      issue_tile<NW>(tp, nv, lds_tiles + st * TILE_BYTES, w, lane, lane_off);
-    }
-  }
-
   ReadOffsets ro;
   {
     const int sw = swz(hl);
@@ -350,288 +334,350 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
   const float sl2 = a.scale_log2;
   constexpr int LPW = LOADS_PER_TILE / NW;  // loads per wave per tile
 
-  f32x16 acc[FB];
-#pragma unroll
-  for (int i = 0; i < FB; ++i) acc[i] = f32x16{};
-  float lsum = 0.f;
-  bool overflow = false;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int item = __builtin_amdgcn_readlane(d_item, rd);
+    const int b = __builtin_amdgcn_readlane(d_b, rd);
+    const int t0 = __builtin_amdgcn_readlane(d_t0, rd);
+    const int t1 = __builtin_amdgcn_readlane(d_t1, rd);
+    const int32_t* __restrict__ btb = a.block_table + (size_t)b * a.max_pages_per_seq;
+    const int ntiles = (t1 - t0 + TT - 1) / TT;
+    auto tile_ptr = [&](int tile, int& nvalid) {
+      const int tok0 = t0 + tile * TT;
+      nvalid = min(TT, t1 - tok0);
+      const int page = btb[tok0 / P];
+      return pool + ((size_t)page * P + (tok0 % P)) * (RW * 2);
+    };
 
-  // tile 0: scores, reference maximum, numerators into P^T buffer 0
-  if (ntiles >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW));
-  else if (ntiles == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
-  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  f32x16 sacc;
-  {
-    constexpr int PF = 3;
-    u32x4 kf[PF];
+    // absorbed query fragments (B operand of the score MFMA: head hq,
+    // k = 16 ks + 8 g .. +7), loaded before the first tiles so the tile waits
+    // below count only tile loads after them
+    u32x4 qf[KS];
+    {
+      const uint16_t* qp = (const uint16_t*)a.q_abs + ((size_t)b * a.H + (hvalid ? hq : 0)) * RW + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x4*)(tiles + ro.s[ks & 3] + 4096 * (ks >> 2));
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 cur = kf[ks % PF];
-      if (ks + PF < KS) kf[ks % PF] = *(const u32x4*)(tiles + ro.s[(ks + PF) & 3] + 4096 * ((ks + PF) >> 2));
-      if (ks == 0) score_first(sacc, cur, qf[ks]);
-      else score_next(sacc, cur, qf[ks]);
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = *(const u32x4*)(qp + 16 * ks);
+        qf[ks] = hvalid ? v : u32x4{0, 0, 0, 0};
+      }
     }
-    score_drain(sacc);
-  }
-  const float m_ref = tile_max(sacc, t0, t1, g) * sl2;  // fixed for the whole item
-  tile_softmax(sacc, t0, t1, g, sl2, m_ref, pbufs, head_off, lsum, ro);
+    // prologue: tiles 0, 1, 2 in flight
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+      if (st < ntiles) {
+        int nv;
+        const char* tp = tile_ptr(st, nv);
+        issue_tile<NW>(tp, nv, lds_tiles + st * TILE_BYTES, w, lane, lane_off);
+      }
+    }
 
-  // step it: latent update of tile it (P^T buffer it % 2) interleaved with the
-  // scores of tile it+1, whose numerators go to P^T buffer (it+1) % 2
-  for (int it = 0; it + 1 < ntiles; ++it) {
-    int nv3 = 0;
-    const char* tp3 = (it + 3 < ntiles) ? tile_ptr(it + 3, nv3) : nullptr;  // scalar page load, early
-    // this wave's loads of tile it+1 are done once only tile it+2's remain
-    if (it + 2 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
+    f32x16 acc[FB];
+#pragma unroll
+    for (int i = 0; i < FB; ++i) acc[i] = f32x16{};
+    float lsum = 0.f;
+    bool overflow = false;
+
+    // tile 0: scores, reference maximum, numerators into P^T buffer 0
+    if (ntiles >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW));
+    else if (ntiles == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    // all waves: tile it+1 in LDS, P^T of tile it written, tile it-1 and
-    // P^T buffer (it+1) % 2 no longer read
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (it + 3 < ntiles) issue_tile<NW>(tp3, nv3, lds_tiles + ((it + 3) & 3) * TILE_BYTES, w, lane, lane_off);
-    const char* cur = tiles + (it & 3) * TILE_BYTES;
-    const char* nxt = tiles + ((it + 1) & 3) * TILE_BYTES;
-    tile_step<NW, true>(sacc, nxt, qf, acc, cur, pbufs + (it & 1) * PBUF_BYTES, w, ro);
-    const int tok1 = t0 + (it + 1) * TT;
-    overflow |= tile_max(sacc, tok1, t1, g) * sl2 > m_ref + kHeadroom;
-    tile_softmax(sacc, tok1, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum, ro);
-  }
-  // latent update of the last tile (its scores were taken in the last step)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  tile_step<NW, false>(sacc, tiles, qf, acc, tiles + ((ntiles - 1) & 3) * TILE_BYTES,
-                       pbufs + ((ntiles - 1) & 1) * PBUF_BYTES, w, ro);
-
-  lsum += __shfl_xor(lsum, 32);
-  // acc[fbl * HB + hb] holds O^T rows f = 32 (FBW w + fbl) + 8 (j/4) + 4 g + j % 4
-  // of head 32 hb + lane % 32
+    f32x16 sacc;
+    {
+      constexpr int PF = 3;
+      u32x4 kf[PF];
 #pragma unroll
-  for (int fbl = 0; fbl < S::FBW; ++fbl)
+      for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x4*)(tiles + ro.s[ks & 3] + 4096 * (ks >> 2));
 #pragma unroll
-    for (int hb = 0; hb < S::HB; ++hb) {
-      const int h = 32 * hb + hl;
-      if (h >= a.H) continue;
-      float* pa = a.part_acc + ((size_t)item * a.H + h) * DC + 32 * (S::FBW * w + fbl) + 4 * g;
-      const f32x16& v = acc[fbl * S::HB + hb];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) *(f32x4*)(pa + 8 * q4) = f32x4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 cur = kf[ks % PF];
+        if (ks + PF < KS) kf[ks % PF] = *(const u32x4*)(tiles + ro.s[(ks + PF) & 3] + 4096 * ((ks + PF) >> 2));
+        if (ks == 0) score_first(sacc, cur, qf[ks]);
+        else score_next(sacc, cur, qf[ks]);
+      }
+      score_drain(sacc);
     }
-  if (hvalid && g == 0) {
-    // +inf marks a partial the combine pass must recompute
-    a.part_ml[((size_t)item * a.H + hq) * 2 + 0] = overflow ? INFINITY : m_ref;
-    a.part_ml[((size_t)item * a.H + hq) * 2 + 1] = lsum;
+    const float m_ref = tile_max(sacc, t0, t1, g) * sl2;  // fixed for the whole item
+    tile_softmax(sacc, t0, t1, g, sl2, m_ref, pbufs, head_off, lsum, ro);
+
+    // step it: latent update of tile it (P^T buffer it % 2) interleaved with the
+    // scores of tile it+1, whose numerators go to P^T buffer (it+1) % 2
+    for (int it = 0; it + 1 < ntiles; ++it) {
+      int nv3 = 0;
+      const char* tp3 = (it + 3 < ntiles) ? tile_ptr(it + 3, nv3) : nullptr;  // scalar page load, early
+      // this wave's loads of tile it+1 are done once only tile it+2's remain
+      if (it + 2 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      // all waves: tile it+1 in LDS, P^T of tile it written, tile it-1 and
+      // P^T buffer (it+1) % 2 no longer read
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (it + 3 < ntiles) issue_tile<NW>(tp3, nv3, lds_tiles + ((it + 3) & 3) * TILE_BYTES, w, lane, lane_off);
+      const char* cur = tiles + (it & 3) * TILE_BYTES;
+      const char* nxt = tiles + ((it + 1) & 3) * TILE_BYTES;
+      tile_step<NW, true>(sacc, nxt, qf, acc, cur, pbufs + (it & 1) * PBUF_BYTES, w, ro);
+      const int tok1 = t0 + (it + 1) * TT;
+      overflow |= tile_max(sacc, tok1, t1, g) * sl2 > m_ref + kHeadroom;
+      tile_softmax(sacc, tok1, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum, ro);
+    }
+    // latent update of the last tile (its scores were taken in the last step)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    tile_step<NW, false>(sacc, tiles, qf, acc, tiles + ((ntiles - 1) & 3) * TILE_BYTES,
+                         pbufs + ((ntiles - 1) & 1) * PBUF_BYTES, w, ro);
+
+    lsum += __shfl_xor(lsum, 32);
+    if (hvalid && g == 0) {
+      // +inf marks a partial the combine pass must recompute
+      a.part_ml[((size_t)item * a.H + hq) * 2 + 0] = overflow ? INFINITY : m_ref;
+      a.part_ml[((size_t)item * a.H + hq) * 2 + 1] = lsum;
+    }
+    // acc[fbl * HB + hb] holds O^T rows f = 32 (FBW w + fbl) + 8 (j/4) + 4 g + j % 4
+    // of head 32 hb + lane % 32
+#pragma unroll
+    for (int fbl = 0; fbl < S::FBW; ++fbl)
+#pragma unroll
+      for (int hb = 0; hb < S::HB; ++hb) {
+        const int h = 32 * hb + hl;
+        if (h >= a.H) continue;
+        float* pa = a.part_acc + ((size_t)item * a.H + h) * DC + 32 * (S::FBW * w + fbl) + 4 * g;
+        const f32x16& v = acc[fbl * S::HB + hb];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(f32x4*)(pa + 8 * q4) = f32x4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+      }
+    // the next round's query loads and tiles reuse LDS and registers
+    __syncthreads();
   }
 }
 
 // --------------------------------------------------------------------------
 // Exact two-pass partial (m, l, acc) of one (item, head) in fp32, used only for
 // partials the split pass flagged.  scratch: >= 576 + 256 floats of LDS.
-__device__ __noinline__ void recompute_partial(const DecodeArgs& a, int item, int b, int h, int t0, int t1,
+// The arguments are plain values (no pointer to the kernel's argument block,
+// which would force that block into scratch memory in the caller).
+__device__ __noinline__ void recompute_partial(const uint16_t* __restrict__ pool, const int32_t* __restrict__ bt,
+                                               const uint16_t* __restrict__ qa, float* __restrict__ pa,
+                                               float* __restrict__ pml, int P, float scale_log2, int t0, int t1,
                                                float* scratch, int* red) {
+  // blockDim.x in {256, 512}: thread tid keeps latent columns tid (+ blockDim.x)
+  const int nth = blockDim.x;
   float* q = scratch;          // 576
-  float* p = scratch + RW;     // 256
+  float* p = scratch + RW;     // blockDim.x
   const int tid = threadIdx.x;
-  const uint16_t* pool = (const uint16_t*)a.pool;
-  const int32_t* bt = a.block_table + (size_t)b * a.max_pages_per_seq;
-  const uint16_t* qa = (const uint16_t*)a.q_abs + ((size_t)b * a.H + h) * RW;
   __syncthreads();
-  for (int f = tid; f < RW; f += blockDim.x) q[f] = bf16_to_f32(qa[f]);
+  for (int f = tid; f < RW; f += nth) q[f] = bf16_to_f32(qa[f]);
   __syncthreads();
   auto score = [&](int t) {
-    const uint16_t* row = pool + ((size_t)bt[t / a.P] * a.P + t % a.P) * RW;
+    const uint16_t* row = pool + ((size_t)bt[t / P] * P + t % P) * RW;
     float d = 0.f;
     for (int f = 0; f < RW; ++f) d += q[f] * bf16_to_f32(row[f]);
-    return d * a.scale_log2;
+    return d * scale_log2;
   };
   float m = -INFINITY;
-  for (int t = t0 + tid; t < t1; t += blockDim.x) m = fmaxf(m, score(t));
+  for (int t = t0 + tid; t < t1; t += nth) m = fmaxf(m, score(t));
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((tid & 63) == 0) red[tid >> 6] = __float_as_int(m);
   __syncthreads();
   m = -INFINITY;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, __int_as_float(red[w]));
+  for (int w = 0; w < (nth >> 6); ++w) m = fmaxf(m, __int_as_float(red[w]));
+  const int c0 = tid, c1 = tid + nth;
   float acc0 = 0.f, acc1 = 0.f, l = 0.f;
-  for (int tb = t0; tb < t1; tb += blockDim.x) {
+  for (int tb = t0; tb < t1; tb += nth) {
     __syncthreads();
     const int t = tb + tid;
     p[tid] = (t < t1) ? exp2f(score(t) - m) : 0.f;
     __syncthreads();
-    const int nt = min((int)blockDim.x, t1 - tb);
+    const int nt = min(nth, t1 - tb);
     for (int k = 0; k < nt; ++k) {
       const int tt = tb + k;
-      const uint16_t* row = pool + ((size_t)bt[tt / a.P] * a.P + tt % a.P) * RW;
+      const uint16_t* row = pool + ((size_t)bt[tt / P] * P + tt % P) * RW;
       const float pk = p[k];
       l += pk;  // every thread keeps the full sum
-      acc0 += pk * bf16_to_f32(row[tid]);
-      acc1 += pk * bf16_to_f32(row[tid + 256]);
+      acc0 += pk * bf16_to_f32(row[c0]);
+      if (c1 < DC) acc1 += pk * bf16_to_f32(row[c1]);
     }
   }
-  float* pa = a.part_acc + ((size_t)item * a.H + h) * DC;
-  pa[tid] = acc0;
-  pa[tid + 256] = acc1;
+  pa[c0] = acc0;
+  if (c1 < DC) pa[c1] = acc1;
   if (tid == 0) {
-    a.part_ml[((size_t)item * a.H + h) * 2 + 0] = m;
-    a.part_ml[((size_t)item * a.H + h) * 2 + 1] = l;
+    pml[0] = m;
+    pml[1] = l;
   }
   __syncthreads();
 }
 
 // --------------------------------------------------------------------------
-// combine: grid (H, ceil(batch/32)), 256 threads.
-constexpr int CB = 32;  // sequences per combine work-group
-__global__ void __launch_bounds__(256) k_combine(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lat_hi[CB * DC];
+// combine: grid (H, ceil(batch / 16)), 512 threads (8 waves).  Work-group
+// (h, sequences b0 .. b0+15): merge the partials of every item of those
+// sequences into the latent output (fp32), then o = W_UV,h lat with MFMA.
+constexpr int CB = 16;   // sequences per combine work-group
+constexpr int CNW = 8;   // waves per combine work-group
+constexpr int CNB = 2;   // items per sequence whose loads are in flight together
+__global__ void __launch_bounds__(64 * CNW, 4) k_combine(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lat_hi[CB * DC];  // [seq][512], 16-byte slot p ^ seq
   __shared__ __attribute__((aligned(16))) uint16_t lat_lo[CB * DC];
-  __shared__ int s_len[kMaxDecodeBatch + 1];
-  __shared__ int s_items[kMaxDecodeBatch + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t o_st[CB * 256];   // output rows (d_v <= 256)
+  __shared__ int s_items[CB + 1], s_len[CB];
   __shared__ int red[16];
-  __shared__ float s_ms[CB], s_il[CB];  // per-sequence reference max m* and 1 / L
-  __shared__ int s_maxn;
+  __shared__ int s_chunk;
 
-  const int cap = a.len_cap;
-  const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
-                                           a.ovh_tokens, s_len, s_items, red);
   const int h = blockIdx.x, b0 = blockIdx.y * CB;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, r = lane & 31;
-  const int bend = min(a.batch, b0 + CB);
-  const int i_lo = s_items[b0], i_hi = s_items[bend];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nb = min(CB, a.batch - b0);
+  const float* __restrict__ pml = a.part_ml;
+  const float* __restrict__ pacc = a.part_acc;
 
-  // W_UV fragments of this wave's first 32 output columns, fetched up front so
-  // their latency hides behind the merge (B operand: v = lane % 32, 8 latent
-  // values from 16 ks + 8 g)
-  const uint16_t* wuv = (const uint16_t*)a.w_uv + (size_t)h * a.d_v * DC;
-  u32x4 wf[DC / 16];
-  const bool wpre = w * 32 < a.d_v;
-  if (wpre) {
-    const uint16_t* wrow = wuv + (size_t)(w * 32 + r) * DC + 8 * g;
+  // the plan the split pass published
+  if (tid <= nb) s_items[tid] = a.plan[b0 + tid];
+  if (tid < nb) s_len[tid] = a.plan[a.batch + 1 + b0 + tid];
+  if (tid == 0) s_chunk = a.plan[2 * a.batch + 1];
+  __syncthreads();
+
+  // thread: latent columns 4 cq .. 4 cq + 3 of sequences bl = tid / 128 + 4 k.
+  // Online merge over the items in index order, CNB items per step:
+  //   m = max(m, m_i);  v = v 2^(m_old - m) + sum_i 2^(m_i - m) acc_i;  L likewise.
+  // A partial flagged by the split pass (m_i = +inf) is recomputed exactly
+  // first and the merge redone.
+  const int cq = tid & 127, blo = tid >> 7;
+  constexpr int NS = CB / 4;
+  f32x4 v[NS];
+  float mrun[NS], lrun[NS];
+  for (int pass = 0; pass < 2; ++pass) {
+    int flagged = 0;
 #pragma unroll
-    for (int ks = 0; ks < DC / 16; ++ks) wf[ks] = *(const u32x4*)(wrow + 16 * ks);
-  }
-
-  // rare path: partials flagged by the split pass are recomputed here, exactly.
-  // The flags of this block's items are checked in parallel first.
-  {
-    int any = 0;
-    for (int i = i_lo + tid; i < i_hi; i += 256) any |= a.part_ml[((size_t)i * a.H + h) * 2] == INFINITY;
-    any = __syncthreads_or(any);
-    if (any) {
-      for (int bl = 0; bl < CB && b0 + bl < a.batch; ++bl) {
-        const int b = b0 + bl;
-        for (int i = s_items[b]; i < s_items[b + 1]; ++i) {
-          if (a.part_ml[((size_t)i * a.H + h) * 2] != INFINITY) continue;  // same value in every thread
-          const int t0 = (i - s_items[b]) * plan.chunk;
-          const int t1 = min(s_len[b], t0 + plan.chunk);
-          recompute_partial(a, i, b, h, t0, t1, (float*)lat_hi, red);
+    for (int k = 0; k < NS; ++k) {
+      v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mrun[k] = -INFINITY;
+      lrun[k] = 0.f;
+    }
+    int maxn = 0;
+    for (int k = 0; k < NS; ++k) {
+      const int bl = blo + 4 * k;
+      if (bl < nb) maxn = max(maxn, s_items[bl + 1] - s_items[bl]);
+    }
+    for (int j0 = 0; j0 < maxn; j0 += CNB) {
+      float mi[NS][CNB], li[NS][CNB];
+      f32x4 ai[NS][CNB];
+#pragma unroll
+      for (int k = 0; k < NS; ++k)
+#pragma unroll
+        for (int jj = 0; jj < CNB; ++jj) {
+          const int bl = blo + 4 * k;
+          const int i = (bl < nb) ? s_items[bl] + j0 + jj : 0;
+          const bool ok = bl < nb && i < s_items[bl + 1];
+          const uint32_t ih = (uint32_t)(ok ? i : 0) * (uint32_t)a.H + (uint32_t)h;
+          const float2 ml = ok ? *(const float2*)((const char*)pml + 8u * ih) : make_float2(-INFINITY, 0.f);
+          mi[k][jj] = ml.x;
+          li[k][jj] = ml.y;
+          ai[k][jj] = ok ? *(const f32x4*)((const char*)pacc + (uint32_t)(DC * 4) * ih + 16u * cq)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-      }
-      __syncthreads();
-    }
-  }
-
-  // per-sequence merge statistics in a fixed item order: m* = max m_i,
-  // L = sum 2^(m_i - m*) l_i; item i then weighs 2^(m_i - m*) / L
-  if (tid == 0) s_maxn = 0;
-  __syncthreads();
-  if (tid < CB) {
-    const int b = b0 + tid;
-    float ms = 0.f, il = 0.f;
-    if (b < a.batch) {
-      const int i0 = s_items[b], i1 = s_items[b + 1];
-      ms = -INFINITY;
-      float L = 0.f;
-      for (int i = i0; i < i1; ++i) ms = fmaxf(ms, a.part_ml[((size_t)i * a.H + h) * 2]);
-      for (int i = i0; i < i1; ++i)
-        L += exp2f(a.part_ml[((size_t)i * a.H + h) * 2] - ms) * a.part_ml[((size_t)i * a.H + h) * 2 + 1];
-      if (a.lse) a.lse[(size_t)b * a.H + h] = (i1 > i0) ? (ms + log2f(L)) * kLn2 : -INFINITY;
-      il = (L > 0.f) ? 1.f / L : 0.f;
-      atomicMax(&s_maxn, i1 - i0);
-    }
-    s_ms[tid] = ms;
-    s_il[tid] = il;
-  }
-  __syncthreads();
-
-  // merged latent of sequence b0 + bl at columns 4 cq .. 4 cq + 3: the thread
-  // takes cq = tid % 128 and the sequences bl = tid / 128 + 2 k; for each item
-  // index j the loads of all its sequences are issued before any is used
-  {
-    const int cq = tid & 127, blo = tid >> 7;
-    f32x4 v[CB / 2];
 #pragma unroll
-    for (int k = 0; k < CB / 2; ++k) v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int maxn = s_maxn;
-    for (int j = 0; j < maxn; ++j) {
-      float ml[CB / 2];
-      bool ok[CB / 2];
-      f32x4 pa[CB / 2];
+      for (int k = 0; k < NS; ++k) {
+        float mn = mrun[k];
 #pragma unroll
-      for (int k = 0; k < CB / 2; ++k) {
-        const int bl = blo + 2 * k, b = b0 + bl;
-        const int i = (b < a.batch) ? s_items[b] + j : 0;
-        ok[k] = b < a.batch && i < s_items[b + 1];
-        const size_t ih = (size_t)(ok[k] ? i : 0) * a.H + h;
-        ml[k] = ok[k] ? a.part_ml[ih * 2] : 0.f;
-        pa[k] = ok[k] ? *(const f32x4*)(a.part_acc + ih * DC + 4 * cq) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+        for (int jj = 0; jj < CNB; ++jj) {
+          flagged |= mi[k][jj] == INFINITY;
+          mn = fmaxf(mn, mi[k][jj]);
+        }
+        if (mn == -INFINITY) continue;  // no item yet
+        const float sc = exp2f(mrun[k] - mn);  // 0 when mrun = -inf
+        v[k] *= sc;
+        lrun[k] *= sc;
 #pragma unroll
-      for (int k = 0; k < CB / 2; ++k) {
-        const int bl = blo + 2 * k;
-        const float wgt = ok[k] ? exp2f(ml[k] - s_ms[bl]) * s_il[bl] : 0.f;
-        v[k] += wgt * pa[k];
+        for (int jj = 0; jj < CNB; ++jj) {
+          const float wgt = exp2f(mi[k][jj] - mn);  // 0 for absent items (m = -inf)
+          v[k] += wgt * ai[k][jj];
+          lrun[k] += wgt * li[k][jj];
+        }
+        mrun[k] = mn;
       }
     }
-#pragma unroll
-    for (int k = 0; k < CB / 2; ++k) {
-      const int bl = blo + 2 * k;
-      const int chunk = cq >> 1, within = (cq & 1) * 4;
-      const int pos = bl * (DC / 8) + (chunk ^ (bl & 7));
-      uint32_t hw[2], lw[2];
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        const uint32_t hp = pack_bf16x2(v[k][e], v[k][e + 1]);
-        const float h0 = __uint_as_float(hp << 16), h1 = __uint_as_float(hp & 0xffff0000u);
-        hw[e >> 1] = hp;
-        lw[e >> 1] = pack_bf16x2(v[k][e] - h0, v[k][e + 1] - h1);
-      }
-      *(uint2*)(lat_hi + pos * 8 + within) = make_uint2(hw[0], hw[1]);
-      *(uint2*)(lat_lo + pos * 8 + within) = make_uint2(lw[0], lw[1]);
-    }
-  }
-  __syncthreads();
-
-  // out[b][h][v] = sum_c lat[b][c] W_UV[h][v][c]: D[b][v], A = lat (b = lane%32),
-  // B = W_UV^T; lat = hi + lo carries the fp32 merge to ~2^-17
-  for (int vb = w; vb * 32 < a.d_v; vb += 4) {
-    f32x16 acc = f32x16{};
-    const uint16_t* wrow = wuv + (size_t)(vb * 32 + r) * DC + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < DC / 16; ++ks) {
-      const u32x4 bw = (vb == w) ? wf[ks] : *(const u32x4*)(wrow + 16 * ks);
-      const int pos = r * (DC / 8) + ((2 * ks + g) ^ (r & 7));
-      const u32x4 ah = *(const u32x4*)(lat_hi + pos * 8);
-      const u32x4 al = *(const u32x4*)(lat_lo + pos * 8);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bw), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(al), as_bf16x8(bw), acc, 0, 0, 0);
-    }
-    const int v = vb * 32 + r;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int bl = 8 * (j >> 2) + 4 * g + (j & 3);
+    if (__syncthreads_or(flagged) == 0) break;
+    if (pass == 1) break;  // recomputed partials are finite
+    for (int bl = 0; bl < nb; ++bl) {
       const int b = b0 + bl;
-      if (b < a.batch) ((uint16_t*)a.out)[((size_t)b * a.H + h) * a.d_v + v] = f32_to_bf16(acc[j]);
+      for (int i = s_items[bl]; i < s_items[bl + 1]; ++i) {
+        if (pml[((size_t)i * a.H + h) * 2] != INFINITY) continue;  // same value in every thread
+        const int t0 = (i - s_items[bl]) * s_chunk;
+        const int t1 = min(s_len[bl], t0 + s_chunk);
+        const size_t ih = (size_t)i * a.H + h;
+        recompute_partial((const uint16_t*)a.pool, a.block_table + (size_t)b * a.max_pages_per_seq,
+                          (const uint16_t*)a.q_abs + ((size_t)b * a.H + h) * RW, a.part_acc + ih * DC,
+                          a.part_ml + ih * 2, a.P, a.scale_log2, t0, t1, (float*)lat_hi, red);
+      }
     }
+    __syncthreads();
+  }
+
+  // lat = v / L as bf16 hi + lo (the pair carries the fp32 value to ~2^-17)
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int bl = blo + 4 * k;
+    const float il = lrun[k] > 0.f ? 1.f / lrun[k] : 0.f;
+    if (cq == 0 && bl < nb && a.lse)
+      a.lse[(size_t)(b0 + bl) * a.H + h] = lrun[k] > 0.f ? (mrun[k] + log2f(lrun[k])) * kLn2 : -INFINITY;
+    const f32x4 x = v[k] * il;
+    const int pos = bl * (DC / 8) + ((cq >> 1) ^ bl);
+    const int within = (cq & 1) * 4;
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const uint32_t hp = pack_bf16x2(x[e], x[e + 1]);
+      const float h0 = __uint_as_float(hp << 16), h1 = __uint_as_float(hp & 0xffff0000u);
+      hw[e >> 1] = hp;
+      lw[e >> 1] = pack_bf16x2(x[e] - h0, x[e + 1] - h1);
+    }
+    *(uint2*)(lat_hi + pos * 8 + within) = make_uint2(hw[0], hw[1]);
+    *(uint2*)(lat_lo + pos * 8 + within) = make_uint2(lw[0], lw[1]);
+  }
+  __syncthreads();
+
+  // out[b][h][v] = sum_c lat[b][c] W_UV[h][v][c], 16x16x32 MFMA: D[seq][v],
+  // A = lat (row = lane % 16, k = 8 (lane / 16) of each 32-wide step),
+  // B = W_UV^T (column v = lane % 16).  Wave w takes 16-column blocks w, w + 8, ...
+  const uint16_t* wuv = (const uint16_t*)a.w_uv + (size_t)h * a.d_v * DC;
+  const int m16 = lane & 15, q = lane >> 4;
+  for (int vb = w; vb * 16 < a.d_v; vb += CNW) {
+    asm volatile("" ::: "memory");  // keeps the latent fragment reads inside the loop (registers)
+    const uint16_t* wrow = wuv + (size_t)(vb * 16 + m16) * DC + 8 * q;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int KH = DC / 64;  // k-steps per half
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 wf[KH];
+#pragma unroll
+      for (int k = 0; k < KH; ++k) wf[k] = *(const u32x4*)(wrow + 32 * (KH * half + k));
+#pragma unroll
+      for (int k = 0; k < KH; ++k) {
+        const int ks = KH * half + k;
+        const int pos = m16 * (DC / 8) + ((4 * ks + q) ^ m16);
+        const u32x4 ah = *(const u32x4*)(lat_hi + pos * 8);
+        const u32x4 al = *(const u32x4*)(lat_lo + pos * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(wf[k]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(wf[k]), acc, 0, 0, 0);
+      }
+    }
+    // D: lane holds column v = lane % 16 of sequences 4 (lane / 16) + j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o_st[(4 * q + j) * 256 + vb * 16 + m16] = f32_to_bf16(acc[j]);
+  }
+  __syncthreads();
+  // output rows to HBM, 16 bytes per lane
+  const int pieces = a.d_v / 8;
+  for (int u = tid; u < nb * pieces; u += 64 * CNW) {
+    const int bl = u / pieces, pc = u % pieces;
+    *(u32x4*)((uint16_t*)a.out + ((size_t)(b0 + bl) * a.H + h) * a.d_v + 8 * pc) =
+        *(const u32x4*)(o_st + bl * 256 + 8 * pc);
   }
 }
 
 }  // namespace
 
 bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch) {
-  return d_c == DC && d_r == DR && H >= 1 && H <= 128 && d_v >= 32 && d_v % 32 == 0 && P >= TT && P % TT == 0 &&
+  return d_c == DC && d_r == DR && H >= 1 && H <= 128 && d_v >= 32 && d_v <= 256 && d_v % 32 == 0 && P >= TT &&
+         P % TT == 0 &&
          batch <= kMaxDecodeBatch;
 }
 
@@ -639,13 +685,19 @@ bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch) {
 static int split_waves(int H) { return H <= 32 ? 1 : (H <= 64 ? 2 : 4); }
 
 int decode_mfma_slots(int H, int cus) {
-  // one work-group per CU at 4 waves (registers); narrower groups pack 4 waves per CU
-  return cus * (4 / split_waves(H));
+  // the split kernel holds the whole LDS of a CU: one work-group per CU
+  (void)H;
+  return cus;
+}
+
+int decode_mfma_grid(int slots, int max_items) {
+  // rounds per work-group stay <= 64 (one per lane of the descriptor wave)
+  return max(slots, (max_items + 63) / 64);
 }
 
 hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  const dim3 g1(a.max_items);
+  const dim3 g1(decode_mfma_grid(a.slots, a.max_items));
   switch (split_waves(a.H)) {
     case 1: hipLaunchKernelGGL(k_split<1>, g1, dim3(64), 0, s, a); break;
     case 2: hipLaunchKernelGGL(k_split<2>, g1, dim3(128), 0, s, a); break;
@@ -653,7 +705,7 @@ hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_combine, dim3(a.H, (a.batch + CB - 1) / CB), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_combine, dim3(a.H, (a.batch + CB - 1) / CB), dim3(64 * CNW), 0, s, a);
   return hipGetLastError();
 }
 

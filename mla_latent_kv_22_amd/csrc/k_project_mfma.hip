@@ -23,8 +23,16 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------- cache write
-template <int TB4, int NWV>
+// Every wave owns a contiguous range of 64-wide k chunks.  A chunk of the 16
+// W rows and 16 * TB4 h rows is fetched with whole 128-byte lines per row (8
+// lanes x 16 bytes), staged in the wave's own LDS slice and read back as MFMA
+// fragments: row-scattered 16-byte fragment loads run at a fraction of the
+// coalesced rate on this part.  LDS slice row layout: 8 16-byte pieces,
+// piece p of row r at slot p ^ (r % 8) (conflict-free fragment reads).
+template <int TB4, int NWV, int KB>
 __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
+  constexpr int ROWS = 16 + 16 * TB4;  // W rows, then h rows
+  __shared__ __attribute__((aligned(16))) uint16_t stage[NWV][KB][ROWS * 64];
   __shared__ f32x4 part[NWV][TB4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int R = a.d_c + a.d_r;
@@ -32,51 +40,85 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
   const int n0 = blockIdx.y * 16 * TB4;
   const uint16_t* __restrict__ W = (const uint16_t*)a.w_dkr;
   const uint16_t* __restrict__ H = (const uint16_t*)a.h;
-  const int D = a.D, ksteps = D / 32;
-  const int m = lane & 15, kq = 8 * (lane >> 4);
+  const int D = a.D, nchunk = D / 64;
+  const int per = (nchunk + NWV - 1) / NWV;
+  const int cbeg = w * per, cend = min(nchunk, cbeg + per);
+  const int lrow = lane >> 3, lpc = lane & 7;  // loader: rows lrow + 8 i, 16-byte piece lpc
+  const int m = lane & 15, q = lane >> 4;      // fragment: row m, k group q
+
+  // slot and position of the epilogue's token, fetched before the main loop
+  long long slot[TB4];
+  int pos[TB4];
+#pragma unroll
+  for (int t = 0; t < TB4; ++t) {
+    const int n = n0 + 16 * t + m;
+    const bool mine = (t % NWV) == w && n < a.n_tokens;
+    slot[t] = mine ? a.slots[n] : -1;
+    pos[t] = mine ? a.positions[n] : 0;
+  }
 
   f32x4 acc[TB4];
 #pragma unroll
   for (int t = 0; t < TB4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* wp = W + (size_t)(r0 + m) * D + kq;
-  const uint16_t* hp[TB4];
-  bool hv[TB4];
+  for (int c0 = cbeg; c0 < cend; c0 += KB) {
+    u32x4 v[KB][ROWS / 8];
 #pragma unroll
-  for (int t = 0; t < TB4; ++t) {
-    const int n = n0 + 16 * t + m;
-    hv[t] = n < a.n_tokens;
-    hp[t] = H + (size_t)(hv[t] ? n : 0) * D + kq;
-  }
-#pragma unroll 8
-  for (int ks = w; ks < ksteps; ks += NWV) {
-    const u32x4 av = *(const u32x4*)(wp + 32 * ks);
+    for (int u = 0; u < KB; ++u) {
+      const bool ok = c0 + u < cend;
+      const int k = 64 * (c0 + u) + 8 * lpc;
 #pragma unroll
-    for (int t = 0; t < TB4; ++t) {
-      u32x4 bv = *(const u32x4*)(hp[t] + 32 * ks);
-      if (!hv[t]) bv = u32x4{0, 0, 0, 0};
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[t], 0, 0, 0);
+      for (int i = 0; i < ROWS / 8; ++i) {
+        const int row = lrow + 8 * i;
+        if (row < 16) {
+          v[u][i] = ok ? *(const u32x4*)(W + (size_t)(r0 + row) * D + k) : u32x4{0, 0, 0, 0};
+        } else {
+          const int n = n0 + row - 16;
+          v[u][i] = (ok && n < a.n_tokens) ? *(const u32x4*)(H + (size_t)n * D + k) : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+#pragma unroll
+      for (int i = 0; i < ROWS / 8; ++i) {
+        const int row = lrow + 8 * i;
+        *(u32x4*)(&stage[w][u][row * 64 + 8 * (lpc ^ (row & 7))]) = v[u][i];
+      }
+    // the slice is private to the wave and LDS operations of one wave complete
+    // in order, so the fragment reads below see the stores without a barrier
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (c0 + u >= cend) break;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int sl = (4 * kk + q) ^ (m & 7);
+        const u32x4 av = *(const u32x4*)(&stage[w][u][m * 64 + 8 * sl]);
+#pragma unroll
+        for (int t = 0; t < TB4; ++t) {
+          const u32x4 bv = *(const u32x4*)(&stage[w][u][(16 + 16 * t + m) * 64 + 8 * sl]);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[t], 0, 0, 0);
+        }
+      }
     }
   }
 #pragma unroll
   for (int t = 0; t < TB4; ++t) part[w][t][lane] = acc[t];
   __syncthreads();
   // epilogue: waves take token sub-blocks; fixed summation order over waves
-  for (int t = w; t < TB4; t += NWV) {
+#pragma unroll
+  for (int t = 0; t < TB4; ++t) {
+    if ((t % NWV) != w || slot[t] < 0) continue;
     f32x4 v = part[0][t][lane];
 #pragma unroll
     for (int k = 1; k < NWV; ++k) v += part[k][t][lane];
-    const int n = n0 + 16 * t + m;  // D: lane holds token n = lane % 16, features 4 (lane / 16) + j
-    if (n >= a.n_tokens) continue;
-    const long long slot = a.slots[n];
-    if (slot < 0) continue;
+    // D: lane holds token n = lane % 16, features 4 (lane / 16) + j
     const int rf = r0 + 4 * (lane >> 4);
     float o[4] = {v[0], v[1], v[2], v[3]};
     if (rf >= a.d_c) {
-      const int pos = a.positions[n];
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         float c, s;
-        rope_cs(pos, (rf - a.d_c) / 2 + pr, a.d_r, a.rope_base, c, s);
+        rope_cs(pos[t], (rf - a.d_c) / 2 + pr, a.d_r, a.rope_base, c, s);
         const float x0 = o[2 * pr], x1 = o[2 * pr + 1];
         o[2 * pr] = x0 * c - x1 * s;
         o[2 * pr + 1] = x0 * s + x1 * c;
@@ -84,7 +126,7 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
     }
     const uint32_t lo = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-    uint16_t* dst = (uint16_t*)a.pool + (size_t)slot * R + rf;
+    uint16_t* dst = (uint16_t*)a.pool + (size_t)slot[t] * R + rf;
     *(uint2*)dst = make_uint2(lo, hi);
   }
 }
@@ -93,45 +135,68 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
 constexpr int AB_C = 128;  // latent columns per work-group
 constexpr int AB_T = 64;   // tokens per work-group
 
+// LDS: W_UK,h column block (d_n rows x 256 bytes), the q_C block (64 tokens x
+// d_n) and the output tile (64 tokens x 128 columns).  q and the output move
+// between HBM and LDS in whole rows (16 lanes x 16 bytes per 256-byte row
+// segment); the MFMA fragments are LDS reads.
+template <int KMAX>
 __global__ void __launch_bounds__(256) k_absorb_mfma(AbsorbArgs a) {
-  // W_UK,h[j][cb*128 .. +128] row-major, 256 bytes per row j; 16-byte chunk
-  // slot XOR 2*(j % 4) makes the 4-row transpose reads conflict-free
-  extern __shared__ __attribute__((aligned(16))) char wtile[];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int dn = a.d_n;
+  char* wtile = smem;                          // dn x 256 B, chunk slot ch ^ 2 (j % 4)
+  char* qtile = smem + dn * 256;               // 64 x (2 dn) B, piece p at slot p ^ (row % 8)
+  char* otile = qtile + AB_T * 2 * dn;         // 64 x 256 B, piece p at slot p ^ (row % 8)
   const int h = blockIdx.x, cb = blockIdx.y, n0 = blockIdx.z * AB_T;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int H = a.H, dn = a.d_n, dc = a.d_c, dq = a.d_n + a.d_r, R = a.d_c + a.d_r;
+  const int H = a.H, dc = a.d_c, dq = a.d_n + a.d_r, R = a.d_c + a.d_r;
+  const int qp_row = dn / 8;  // 16-byte pieces per q_C row
   const uint16_t* __restrict__ wuk = (const uint16_t*)a.w_uk + (size_t)h * dn * dc + cb * AB_C;
-  // staged 8 chunks per thread at a time, all loads in flight before the stores
-  for (int u0 = 0; u0 < dn * (AB_C / 8); u0 += 8 * 256) {
+  const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
+  uint16_t* __restrict__ out = (uint16_t*)a.q_abs;
+
+  // stage W_UK block and q_C block, 8 chunks per thread in flight at a time
+  const int nw = dn * (AB_C / 8), nq = AB_T * qp_row;
+  for (int u0 = 0; u0 < nw + nq; u0 += 8 * 256) {
     u32x4 v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int u = u0 + k * 256 + tid, j = u >> 4, ch = u & 15;
-      if (u < dn * (AB_C / 8)) v[k] = *(const u32x4*)(wuk + (size_t)j * dc + 8 * ch);
+      const int u = u0 + k * 256 + tid;
+      if (u < nw) {
+        const int j = u >> 4, ch = u & 15;
+        v[k] = *(const u32x4*)(wuk + (size_t)j * dc + 8 * ch);
+      } else if (u < nw + nq) {
+        const int t = (u - nw) / qp_row, pc = (u - nw) % qp_row;
+        const int n = n0 + t;
+        v[k] = n < a.n_tokens ? *(const u32x4*)(Q + ((size_t)n * H + h) * dq + 8 * pc) : u32x4{0, 0, 0, 0};
+      }
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int u = u0 + k * 256 + tid, j = u >> 4, ch = u & 15;
-      if (u < dn * (AB_C / 8)) *(u32x4*)(wtile + j * 256 + 16 * (ch ^ (2 * (j & 3)))) = v[k];
+      const int u = u0 + k * 256 + tid;
+      if (u < nw) {
+        const int j = u >> 4, ch = u & 15;
+        *(u32x4*)(wtile + j * 256 + 16 * (ch ^ (2 * (j & 3)))) = v[k];
+      } else if (u < nw + nq) {
+        const int t = (u - nw) / qp_row, pc = (u - nw) % qp_row;
+        *(u32x4*)(qtile + t * 2 * dn + 16 * (pc ^ (t & 7))) = v[k];
+      }
     }
   }
   __syncthreads();
 
-  const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
-  uint16_t* __restrict__ out = (uint16_t*)a.q_abs;
   const int g = lane >> 5, r = lane & 31;
   const int grp = lane >> 4, jl = lane & 15;
   // B operand (W^T fragment): lane gets W[k0 .. k0+3][col], col = 32 w + lane % 32
   const int tcol = 32 * w + 16 * (grp & 1) + 4 * (jl & 3);  // first column of the lane's 8-byte load
+#pragma unroll
   for (int tb = 0; tb < AB_T / 32; ++tb) {
-    const int n = n0 + 32 * tb + r;  // A operand: token = lane % 32
-    const bool nv = n < a.n_tokens;
-    const uint16_t* qp = Q + ((size_t)(nv ? n : 0) * H + h) * dq + 8 * g;
+    const int trow = 32 * tb + r;  // A operand: token row = lane % 32
     f32x16 acc = f32x16{};
-#pragma unroll 8
-    for (int ks = 0; ks < dn / 16; ++ks) {
-      u32x4 av = *(const u32x4*)(qp + 16 * ks);
-      if (!nv) av = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < KMAX; ++ks) {
+      if (ks >= dn / 16) continue;
+      const int pc = 2 * ks + g;
+      const u32x4 av = *(const u32x4*)(qtile + trow * 2 * dn + 16 * (pc ^ (trow & 7)));
       const int k0 = 16 * ks + 8 * g;
       const int j1 = k0 + (jl >> 2), j2 = j1 + 4;
       const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -142,55 +207,82 @@ __global__ void __launch_bounds__(256) k_absorb_mfma(AbsorbArgs a) {
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
     }
     // D[token][col]: lane holds col = 32 w + lane % 32, tokens 8 (j/4) + 4 g + j % 4
-    const int col = cb * AB_C + 32 * w + r;
+    const int col = 32 * w + r;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int nn = n0 + 32 * tb + 8 * (j >> 2) + 4 * g + (j & 3);
-      if (nn < a.n_tokens) out[((size_t)nn * H + h) * R + col] = f32_to_bf16(acc[j]);
+      const int t = 32 * tb + 8 * (j >> 2) + 4 * g + (j & 3);
+      *(uint16_t*)(otile + t * 256 + 16 * ((col >> 3) ^ (t & 7)) + 2 * (col & 7)) = f32_to_bf16(acc[j]);
     }
   }
+  __syncthreads();
+  // output tile to HBM in whole 256-byte row segments
+#pragma unroll
+  for (int k = 0; k < AB_T * 16 / 256; ++k) {
+    const int u = k * 256 + tid, t = u >> 4, pc = u & 15;
+    const int n = n0 + t;
+    if (n < a.n_tokens)
+      *(u32x4*)(out + ((size_t)n * H + h) * R + cb * AB_C + 8 * pc) =
+          *(const u32x4*)(otile + t * 256 + 16 * (pc ^ (t & 7)));
+  }
   if (cb == 0) {
+    // rotary half: 8 (token, pair) units per thread in flight at once
     const int np = a.d_r / 2;
-    for (int u = tid; u < AB_T * np; u += 256) {
-      const int nn = n0 + u / np, i = u % np;
-      if (nn >= a.n_tokens) continue;
-      const uint16_t* qr = Q + ((size_t)nn * H + h) * dq + dn;
-      const float x0 = bf16_to_f32(qr[2 * i]), x1 = bf16_to_f32(qr[2 * i + 1]);
-      float c, s;
-      rope_cs(a.positions[nn], i, a.d_r, a.rope_base, c, s);
-      uint16_t* o = out + ((size_t)nn * H + h) * R + dc;
-      o[2 * i] = f32_to_bf16(x0 * c - x1 * s);
-      o[2 * i + 1] = f32_to_bf16(x0 * s + x1 * c);
+    for (int u0 = 0; u0 < AB_T * np; u0 += 8 * 256) {
+      float x0[8], x1[8];
+      int ps[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int u = u0 + 256 * k + tid;
+        const int nn = n0 + u / np, i = u % np;
+        const bool ok = u < AB_T * np && nn < a.n_tokens;
+        const uint16_t* qr = Q + ((size_t)(ok ? nn : 0) * H + h) * dq + dn;
+        const uint32_t pr = ok ? *(const uint32_t*)(qr + 2 * i) : 0u;
+        x0[k] = __uint_as_float(pr << 16);
+        x1[k] = __uint_as_float(pr & 0xffff0000u);
+        ps[k] = ok ? a.positions[nn] : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int u = u0 + 256 * k + tid;
+        const int nn = n0 + u / np, i = u % np;
+        if (u >= AB_T * np || nn >= a.n_tokens) continue;
+        float c, s;
+        rope_cs(ps[k], i, a.d_r, a.rope_base, c, s);
+        const uint32_t o = (uint32_t)f32_to_bf16(x0[k] * c - x1[k] * s) |
+                           ((uint32_t)f32_to_bf16(x0[k] * s + x1[k] * c) << 16);
+        *(uint32_t*)(out + ((size_t)nn * H + h) * R + dc + 2 * i) = o;
+      }
     }
   }
 }
 
 }  // namespace
 
-bool write_mfma_supported(int D, int d_c, int d_r) { return D % 32 == 0 && d_c % 16 == 0 && d_r % 16 == 0; }
+bool write_mfma_supported(int D, int d_c, int d_r) { return D % 64 == 0 && d_c % 16 == 0 && d_r % 16 == 0; }
 
 hipError_t write_cache_mfma(const WriteCacheArgs& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
   const int R = a.d_c + a.d_r;
-  // few tokens (decode): W_DKR dominates the bytes, so 16 waves per work-group
-  // split the hidden axis and keep many loads in flight; many tokens: 4 token
-  // blocks per work-group reuse each W fragment 4 times
+  // few tokens (decode): W_DKR dominates the bytes, so 8 waves per work-group
+  // split the hidden axis; many tokens: 4 token blocks per work-group reuse
+  // each W fragment 4 times
   if (a.n_tokens <= 1024) {
-    hipLaunchKernelGGL((k_write_mfma<1, 16>), dim3(R / 16, (a.n_tokens + 15) / 16), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL((k_write_mfma<1, 8, 2>), dim3(R / 16, (a.n_tokens + 15) / 16), dim3(512), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_write_mfma<4, 4>), dim3(R / 16, (a.n_tokens + 63) / 64), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_write_mfma<4, 4, 2>), dim3(R / 16, (a.n_tokens + 63) / 64), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
 
 bool absorb_mfma_supported(int H, int d_n, int d_c, int d_r) {
-  return d_n % 16 == 0 && d_n <= 256 && d_c % AB_C == 0 && d_r % 2 == 0 && H >= 1;
+  return d_n % 64 == 0 && d_n <= 128 && d_c % AB_C == 0 && d_r % 8 == 0 && H >= 1;
 }
 
 hipError_t absorb_mfma(const AbsorbArgs& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
   const dim3 grid(a.H, a.d_c / AB_C, (a.n_tokens + AB_T - 1) / AB_T);
-  hipLaunchKernelGGL(k_absorb_mfma, grid, dim3(256), (size_t)a.d_n * 256, s, a);
+  const size_t lds = (size_t)a.d_n * 256 + (size_t)AB_T * 2 * a.d_n + (size_t)AB_T * 256;
+  hipLaunchKernelGGL(k_absorb_mfma<8>, grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

@@ -57,7 +57,8 @@ bool decode_fast(const mla_dims_t* d, int batch) {
 
 struct DecodeLayout {
   int slots, max_items;
-  size_t acc_bytes, ml_bytes;
+  size_t acc_bytes, ml_bytes, plan_bytes;
+  size_t total() const { return acc_bytes + ml_bytes + plan_bytes; }
 };
 
 // Returns false when the device cannot be queried.  Items per call are at
@@ -72,6 +73,8 @@ bool decode_layout(const mla_dims_t* d, int batch, int max_seq_len, DecodeLayout
   L.acc_bytes = (size_t)L.max_items * d->num_heads * d->d_c * sizeof(float);
   L.acc_bytes = (L.acc_bytes + 255) & ~(size_t)255;
   L.ml_bytes = (size_t)L.max_items * d->num_heads * 2 * sizeof(float);
+  L.ml_bytes = (L.ml_bytes + 255) & ~(size_t)255;
+  L.plan_bytes = (size_t)(2 * batch + 2) * sizeof(int);
   return true;
 }
 
@@ -149,7 +152,7 @@ size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t 
   if (check_dims(dims) != MLA_OK || batch < 0 || batch > kMaxDecodeBatch || max_seq_len < 0) return 0;
   DecodeLayout L;
   if (!decode_layout(dims, batch, max_seq_len, L)) return 0;
-  return L.acc_bytes + L.ml_bytes;
+  return L.total();
 }
 
 int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int32_t num_pages,
@@ -165,7 +168,7 @@ int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int3
   if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * dims->page_size) return MLA_ERR_CAPACITY;
   DecodeLayout L;
   if (!decode_layout(dims, batch, max_seq_len, L)) return MLA_ERR_HIP;
-  if (workspace_bytes < L.acc_bytes + L.ml_bytes) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < L.total()) return MLA_ERR_WORKSPACE;
   DecodeArgs a;
   memset(&a, 0, sizeof a);
   a.q_abs = q_abs;
@@ -177,6 +180,7 @@ int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int3
   a.lse = lse;
   a.part_acc = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + L.acc_bytes);
+  a.plan = (int*)((char*)workspace + L.acc_bytes + L.ml_bytes);
   a.batch = batch;
   a.H = dims->num_heads;
   a.d_c = dims->d_c;
@@ -192,7 +196,8 @@ int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int3
   a.ovh_tokens = (int)((2.0 * dims->num_heads * (dims->d_c + 2) * 4.0) /
                        ((double)(dims->d_c + dims->d_r) * elem_bytes(dims->dtype)));
   a.scale_log2 = dims->softmax_scale * kLog2e;
-  if (decode_fast(dims, batch)) return launched(decode_mfma(a, stream));
+  // the MFMA path addresses partials with 32-bit offsets
+  if (decode_fast(dims, batch) && L.acc_bytes < ((size_t)1 << 32)) return launched(decode_mfma(a, stream));
   return launched(decode_generic(a, dims->dtype == MLA_BF16, stream));
 }
 

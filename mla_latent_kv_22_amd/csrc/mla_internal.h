@@ -45,7 +45,8 @@ struct DecodeArgs {
   void* out;
   float* lse;
   float* part_acc;  // [max_items, H, d_c]
-  float* part_ml;   // [max_items, H, 2]  (running max in log2 units, sum)
+  float* part_ml;   // [max_items, H, 2]  (reference max in log2 units, sum)
+  int* plan;        // [2 batch + 2]: first item per sequence (batch + 1), lengths, chunk
   int batch, H, d_c, d_r, d_v, P, max_pages_per_seq;
   int len_cap;      // lengths are clamped to min(max_seq_len, block-table capacity)
   int slots;        // concurrent work-groups the split kernel can hold
