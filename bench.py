@@ -48,7 +48,7 @@ def _traffic(n_steps_note=""):
     return t.get("bytes_per_decode_call")
 
 
-def cpu_baseline(cfg, inp, budget_s=15.0):
+def cpu_baseline(cfg, inp, budget_s=20.0):
     """Time the float64 oracle on a bounded sample of the same workload: whole
     sequences over all heads (the oracle's cost is linear in both), as many as
     fit in about budget_s seconds after timing the first one."""
