@@ -45,10 +45,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // bit 1 so that rows r and r + 8 also differ.
 __device__ __forceinline__ int swz(int r) { return (((r & 3) << 1) | ((r >> 2) & 1)) ^ ((r >> 2) & 2); }
 
-__device__ __forceinline__ constexpr int waitcnt_vm(int n) {
-  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
-  return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
-}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -86,20 +82,7 @@ __device__ __forceinline__ uint32_t load_lane_off(int lane, int rb) {
   return (uint32_t)(r * (RW * 2) + (((lane & 7) ^ swz(r)) << 4));
 }
 
-__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
 
-template <int COL>
-__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1 offset:%3"
-      :
-      : "v"(voff), "s"(sbase), "s"(lds_addr), "i"(COL)
-      : "memory", "m0");
-}
 
 template <int NW, int I0>
 __device__ __forceinline__ void issue_full(const char* tile_base, uint32_t lds0, int w, const uint32_t* lane_off) {

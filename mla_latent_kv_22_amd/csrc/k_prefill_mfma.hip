@@ -1,0 +1,384 @@
+// MFMA kernels of the causal prefill (gfx950, bf16; d_n = d_v = 128, d_R = 64).
+//
+// Prefill is compute-bound, so it takes the non-absorbed order: the per-head
+// keys and values are decompressed from the latent once (yapayzekasozluk.tr
+// "Multi-head Latent Attention (MLA) Nedir?", section "MLA nasil calisir?":
+// K and V are rebuilt from c_KV), and attention then runs over 192-wide keys
+// [K_C | k_R] and 128-wide values, 2 (192 + 128) flops per (query, key, head)
+// instead of 2 (576 + 512) in the absorbed order.
+//
+// 1. k_prefill_proj: K_C[h][n] = W_UK,h c_n and V[h][n] = W_UV,h c_n for every
+//    token, a GEMM [tokens x d_c] x [d_c x 128] per head (32x32x16 MFMA).
+//    Latent rows come from the paged pool; outputs go to the workspace as
+//    bf16, head-major ([H][tokens][128]) so that one head's keys of one
+//    sequence are contiguous.
+// 2. k_prefill_attn_mfma: causal flash attention per (sequence, head,
+//    128-query block).  Each wave owns 32 queries.  Scores are computed
+//    transposed, S^T = K Q^T, so that a lane holds all its scores for one
+//    query: the softmax numerators then feed the P.V MFMA straight from
+//    registers as its B operand, and the V^T operand comes from LDS transpose
+//    reads in the matching key order.  Key tiles of 32 keys (K_C, k_R, V)
+//    stream HBM -> LDS by DMA through a 4-stage ring.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// Direct-to-LDS load from a 64-bit per-lane address (rows gathered through
+// the block table can lie anywhere in a pool larger than 4 GiB).
+__device__ __forceinline__ void dma16_v(const void* p, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(p), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ int seq_of(const int32_t* __restrict__ cu, int num_seqs, int n) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= n) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+constexpr int PD = 128;  // d_n = d_v
+constexpr int PDR = 64;  // d_R
+
+// ---------------------------------------------------------------- up-projection
+constexpr int XT = 128;                     // tokens per work-group
+constexpr int XK = 64;                      // latent columns per k-chunk (128-byte rows)
+constexpr int XSTAGE = (XT + PD) * XK * 2;  // 32 KiB: 128 latent rows, then 128 weight rows
+
+// LDS stage row r (128 bytes): 16-byte chunk c at slot c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int xslot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__global__ void __launch_bounds__(256, 2) k_prefill_proj(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * XSTAGE];
+  const int n0 = blockIdx.x * XT, h = blockIdx.y, which = blockIdx.z;  // 0: K_C, 1: V
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r32 = lane & 31;
+  const int N = a.total, R = a.d_c + a.d_r;
+  const char* __restrict__ Wh = (const char*)(which ? a.w_uv : a.w_uk) + (size_t)h * PD * a.d_c * 2;
+  const uint32_t lds0 = lds_addr_of(smem);
+
+  // loads: instruction k (0..31) of a stage fills LDS bytes [1024 k, +1024):
+  // rows 8 (k % 16) + lane / 8 of the latent block (k < 16) or of the weight
+  // block (k >= 16), slot lane % 8.  Wave w issues k = w + 4 i.
+  const char* crow[4];
+  uint32_t cchunk[4], woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * ((w + 4 * i) & 15) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int n = min(n0 + r, N - 1);
+    const int s = seq_of(a.cu_seqlens, a.num_seqs, n);
+    const int t = n - a.cu_seqlens[s];
+    const int page = a.block_table[(size_t)s * a.max_pages_per_seq + t / a.P];
+    crow[i] = (const char*)a.pool + ((size_t)page * a.P + t % a.P) * (size_t)R * 2;
+    cchunk[i] = 16u * c;
+    woff[i] = (uint32_t)(r * a.d_c * 2 + 16 * c);
+  }
+  auto issue = [&](int kc, int st) {
+    const uint32_t base = lds0 + st * XSTAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16_v(crow[i] + 128 * kc + cchunk[i], base + 1024 * (w + 4 * i));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16<0>(Wh + 128 * kc, woff[i], base + 1024 * (16 + w + 4 * i));
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
+  const int nk = a.d_c / XK;
+  issue(0, 0);
+  for (int kc = 0; kc < nk; ++kc) {
+    if (kc + 1 < nk) {
+      issue(kc + 1, (kc + 1) & 1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* st = smem + (kc & 1) * XSTAGE;
+    const int ra = 32 * w + r32;  // A row: token
+#pragma unroll
+    for (int ks = 0; ks < XK / 16; ++ks) {
+      const int c = 2 * ks + g;
+      const u32x4 av = *(const u32x4*)(st + ra * 128 + 16 * xslot(ra, c));
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int rb = 32 * jt + r32;  // B column: output j (weight row)
+        const u32x4 bv = *(const u32x4*)(st + XT * 128 + rb * 128 + 16 * xslot(rb, c));
+        acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), acc[jt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the stage is free for the load two chunks on
+  }
+
+  // D[token][j]: lane holds j = 32 jt + lane % 32, tokens 32 w + 8 (e/4) + 4 g + e % 4.
+  // Staged as bf16 [token][128], 16-byte slot (j / 8) ^ (token % 16), then
+  // written in whole 256-byte rows.
+  uint16_t* ot = (uint16_t*)smem;
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int tk = 32 * w + 8 * (e >> 2) + 4 * g + (e & 3);
+      const int j = 32 * jt + r32;
+      ot[tk * PD + 8 * ((j >> 3) ^ (tk & 15)) + (j & 7)] = f32_to_bf16(acc[jt][e]);
+    }
+  __syncthreads();
+  uint16_t* dst = (uint16_t*)(which ? a.ws_v : a.ws_k) + ((size_t)h * N + n0) * PD;
+#pragma unroll
+  for (int i = 0; i < XT * 16 / 256; ++i) {
+    const int u = i * 256 + tid, tk = u >> 4, c = u & 15;
+    if (n0 + tk < N) *(u32x4*)(dst + (size_t)tk * PD + 8 * c) = *(const u32x4*)(ot + tk * PD + 8 * (c ^ (tk & 15)));
+  }
+}
+
+// ---------------------------------------------------------------- attention
+constexpr int AQ = 128;  // queries per work-group (4 waves x 32)
+constexpr int AK = 32;   // keys per tile
+constexpr int ST_KC = 0;                   // K_C tile: 32 rows x 256 bytes, slot c ^ (r % 16)
+constexpr int ST_KR = AK * PD * 2;         // k_R tile: 32 rows x 128 bytes, slot c ^ ((r >> 1) % 8)
+constexpr int ST_V = ST_KR + AK * PDR * 2;  // V tile: 32 rows x 256 bytes, slot c ^ 2 (r % 4)
+constexpr int ST_BYTES = ST_V + AK * PD * 2;  // 20480
+constexpr int NST = 4;
+constexpr int LPT = 5;  // loads per wave per tile (20 wave-wide loads)
+
+__global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int nqb) {
+  __shared__ __attribute__((aligned(16))) char smem[NST * ST_BYTES];
+  // work item: (sequence, head) pair and query block; the query blocks of one
+  // pair run on one XCD (work-group i runs on XCD i % 8), heaviest first
+  const int id = blockIdx.x;
+  const int pairs = a.num_seqs * a.H;
+  int pair, qr;
+  if ((pairs & 7) == 0) {
+    const int slot = id >> 3;
+    pair = (slot / nqb) * 8 + (id & 7);
+    qr = slot % nqb;
+  } else {
+    pair = id / nqb;
+    qr = id % nqb;
+  }
+  const int qb = nqb - 1 - qr;
+  const int s = pair / a.H, h = pair % a.H;
+  const int cu0 = a.cu_seqlens[s], len = a.cu_seqlens[s + 1] - cu0;
+  const int q0 = qb * AQ;
+  if (q0 >= len) return;
+  const int qend = min(len, q0 + AQ);
+  const int n_kt = (qend + AK - 1) / AK;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r32 = lane & 31;
+  const int N = a.total, R = a.d_c + a.d_r;
+  const int qi = q0 + 32 * w + r32;  // this lane's query (position in its sequence)
+  const bool qvalid = qi < qend;
+  const int w_last = min(qend - 1, q0 + 32 * w + 31);
+  const int kt_last = q0 + 32 * w < qend ? w_last / AK : -1;  // last tile this wave computes
+
+  // query fragments (B operand of S^T = K Q^T): query = lane % 32,
+  // k = 16 ks + 8 g .. +7; ks < 8: q_C, ks >= 8: RoPE(q_R, qi) rounded to bf16
+  u32x4 qf[12];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(cu0 + (qvalid ? qi : q0)) * a.H + h) * (PD + PDR) + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks);
+#pragma unroll
+    for (int ks = 8; ks < 12; ++ks) {
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pr = qf[ks][e];
+        const float x0 = __uint_as_float(pr << 16), x1 = __uint_as_float(pr & 0xffff0000u);
+        float c, sn;
+        rope_cs(qi, (16 * (ks - 8) + 8 * g) / 2 + e, PDR, a.rope_base, c, sn);
+        o[e] = pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
+      }
+      qf[ks] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  }
+
+  // tile loads: wave w issues loads u = w + 4 i (i < 5) of the 20:
+  // u < 8 K_C rows 4 u .. +3; u < 12 k_R rows 8 (u - 8) .. +7; else V rows 4 (u - 12) .. +3.
+  // Rows past the sequence end repeat its last key (masked in the scores).
+  const char* __restrict__ kc_base = (const char*)a.ws_k + ((size_t)h * N + cu0) * (PD * 2);
+  const char* __restrict__ v_base = (const char*)a.ws_v + ((size_t)h * N + cu0) * (PD * 2);
+  const int32_t* __restrict__ bt = a.block_table + (size_t)s * a.max_pages_per_seq;
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto issue = [&](int kt) {
+    const int key0 = kt * AK;
+    const int maxr = len - 1 - key0;
+    const int page = bt[key0 / a.P];
+    const char* kr_base = (const char*)a.pool + ((size_t)page * a.P + key0 % a.P) * (size_t)R * 2 + a.d_c * 2;
+    const uint32_t st = lds0 + (kt & (NST - 1)) * ST_BYTES;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int u = w + 4 * i;
+      if (u < 8) {
+        const int r = 4 * u + (lane >> 4), c = (lane & 15) ^ (r & 15);
+        dma16<0>(kc_base + (size_t)key0 * (PD * 2), (uint32_t)(min(r, maxr) * (PD * 2) + 16 * c),
+                 st + ST_KC + 1024 * u);
+      } else if (u < 12) {
+        const int r = 8 * (u - 8) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+        dma16<0>(kr_base, (uint32_t)(min(r, maxr) * R * 2 + 16 * c), st + ST_KR + 1024 * (u - 8));
+      } else {
+        const int r = 4 * (u - 12) + (lane >> 4), c = (lane & 15) ^ (2 * (r & 3));
+        dma16<0>(v_base + (size_t)key0 * (PD * 2), (uint32_t)(min(r, maxr) * (PD * 2) + 16 * c),
+                 st + ST_V + 1024 * (u - 12));
+      }
+    }
+  };
+
+  // V^T fragment offsets (A operand of O^T += V^T P^T): lane (d = lane % 32, g)
+  // needs keys 4 g + 0..3 (lo) and 8 + 4 g + 0..3 (hi) of each 16-key half;
+  // the transpose read of a 16-lane group takes 4 rows x 32 bytes.
+  const int grp = lane >> 4, jl = lane & 15;
+  const int trow = 4 * g + (jl >> 2);          // + 16 kk (+ 8 for hi); trow % 4 = jl >> 2
+  const int tch = 2 * (grp & 1) + ((jl & 3) >> 1);  // + 4 dt
+  int voff[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) voff[hf] = ST_V + (trow + 8 * hf) * 256 + 8 * (jl & 1);
+  const int vsw = 2 * (jl >> 2);  // slot swizzle of these rows
+
+  const float sl2 = a.scale * kLog2e;
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+    if (t < n_kt) issue(t);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int ahead = min(2, n_kt - 1 - kt);
+    if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();  // tile kt in LDS; tile kt-1's stage no longer read
+    asm volatile("" ::: "memory");
+    if (kt + 3 < n_kt) issue(kt + 3);
+    if (kt > kt_last) continue;
+    const char* st = smem + (kt & (NST - 1)) * ST_BYTES;
+
+    // S^T[key][query], key = lane-row of A: 8 steps over K_C, 4 over k_R
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int c = 2 * ks + g;
+      const u32x4 kv = *(const u32x4*)(st + ST_KC + r32 * 256 + 16 * (c ^ (r32 & 15)));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qf[ks]), sc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = 2 * ks + g;
+      const u32x4 kv = *(const u32x4*)(st + ST_KR + r32 * 128 + 16 * (c ^ ((r32 >> 1) & 7)));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qf[8 + ks]), sc, 0, 0, 0);
+    }
+    // sc[j]: key kt*32 + 8 (j/4) + 4 g + j % 4 against query qi; causal mask
+    const int key0 = kt * AK;
+    const bool full = key0 + AK - 1 <= q0 + 32 * w && key0 + AK <= len;  // no masking in this wave's tile
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = key0 + 8 * (j >> 2) + 4 * g + (j & 3);
+      float v = sc[j] * sl2;
+      if (!full && (key > qi || key >= len)) v = -INFINITY;
+      sc[j] = v;
+      mt = fmaxf(mt, v);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 while m = -inf
+    u32x4 pk[2];
+    float ls = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint32_t wd[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t pp = pack_bf16x2(__builtin_amdgcn_exp2f(sc[8 * kk + e] - mn),
+                                        __builtin_amdgcn_exp2f(sc[8 * kk + e + 1] - mn));
+        ls += __uint_as_float(pp << 16) + __uint_as_float(pp & 0xffff0000u);
+        wd[e >> 1] = pp;
+      }
+      pk[kk] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+    }
+    l = l * alpha + ls;
+    m = mn;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+    }
+    // O^T[d][query] += V^T[d][keys] P^T[keys][query]
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int sl = (4 * dt + tch) ^ vsw;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + voff[0] + 16 * kk * 256 + 16 * sl));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + voff[1] + 16 * kk * 256 + 16 * sl));
+        const s16x8 av = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), as_bf16x8(pk[kk]), acc[dt], 0, 0, 0);
+      }
+  }
+
+  // out[query][h][d] = O^T[d][query] / l: staged as bf16 rows [query][128]
+  // (16-byte slot (d / 8) ^ (query % 16)), then written in whole rows
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qvalid && g == 0 && a.lse) a.lse[(size_t)(cu0 + qi) * a.H + h] = (m + log2f(lt)) * kLn2;
+  __syncthreads();  // every wave is done with the tile stages
+  uint16_t* ot = (uint16_t*)smem;
+  const int ql = 32 * w + r32;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      // rows d and d+1 of one lane are e and e + 1 (same 8-aligned group)
+      const int d = 32 * dt + 8 * (e >> 2) + 4 * g + (e & 3);
+      *(uint32_t*)(ot + ql * PD + 8 * ((d >> 3) ^ (ql & 15)) + (d & 7)) =
+          pack_bf16x2(acc[dt][e] * inv, acc[dt][e + 1] * inv);
+    }
+  __syncthreads();
+  uint16_t* out = (uint16_t*)a.out;
+#pragma unroll
+  for (int i = 0; i < AQ * 16 / 256; ++i) {
+    const int u = i * 256 + tid, qq = u >> 4, c = u & 15;
+    if (q0 + qq < qend)
+      *(u32x4*)(out + ((size_t)(cu0 + q0 + qq) * a.H + h) * PD + 8 * c) = *(const u32x4*)(ot + qq * PD + 8 * (c ^ (qq & 15)));
+  }
+}
+
+}  // namespace
+
+bool prefill_mfma_supported(int d_n, int d_v, int d_r, int d_c, int P) {
+  return d_n == PD && d_v == PD && d_r == PDR && d_c % XK == 0 && d_c >= XK && P % AK == 0;
+}
+
+hipError_t prefill_mfma(const PrefillArgs& a, hipStream_t s) {
+  if (a.total == 0 || a.num_seqs == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prefill_proj, dim3((a.total + XT - 1) / XT, a.H, 2), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqb = (a.max_seq_len + AQ - 1) / AQ;
+  if (nqb == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prefill_attn_mfma, dim3(a.num_seqs * a.H * nqb), dim3(256), 0, s, a, nqb);
+  return hipGetLastError();
+}
+
+}  // namespace mla

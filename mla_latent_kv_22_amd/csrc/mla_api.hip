@@ -50,6 +50,10 @@ bool absorb_fast(const mla_dims_t* d) {
   return bf16_fast(d) && absorb_mfma_supported(d->num_heads, d->qk_nope, d->d_c, d->d_r);
 }
 
+bool prefill_fast(const mla_dims_t* d) {
+  return bf16_fast(d) && prefill_mfma_supported(d->qk_nope, d->v_head, d->d_r, d->d_c, d->page_size);
+}
+
 bool decode_fast(const mla_dims_t* d, int batch) {
   return d->dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC) &&
          decode_mfma_supported(d->num_heads, d->d_c, d->d_r, d->v_head, d->page_size, batch);
@@ -116,7 +120,7 @@ int mla_uses_fast_path(const mla_dims_t* dims, int32_t op) {
     case 0: return write_fast(dims) ? 1 : 0;
     case 1: return absorb_fast(dims) ? 1 : 0;
     case 2: return decode_fast(dims, 1) ? 1 : 0;
-    case 3: return 0;
+    case 3: return prefill_fast(dims) ? 1 : 0;
     default: return MLA_ERR_ARG;
   }
 }
@@ -245,6 +249,7 @@ int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t
   a.max_pages_per_seq = max_pages_per_seq;
   a.rope_base = dims->rope_base;
   a.scale = dims->softmax_scale;
+  if (prefill_fast(dims)) return launched(prefill_mfma(a, stream));
   return launched(prefill_generic(a, dims->dtype == MLA_BF16, stream));
 }
 

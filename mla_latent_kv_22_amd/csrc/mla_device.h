@@ -33,6 +33,38 @@ __device__ __forceinline__ float ld(const uint16_t* p, size_t i) { return bf16_t
 __device__ __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 
+
+// ---------------------------------------------------------------- LDS DMA
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt_hi[15:14]; the other counters left at their maximum).
+__device__ __forceinline__ constexpr int waitcnt_vm(int n) {
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One wave-wide direct-to-LDS load: lane l copies 16 bytes from
+// sbase + voff(l) to LDS byte M0 + 16 l (M0 = lds_addr).  Written as inline
+// asm so that the compiler adds no wait of its own before later LDS reads;
+// callers wait with s_waitcnt vmcnt for exactly the loads they need.  The
+// instruction writes no VGPR.  (The immediate offset of the instruction
+// would move the LDS destination as well, so column offsets go into sbase.)
+template <int COL>
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1 offset:%3"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_addr), "i"(COL)
+      : "memory", "m0");
+}
+
 // ---------------------------------------------------------------- RoPE
 // Rotation of pair i of a d-wide vector at position pos: angle pos * base^(-2i/d).
 // The angle and its sine/cosine are taken in double so that large positions

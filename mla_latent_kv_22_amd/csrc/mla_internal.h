@@ -64,8 +64,8 @@ struct PrefillArgs {
   const void* w_uv;
   void* out;
   float* lse;
-  void* ws_k;  // up-projected K_C  [total, H, d_n]
-  void* ws_v;  // up-projected V    [total, H, d_v]
+  void* ws_k;  // up-projected K_C: fp32 [total, H, d_n] (generic) or bf16 [H, total, d_n] (MFMA)
+  void* ws_v;  // up-projected V:   fp32 [total, H, d_v] (generic) or bf16 [H, total, d_v] (MFMA)
   int num_seqs, total, max_seq_len, H, d_n, d_r, d_c, d_v, P, max_pages_per_seq;
   float rope_base, scale;
 };
@@ -86,5 +86,8 @@ hipError_t absorb_mfma(const AbsorbArgs& a, hipStream_t s);
 bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch);
 int decode_mfma_slots(int H, int cus);
 hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s);
+// MFMA prefill: d_n = d_v = 128, d_R = 64, bf16; workspace K_C and V as bf16 [H][total][128]
+bool prefill_mfma_supported(int d_n, int d_v, int d_r, int d_c, int P);
+hipError_t prefill_mfma(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace mla

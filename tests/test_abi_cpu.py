@@ -61,6 +61,9 @@ def test_fast_path_selection():
     assert mla.uses_fast_path(_dims(dtype="f32"), mla.OP_DECODE) == 0
     assert mla.uses_fast_path(_dims(d_c=64, d_r=16), mla.OP_DECODE) == 0
     assert mla.uses_fast_path(_dims(num_heads=256), mla.OP_DECODE) == 0
+    assert mla.uses_fast_path(_dims(), mla.OP_PREFILL) == 1
+    assert mla.uses_fast_path(_dims(dtype="f32"), mla.OP_PREFILL) == 0
+    assert mla.uses_fast_path(_dims(qk_nope=64), mla.OP_PREFILL) == 0
     assert mla.uses_fast_path(_dims(), 9) == -7
 
 
