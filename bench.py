@@ -74,6 +74,53 @@ def cpu_baseline(cfg, inp, budget_s=20.0):
                       f"bytes / oracle seconds"}
 
 
+def prefill_flops(cfg, lens):
+    """Useful flops of the non-absorbed causal prefill: 2 (d_n + d_R + d_v) per
+    (query, visible key, head), plus the K_C / V up-projection 2 d_c (d_n + d_v)
+    per (token, head)."""
+    pairs = sum(int(L) * (int(L) + 1) // 2 for L in lens)
+    toks = sum(int(L) for L in lens)
+    attn = 2.0 * (cfg.qk_nope + cfg.d_r + cfg.v_head) * cfg.num_heads * pairs
+    proj = 2.0 * cfg.d_c * (cfg.qk_nope + cfg.v_head) * cfg.num_heads * toks
+    return attn, proj
+
+
+def prefill_leg(steps=5):
+    """Cache write of every token + causal prefill at the v3_prefill workload."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_22_amd import harness, inputs as I
+    cfg = I.PREFILL
+    print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
+    inp = I.make(cfg, 0)
+    pf = harness.Prefill(cfg, inp)
+    stream = torch.cuda.current_stream()
+    pf.write()
+    pf.attend()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    w_ms = timed(pf.write)
+    a_ms = timed(pf.attend)
+    attn, proj = prefill_flops(cfg, inp["seq_lens"])
+    tf = (attn + proj) / (a_ms * 1e-3) / 1e12
+    wflops = 2.0 * cfg.row_width * cfg.hidden * float(np.sum(inp["seq_lens"]))
+    return {"workload": f"{cfg.name}: {cfg.batch} x {cfg.seq_len} tokens, H={cfg.num_heads}, d_n=d_v={cfg.qk_nope}, "
+                        f"d_R={cfg.d_r}, d_c={cfg.d_c}, D={cfg.hidden}, bf16, page={cfg.page_size}",
+            "prefill_ms": round(a_ms, 4), "useful_tflop": round((attn + proj) / 1e12, 4),
+            "tflops": round(tf, 1), "mfma_frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+            "write_cache_ms": round(w_ms, 4),
+            "write_cache_tflops": round(wflops / (w_ms * 1e-3) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,6 +128,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="v3_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); multi-GPU runs are not part of this "
@@ -94,7 +142,10 @@ def main():
     mla.lib()
     cfg = I.CONFIGS[args.workload]
     if cfg.prefill:
-        raise SystemExit("use the decode workloads here; prefill is timed in the prefill block")
+        # prefill only (profiling runs): one JSON line for the prefill leg
+        print(json.dumps({"metric": "MLA causal prefill useful TFLOP/s", "n_gpus": 1, **prefill_leg(args.steps)}),
+              flush=True)
+        return
     print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = I.make(cfg, 0)
     st = harness.DecodeStep(cfg, inp)
@@ -172,6 +223,8 @@ def main():
                      "mfma_frac_of_bf16_peak": round(flops / (dec_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "wall_s_timed": round(wall, 3),
     }
+    if not args.no_prefill:
+        res["prefill"] = prefill_leg()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, inp)
