@@ -11,9 +11,10 @@
 // transpose read (ds_read_b64_tr_b16), so no transposed copy is staged.  Each
 // item fixes its per-head reference maximum on its first tile and never
 // rescales the accumulator (the merge stays exact: every partial carries its
-// own reference); a score more than 2^64 above the reference would overflow,
-// so such an (item, head) is flagged and recomputed exactly by the combine.
-// Pass 2 (combine): per (head, 32 sequences): LSE-merge of the items in a
+// own reference); a score more than 2^100 above the reference could overflow,
+// so such an (item, head) -- detected from its sum of numerators -- is
+// flagged and recomputed exactly by the combine.
+// Pass 2 (combine): per (head, 16 sequences): LSE-merge of the items in a
 // fixed order, the merged latent split into bf16 hi + lo parts, and W_UV
 // applied with MFMA (so the fp32 latent reaches the product intact to ~2^-17).
 #include "mla_device.h"
@@ -31,7 +32,7 @@ constexpr int TILE_BYTES = TILE_CHUNKS * 16;  // 36864
 constexpr int LOADS_PER_TILE = TILE_CHUNKS / 64;  // 36 wave-wide 16-byte loads
 constexpr int KS = RW / 16;        // 36 k-steps of the score MFMA
 constexpr int FB = DC / 32;        // 16 f-blocks of the latent accumulator
-constexpr float kHeadroom = 64.f;  // largest score above the item's reference, log2 units
+constexpr float kHeadroom = 100.f;  // largest score above the item's reference, log2 units
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -47,6 +48,7 @@ __device__ __forceinline__ int swz(int r) { return (((r & 3) << 1) | ((r >> 2) &
 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -149,7 +151,9 @@ __device__ __forceinline__ void tile_softmax(const f32x16& sacc, int tok0, int t
         if (tok0 + t + 1 >= t1) p1 = 0.f;
       }
       const uint32_t pk = pack_bf16x2(p0, p1);  // hardware round-to-nearest-even
-      lsum += __uint_as_float(pk << 16) + __uint_as_float(pk & 0xffff0000u);
+      // lsum += both rounded numerators: one bf16 dot product with (1, 1)
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                             lsum, false);
       wds[e >> 1] = pk;
     }
     *(u32x4*)(pbuf + head_off + o.p[kk]) = u32x4{wds[0], wds[1], wds[2], wds[3]};
@@ -357,7 +361,6 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < FB; ++i) acc[i] = f32x16{};
     float lsum = 0.f;
-    bool overflow = false;
 
     // tile 0: scores, reference maximum, numerators into P^T buffer 0
     if (ntiles >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW));
@@ -400,7 +403,6 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
       const char* nxt = tiles + ((it + 1) & 3) * TILE_BYTES;
       tile_step<NW, true>(sacc, nxt, qf, acc, cur, pbufs + (it & 1) * PBUF_BYTES, w, ro);
       const int tok1 = t0 + (it + 1) * TT;
-      overflow |= tile_max(sacc, tok1, t1, g) * sl2 > m_ref + kHeadroom;
       tile_softmax(sacc, tok1, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum, ro);
     }
     // latent update of the last tile (its scores were taken in the last step)
@@ -410,8 +412,13 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
                          pbufs + ((ntiles - 1) & 1) * PBUF_BYTES, w, ro);
 
     lsum += __shfl_xor(lsum, 32);
+    // a score more than kHeadroom (log2) above the item's reference makes its
+    // numerator, and so lsum, at least 2^kHeadroom (or inf / NaN past the fp32
+    // range): such a partial is flagged with m = +inf and recomputed exactly by
+    // the combine pass.  Below that bound every numerator, sum and latent
+    // product stays far inside the fp32 range.
+    const bool overflow = !(lsum < 0x1p100f);
     if (hvalid && g == 0) {
-      // +inf marks a partial the combine pass must recompute
       a.part_ml[((size_t)item * a.H + hq) * 2 + 0] = overflow ? INFINITY : m_ref;
       a.part_ml[((size_t)item * a.H + hq) * 2 + 1] = lsum;
     }

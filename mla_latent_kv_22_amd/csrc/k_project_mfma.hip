@@ -29,10 +29,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // fragments: row-scattered 16-byte fragment loads run at a fraction of the
 // coalesced rate on this part.  LDS slice row layout: 8 16-byte pieces,
 // piece p of row r at slot p ^ (r % 8) (conflict-free fragment reads).
-template <int TB4, int NWV, int KB>
+// KB chunks are loaded into registers at a time (all of a wave's chunks in
+// one round trip when KB covers them) and pass through NSL LDS slices.
+template <int TB4, int NWV, int KB, int NSL>
 __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
   constexpr int ROWS = 16 + 16 * TB4;  // W rows, then h rows
-  __shared__ __attribute__((aligned(16))) uint16_t stage[NWV][KB][ROWS * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[NWV][NSL][ROWS * 64];
   __shared__ f32x4 part[NWV][TB4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int R = a.d_c + a.d_r;
@@ -46,56 +48,73 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
   const int lrow = lane >> 3, lpc = lane & 7;  // loader: rows lrow + 8 i, 16-byte piece lpc
   const int m = lane & 15, q = lane >> 4;      // fragment: row m, k group q
 
-  // slot and position of the epilogue's token, fetched before the main loop
   long long slot[TB4];
   int pos[TB4];
-#pragma unroll
-  for (int t = 0; t < TB4; ++t) {
-    const int n = n0 + 16 * t + m;
-    const bool mine = (t % NWV) == w && n < a.n_tokens;
-    slot[t] = mine ? a.slots[n] : -1;
-    pos[t] = mine ? a.positions[n] : 0;
-  }
 
   f32x4 acc[TB4];
 #pragma unroll
   for (int t = 0; t < TB4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // 32-bit byte offsets of this lane's rows from W_DKR and from the
+  // work-group's h block
+  const char* __restrict__ Wb = (const char*)W;
+  const char* __restrict__ Hb = (const char*)H + (size_t)n0 * D * 2;
+  uint32_t roff[ROWS / 8];
+  bool rvalid[ROWS / 8];
+#pragma unroll
+  for (int i = 0; i < ROWS / 8; ++i) {
+    const int row = lrow + 8 * i;
+    if (row < 16) {
+      roff[i] = (uint32_t)((r0 + row) * D * 2 + 16 * lpc);
+      rvalid[i] = true;
+    } else {
+      roff[i] = (uint32_t)((row - 16) * D * 2 + 16 * lpc);
+      rvalid[i] = n0 + row - 16 < a.n_tokens;
+    }
+  }
   for (int c0 = cbeg; c0 < cend; c0 += KB) {
     u32x4 v[KB][ROWS / 8];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const bool ok = c0 + u < cend;
-      const int k = 64 * (c0 + u) + 8 * lpc;
+      const uint32_t kb = 128u * (uint32_t)(c0 + u);
 #pragma unroll
       for (int i = 0; i < ROWS / 8; ++i) {
         const int row = lrow + 8 * i;
-        if (row < 16) {
-          v[u][i] = ok ? *(const u32x4*)(W + (size_t)(r0 + row) * D + k) : u32x4{0, 0, 0, 0};
-        } else {
-          const int n = n0 + row - 16;
-          v[u][i] = (ok && n < a.n_tokens) ? *(const u32x4*)(H + (size_t)n * D + k) : u32x4{0, 0, 0, 0};
-        }
+        const char* base = row < 16 ? Wb : Hb;
+        v[u][i] = (ok && rvalid[i]) ? *(const u32x4*)(base + (roff[i] + kb)) : u32x4{0, 0, 0, 0};
       }
     }
+    if (c0 == cbeg) {
+      // slot and position of the epilogue's token, in flight with the first
+      // batch (unconditional loads from a clamped index; -1 marks no store)
 #pragma unroll
-    for (int u = 0; u < KB; ++u)
-#pragma unroll
-      for (int i = 0; i < ROWS / 8; ++i) {
-        const int row = lrow + 8 * i;
-        *(u32x4*)(&stage[w][u][row * 64 + 8 * (lpc ^ (row & 7))]) = v[u][i];
+      for (int t = 0; t < TB4; ++t) {
+        const int n = n0 + 16 * t + m;
+        const int nc = min(n, a.n_tokens - 1);
+        const long long sl = a.slots[nc];
+        pos[t] = a.positions[nc];
+        slot[t] = ((t % NWV) == w && n < a.n_tokens) ? sl : -1;
       }
-    // the slice is private to the wave and LDS operations of one wave complete
-    // in order, so the fragment reads below see the stores without a barrier
+    }
+    // the slices are private to the wave and LDS operations of one wave
+    // complete in order, so fragment reads see the stores before them and
+    // precede the store that reuses their slice, without a barrier
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       if (c0 + u >= cend) break;
+      uint16_t* sl_base = stage[w][u % NSL];
+#pragma unroll
+      for (int i = 0; i < ROWS / 8; ++i) {
+        const int row = lrow + 8 * i;
+        *(u32x4*)(sl_base + row * 64 + 8 * (lpc ^ (row & 7))) = v[u][i];
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int sl = (4 * kk + q) ^ (m & 7);
-        const u32x4 av = *(const u32x4*)(&stage[w][u][m * 64 + 8 * sl]);
+        const u32x4 av = *(const u32x4*)(sl_base + m * 64 + 8 * sl);
 #pragma unroll
         for (int t = 0; t < TB4; ++t) {
-          const u32x4 bv = *(const u32x4*)(&stage[w][u][(16 + 16 * t + m) * 64 + 8 * sl]);
+          const u32x4 bv = *(const u32x4*)(sl_base + (16 + 16 * t + m) * 64 + 8 * sl);
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[t], 0, 0, 0);
         }
       }
@@ -134,53 +153,83 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
 // ---------------------------------------------------------------- absorption
 constexpr int AB_C = 128;  // latent columns per work-group
 constexpr int AB_T = 64;   // tokens per work-group
+constexpr int AB_DR = 64;  // rotary width on this path
 
 // LDS: W_UK,h column block (d_n rows x 256 bytes), the q_C block (64 tokens x
 // d_n) and the output tile (64 tokens x 128 columns).  q and the output move
 // between HBM and LDS in whole rows (16 lanes x 16 bytes per 256-byte row
 // segment); the MFMA fragments are LDS reads.
-template <int KMAX>
+template <int DN>
 __global__ void __launch_bounds__(256) k_absorb_mfma(AbsorbArgs a) {
+  constexpr int KMAX = DN / 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int dn = a.d_n;
+  constexpr int dn = DN;
   char* wtile = smem;                          // dn x 256 B, chunk slot ch ^ 2 (j % 4)
   char* qtile = smem + dn * 256;               // 64 x (2 dn) B, piece p at slot p ^ (row % 8)
   char* otile = qtile + AB_T * 2 * dn;         // 64 x 256 B, piece p at slot p ^ (row % 8)
   const int h = blockIdx.x, cb = blockIdx.y, n0 = blockIdx.z * AB_T;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int H = a.H, dc = a.d_c, dq = a.d_n + a.d_r, R = a.d_c + a.d_r;
-  const int qp_row = dn / 8;  // 16-byte pieces per q_C row
+  constexpr int qp_row = DN / 8;  // 16-byte pieces per q_C row
   const uint16_t* __restrict__ wuk = (const uint16_t*)a.w_uk + (size_t)h * dn * dc + cb * AB_C;
   const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
   uint16_t* __restrict__ out = (uint16_t*)a.q_abs;
 
-  // stage W_UK block and q_C block, 8 chunks per thread in flight at a time
-  const int nw = dn * (AB_C / 8), nq = AB_T * qp_row;
-  for (int u0 = 0; u0 < nw + nq; u0 += 8 * 256) {
-    u32x4 v[8];
+  // loads, in this order: the rotary inputs (column-block-0 work-groups: 8
+  // (token, pair) units per thread), then the W_UK block and the q_C block
+  // (8 + 4 chunks per thread at d_n = 128).  vmcnt retires loads in issue
+  // order, so the rotation can run while the staging loads are in flight.  q
+  // rows past the last token are clamped and zeroed at the LDS store; no load
+  // sits behind a branch.
+  constexpr int np = AB_DR / 2;
+  static_assert(AB_T * np == 8 * 256, "one batch of rotary units");
+  uint32_t pr[8];
+  int ps[8];
+  if (cb == 0) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int u = u0 + k * 256 + tid;
-      if (u < nw) {
-        const int j = u >> 4, ch = u & 15;
-        v[k] = *(const u32x4*)(wuk + (size_t)j * dc + 8 * ch);
-      } else if (u < nw + nq) {
-        const int t = (u - nw) / qp_row, pc = (u - nw) % qp_row;
-        const int n = n0 + t;
-        v[k] = n < a.n_tokens ? *(const u32x4*)(Q + ((size_t)n * H + h) * dq + 8 * pc) : u32x4{0, 0, 0, 0};
-      }
+      const int u = 256 * k + tid;
+      const int nn = min(n0 + u / np, a.n_tokens - 1), i = u % np;
+      pr[k] = *(const uint32_t*)(Q + ((size_t)nn * H + h) * dq + dn + 2 * i);
+      ps[k] = a.positions[nn];
     }
+  }
+  constexpr int NWC = DN * (AB_C / 8) / 256, NQC = AB_T * (DN / 8) / 256;
+  static_assert(DN * (AB_C / 8) % 256 == 0 && AB_T * (DN / 8) % 256 == 0, "whole chunks per thread");
+  u32x4 wv[NWC], qv[NQC];
+#pragma unroll
+  for (int k = 0; k < NWC; ++k) {
+    const int u = k * 256 + tid, j = u >> 4, ch = u & 15;
+    wv[k] = *(const u32x4*)(wuk + (size_t)j * dc + 8 * ch);
+  }
+#pragma unroll
+  for (int k = 0; k < NQC; ++k) {
+    const int u = k * 256 + tid, t = u / qp_row, pc = u % qp_row;
+    qv[k] = *(const u32x4*)(Q + ((size_t)min(n0 + t, a.n_tokens - 1) * H + h) * dq + 8 * pc);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the rotation starts
+  if (cb == 0) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int u = u0 + k * 256 + tid;
-      if (u < nw) {
-        const int j = u >> 4, ch = u & 15;
-        *(u32x4*)(wtile + j * 256 + 16 * (ch ^ (2 * (j & 3)))) = v[k];
-      } else if (u < nw + nq) {
-        const int t = (u - nw) / qp_row, pc = (u - nw) % qp_row;
-        *(u32x4*)(qtile + t * 2 * dn + 16 * (pc ^ (t & 7))) = v[k];
-      }
+      const int u = 256 * k + tid;
+      const int nn = n0 + u / np, i = u % np;
+      if (nn >= a.n_tokens) continue;
+      float c, s;
+      rope_cs(ps[k], i, AB_DR, a.rope_base, c, s);
+      const float x0 = __uint_as_float(pr[k] << 16), x1 = __uint_as_float(pr[k] & 0xffff0000u);
+      const uint32_t o = (uint32_t)f32_to_bf16(x0 * c - x1 * s) | ((uint32_t)f32_to_bf16(x0 * s + x1 * c) << 16);
+      *(uint32_t*)(out + ((size_t)nn * H + h) * R + dc + 2 * i) = o;
     }
+  }
+#pragma unroll
+  for (int k = 0; k < NWC; ++k) {
+    const int u = k * 256 + tid, j = u >> 4, ch = u & 15;
+    *(u32x4*)(wtile + j * 256 + 16 * (ch ^ (2 * (j & 3)))) = wv[k];
+  }
+#pragma unroll
+  for (int k = 0; k < NQC; ++k) {
+    const int u = k * 256 + tid, t = u / qp_row, pc = u % qp_row;
+    *(u32x4*)(qtile + t * 2 * dn + 16 * (pc ^ (t & 7))) = (n0 + t < a.n_tokens) ? qv[k] : u32x4{0, 0, 0, 0};
   }
   __syncthreads();
 
@@ -224,36 +273,6 @@ __global__ void __launch_bounds__(256) k_absorb_mfma(AbsorbArgs a) {
       *(u32x4*)(out + ((size_t)n * H + h) * R + cb * AB_C + 8 * pc) =
           *(const u32x4*)(otile + t * 256 + 16 * (pc ^ (t & 7)));
   }
-  if (cb == 0) {
-    // rotary half: 8 (token, pair) units per thread in flight at once
-    const int np = a.d_r / 2;
-    for (int u0 = 0; u0 < AB_T * np; u0 += 8 * 256) {
-      float x0[8], x1[8];
-      int ps[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int u = u0 + 256 * k + tid;
-        const int nn = n0 + u / np, i = u % np;
-        const bool ok = u < AB_T * np && nn < a.n_tokens;
-        const uint16_t* qr = Q + ((size_t)(ok ? nn : 0) * H + h) * dq + dn;
-        const uint32_t pr = ok ? *(const uint32_t*)(qr + 2 * i) : 0u;
-        x0[k] = __uint_as_float(pr << 16);
-        x1[k] = __uint_as_float(pr & 0xffff0000u);
-        ps[k] = ok ? a.positions[nn] : 0;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int u = u0 + 256 * k + tid;
-        const int nn = n0 + u / np, i = u % np;
-        if (u >= AB_T * np || nn >= a.n_tokens) continue;
-        float c, s;
-        rope_cs(ps[k], i, a.d_r, a.rope_base, c, s);
-        const uint32_t o = (uint32_t)f32_to_bf16(x0[k] * c - x1[k] * s) |
-                           ((uint32_t)f32_to_bf16(x0[k] * s + x1[k] * c) << 16);
-        *(uint32_t*)(out + ((size_t)nn * H + h) * R + dc + 2 * i) = o;
-      }
-    }
-  }
 }
 
 }  // namespace
@@ -263,26 +282,30 @@ bool write_mfma_supported(int D, int d_c, int d_r) { return D % 64 == 0 && d_c %
 hipError_t write_cache_mfma(const WriteCacheArgs& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
   const int R = a.d_c + a.d_r;
-  // few tokens (decode): W_DKR dominates the bytes, so 8 waves per work-group
-  // split the hidden axis; many tokens: 4 token blocks per work-group reuse
-  // each W fragment 4 times
+  // few tokens (decode): W_DKR dominates the bytes, so 16 waves per work-group
+  // split the hidden axis, fetching their chunks in batches of 4 (two round
+  // trips at D = 7168); many tokens: 4 token blocks per work-group reuse each W
+  // fragment 4 times
   if (a.n_tokens <= 1024) {
-    hipLaunchKernelGGL((k_write_mfma<1, 8, 2>), dim3(R / 16, (a.n_tokens + 15) / 16), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((k_write_mfma<1, 16, 4, 2>), dim3(R / 16, (a.n_tokens + 15) / 16), dim3(1024), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_write_mfma<4, 4, 2>), dim3(R / 16, (a.n_tokens + 63) / 64), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_write_mfma<4, 4, 2, 2>), dim3(R / 16, (a.n_tokens + 63) / 64), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
 
 bool absorb_mfma_supported(int H, int d_n, int d_c, int d_r) {
-  return d_n % 64 == 0 && d_n <= 128 && d_c % AB_C == 0 && d_r % 8 == 0 && H >= 1;
+  return d_n % 64 == 0 && d_n <= 128 && d_c % AB_C == 0 && d_r == AB_DR && H >= 1;
 }
 
 hipError_t absorb_mfma(const AbsorbArgs& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
   const dim3 grid(a.H, a.d_c / AB_C, (a.n_tokens + AB_T - 1) / AB_T);
   const size_t lds = (size_t)a.d_n * 256 + (size_t)AB_T * 2 * a.d_n + (size_t)AB_T * 256;
-  hipLaunchKernelGGL(k_absorb_mfma<8>, grid, dim3(256), lds, s, a);
+  if (a.d_n == 128)
+    hipLaunchKernelGGL(k_absorb_mfma<128>, grid, dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL(k_absorb_mfma<64>, grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

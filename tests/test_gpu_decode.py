@@ -254,19 +254,23 @@ def test_decode_ragged_paged_full_size():
     _check(cfg, inp, st, seqs, heads=[0, 1, 31, 32, 63, 64, 65, 95, 96, 100, 126, 127])
 
 
-@pytest.mark.parametrize("flags", [0, mla.FLAG_GENERIC], ids=["mfma", "generic"])
-def test_decode_score_spike_far_above_first_tile(flags):
+@pytest.mark.parametrize("flags,amp", [(0, 40.0), (mla.FLAG_GENERIC, 40.0), (0, 13.0), (0, 17.0)],
+                         ids=["mfma_huge", "generic_huge", "mfma_below_bound", "mfma_above_bound"])
+def test_decode_score_spike_far_above_first_tile(flags, amp):
     """One row of sequence 1 aligned with head 0's absorbed query and scaled so
-    its score exceeds the rest of its work item by ~500 (natural log units):
-    the MFMA split pass must hand this (item, head) to the exact recompute
-    path; the output is then W_UV,0 c_spike for head 0."""
+    its score exceeds the rest of its work item by about 7 amp in log2 units:
+    amp 40 (~277) overflows the numerators and the MFMA split pass must hand
+    this (item, head) to the exact recompute path; amp 13 (~90) stays under
+    the 2^100 bound and is computed in place with huge numerators; amp 17
+    (~118) crosses it and is flagged through the numerator sum.  The output
+    for head 0 is then W_UV,0 c_spike in every case."""
     need_gpu()
-    _case(f"score spike flags={flags}")
+    _case(f"score spike flags={flags} amp={amp}")
     cfg = I.scaled(I.RAGGED, hidden=512, batch=3, seq_len=2100, min_seq_len=1)
     inp = I.make(cfg, 21, lengths=[700, 2100, 64])
     q = O.from_storage(inp["q"], "bf16")
     qa = O.absorb_query(q, O.from_storage(inp["w_uk"], "bf16"), inp["q_positions"], cfg.qk_nope, cfg.rope_base)
-    spike = np.where(qa[1, 0] >= 0, 40.0, -40.0).astype(np.float32)
+    spike = np.where(qa[1, 0] >= 0, amp, -amp).astype(np.float32)
     t_spike = 1000  # inside a work item, past its first tile
     P = cfg.page_size
     rows = inp["rows"].copy()
