@@ -335,9 +335,15 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
       return pool + ((size_t)page * P + (tok0 % P)) * (RW * 2);
     };
 
-    // absorbed query fragments (B operand of the score MFMA: head hq,
-    // k = 16 ks + 8 g .. +7), loaded before the first tiles so the tile waits
-    // below count only tile loads after them
+    // prologue: tile 0 first, so its bytes are on the way while the absorbed
+    // query fragments load (B operand of the score MFMA: head hq,
+    // k = 16 ks + 8 g .. +7), then tiles 1 and 2; the tile waits below count
+    // the loads issued after the ones they need
+    {
+      int nv;
+      const char* tp = tile_ptr(0, nv);
+      issue_tile<NW>(tp, nv, lds_tiles, w, lane, lane_off);
+    }
     u32x4 qf[KS];
     {
       const uint16_t* qp = (const uint16_t*)a.q_abs + ((size_t)b * a.H + (hvalid ? hq : 0)) * RW + 8 * g;
@@ -347,9 +353,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
         qf[ks] = hvalid ? v : u32x4{0, 0, 0, 0};
       }
     }
-    // prologue: tiles 0, 1, 2 in flight
 #pragma unroll
-    for (int st = 0; st < 3; ++st) {
+    for (int st = 1; st < 3; ++st) {
       if (st < ntiles) {
         int nv;
         const char* tp = tile_ptr(st, nv);

@@ -78,41 +78,6 @@ __device__ __forceinline__ void rope_cs(int pos, int i, int d, float base, float
   s = (float)sd;
 }
 
-// ---------------------------------------------------------------- block reductions
-__device__ __forceinline__ int block_sum_int(int v, int* red) {
-  // red: >= blockDim.x/64 ints of LDS
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  int s = 0;
-  for (int i = 0; i < nw; ++i) s += red[i];
-  return s;
-}
-
-// Exclusive prefix sum of one int per thread over the work-group.
-// red: >= blockDim.x/64 ints of LDS.  Returns the prefix, writes the total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  __syncthreads();
-  if (lane == 63) red[w] = x;
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int i = 0; i < nw; ++i) {
-    const int r = red[i];
-    if (i < w) base += r;
-    tot += r;
-  }
-  total = tot;
-  return base + x - v;
-}
-
 // ---------------------------------------------------------------- decode work split
 // The token axis of every sequence is cut into chunks of `chunk` tokens
 // (a multiple of 32); chunk k of sequence b is work item s_items[b] + k.  The
@@ -131,52 +96,69 @@ __device__ __forceinline__ int clamp_len(int len, int cap) { return len < 0 ? 0 
 // for k = 1, 2, 4, rounded up to 32 and clamped to [min_chunk, max_chunk].  The chosen one
 // minimises (rounds of `slots` items) * chunk + the partial-result overhead
 // (ovh_tokens token-equivalents per item, spread over the slots).
-// s_len, s_items: LDS, >= batch + 1 ints; red: LDS, >= 16 ints.  All threads call.
+// The first wave computes the plan with wave reductions (no barrier inside);
+// one barrier then publishes it.  s_len, s_items: LDS, >= batch + 1 ints;
+// red: LDS, >= 16 ints.  All threads call.
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 __device__ inline DecodePlan make_decode_plan(const int32_t* __restrict__ seq_lens, int batch, int cap,
                                               int slots, int min_chunk, int max_chunk, int ovh_tokens, int* s_len,
                                               int* s_items, int* red) {
-  int part = 0;
-  for (int b = threadIdx.x; b < batch; b += blockDim.x) {
-    const int L = clamp_len(seq_lens[b], cap);
-    s_len[b] = L;
-    part += L;
-  }
-  const int total = block_sum_int(part, red);  // (barriers inside publish s_len)
-  int best_chunk = 0;
-  long long best_cost = -1;
-  for (int k = 1; k <= 4; k <<= 1) {
-    const long long denom = (long long)k * slots;
-    int ch = (int)((total + denom - 1) / denom);
-    ch = ((ch + 31) / 32) * 32;
-    if (ch < min_chunk) ch = min_chunk;
-    if (ch > max_chunk) ch = max_chunk;
-    int it = 0;
-    for (int b = threadIdx.x; b < batch; b += blockDim.x) it += (s_len[b] + ch - 1) / ch;
-    it = block_sum_int(it, red);
-    const long long rounds = (it + slots - 1) / slots;
-    const long long cost = rounds * ch + ((long long)it * ovh_tokens) / slots;
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best_chunk = ch;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    long long part = 0;
+    for (int b = lane; b < batch; b += 64) {
+      const int L = clamp_len(seq_lens[b], cap);
+      s_len[b] = L;
+      part += L;
+    }
+    const long long total = wave_sum_ll(part);
+    int best_chunk = 0;
+    long long best_cost = -1;
+    for (int k = 1; k <= 4; k <<= 1) {
+      const long long denom = (long long)k * slots;
+      long long chl = (total + denom - 1) / denom;
+      chl = ((chl + 31) / 32) * 32;
+      int ch = (int)(chl < min_chunk ? min_chunk : (chl > max_chunk ? max_chunk : chl));
+      long long it = 0;
+      for (int b = lane; b < batch; b += 64) it += (s_len[b] + ch - 1) / ch;  // this lane's own entries
+      it = wave_sum_ll(it);
+      const long long rounds = (it + slots - 1) / slots;
+      const long long cost = rounds * ch + (it * ovh_tokens) / slots;
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best_chunk = ch;
+      }
+    }
+    // exclusive prefix of item counts: lane l owns the contiguous run of
+    // sequences [l per, l per + per); LDS operations of one wave complete in
+    // order, so the lengths written above are visible here
+    const int per = (batch + 63) / 64;
+    const int b0 = lane * per, b1 = min(batch, b0 + per);
+    int mine = 0;
+    for (int b = b0; b < b1; ++b) mine += (s_len[b] + best_chunk - 1) / best_chunk;
+    int x = mine;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    int pre = x - mine;
+    for (int b = b0; b < b1; ++b) {
+      s_items[b] = pre;
+      pre += (s_len[b] + best_chunk - 1) / best_chunk;
+    }
+    if (lane == 63) {
+      s_items[batch] = x;
+      red[0] = best_chunk;
     }
   }
-  // exclusive prefix of item counts: thread t owns a contiguous run of sequences
-  const int per = (batch + blockDim.x - 1) / blockDim.x;
-  const int b0 = threadIdx.x * per;
-  const int b1 = min(batch, b0 + per);
-  int mine = 0;
-  for (int b = b0; b < b1; ++b) mine += (s_len[b] + best_chunk - 1) / best_chunk;
-  int n_items = 0;
-  int pre = block_exclusive_scan(mine, red, n_items);
-  for (int b = b0; b < b1; ++b) {
-    s_items[b] = pre;
-    pre += (s_len[b] + best_chunk - 1) / best_chunk;
-  }
-  if (threadIdx.x == 0) s_items[batch] = n_items;
   __syncthreads();
   DecodePlan p;
-  p.chunk = best_chunk;
-  p.n_items = n_items;
+  p.chunk = red[0];
+  p.n_items = s_items[batch];
   return p;
 }
 
