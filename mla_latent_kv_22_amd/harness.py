@@ -69,13 +69,21 @@ class DecodeStep:
         mla.decode(self.d, self.q_abs, self.pool if pool is None else pool, self.block_table, self.seq_lens,
                    self.max_seq_len, self.w_uv, self.out, self.lse, self.workspace, stream)
 
-    def step(self, stream=None, pool=None):
-        if pool is not None:
-            mla.write_cache(self.d, self.h, self.w_dkr, self.positions, self.slots, pool, stream)
+    def step(self, stream=None, pool=None, side_stream=None):
+        """write_cache, absorb_q, decode.  With side_stream, the cache write
+        (which only touches the new rows) runs there concurrently with the
+        absorption, and decode waits for both."""
+        pool = self.pool if pool is None else pool
+        main = stream if stream is not None else torch.cuda.current_stream()
+        if side_stream is not None:
+            side_stream.wait_stream(main)
+            mla.write_cache(self.d, self.h, self.w_dkr, self.positions, self.slots, pool, side_stream)
+            self.absorb(main)
+            main.wait_stream(side_stream)
         else:
-            self.write(stream)
-        self.absorb(stream)
-        self.attend(stream, pool)
+            mla.write_cache(self.d, self.h, self.w_dkr, self.positions, self.slots, pool, main)
+            self.absorb(main)
+        self.attend(main, pool)
 
 
 class Prefill:
