@@ -19,6 +19,8 @@
 //    registers as its B operand, and the V^T operand comes from LDS transpose
 //    reads in the matching key order.  Key tiles of 32 keys (K_C, k_R, V)
 //    stream HBM -> LDS by DMA through a 4-stage ring.
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -26,6 +28,8 @@ namespace mla {
 namespace {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -159,6 +163,9 @@ constexpr int ST_V = ST_KR + AK * PDR * 2;  // V tile: 32 rows x 256 bytes, slot
 constexpr int ST_BYTES = ST_V + AK * PD * 2;  // 20480
 constexpr int NST = 4;
 constexpr int LPT = 5;  // loads per wave per tile (20 wave-wide loads)
+constexpr float kLazy = 8.f;     // log2 headroom of the softmax reference maximum
+constexpr float kMInit = -1e30f;
+constexpr bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
 
 __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int nqb) {
   __shared__ __attribute__((aligned(16))) char smem[NST * ST_BYTES];
@@ -259,12 +266,13 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  // m: reference maximum of this lane's query (log2 units).  It moves only
+  // when a tile's maximum exceeds it by more than kLazy, so numerators stay
+  // below 2^kLazy and the accumulator is rescaled on few tiles.  It starts
+  // finite so that a fully masked score never meets inf - inf.
+  float m = kMInit, l = 0.f;
 
-#pragma unroll
-  for (int t = 0; t < 3; ++t)
-    if (t < n_kt) issue(t);
-  for (int kt = 0; kt < n_kt; ++kt) {
+  auto sync = [&](int kt) {
     const int ahead = min(2, n_kt - 1 - kt);
     if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
     else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
@@ -272,38 +280,62 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
     __builtin_amdgcn_s_barrier();  // tile kt in LDS; tile kt-1's stage no longer read
     asm volatile("" ::: "memory");
     if (kt + 3 < n_kt) issue(kt + 3);
-    if (kt > kt_last) continue;
-    const char* st = smem + (kt & (NST - 1)) * ST_BYTES;
+  };
 
+  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASKED is
+  // the diagonal tile (keys past the query); every earlier tile is full.
+  auto tile = [&](int kt, auto masked) {
+    const char* st = smem + (kt & (NST - 1)) * ST_BYTES;
     // S^T[key][query], key = lane-row of A: 8 steps over K_C, 4 over k_R
+    u32x4 kf[12];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      kf[ks] = *(const u32x4*)(st + ST_KC + r32 * 256 + 16 * ((2 * ks + g) ^ (r32 & 15)));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[8 + ks] = *(const u32x4*)(st + ST_KR + r32 * 128 + 16 * ((2 * ks + g) ^ ((r32 >> 1) & 7)));
+    __builtin_amdgcn_sched_barrier(0);  // all reads in flight before the chain starts
     f32x16 sc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int c = 2 * ks + g;
-      const u32x4 kv = *(const u32x4*)(st + ST_KC + r32 * 256 + 16 * (c ^ (r32 & 15)));
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qf[ks]), sc, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 12; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[ks]), as_bf16x8(qf[ks]), sc, 0, 0, 0);
+    // V^T fragments of this tile, read while the softmax below runs
+    s16x4 vf[2][4][2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int c = 2 * ks + g;
-      const u32x4 kv = *(const u32x4*)(st + ST_KR + r32 * 128 + 16 * (c ^ ((r32 >> 1) & 7)));
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qf[8 + ks]), sc, 0, 0, 0);
-    }
-    // sc[j]: key kt*32 + 8 (j/4) + 4 g + j % 4 against query qi; causal mask
-    const int key0 = kt * AK;
-    const bool full = key0 + AK - 1 <= q0 + 32 * w && key0 + AK <= len;  // no masking in this wave's tile
-    float mt = -INFINITY;
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = key0 + 8 * (j >> 2) + 4 * g + (j & 3);
-      float v = sc[j] * sl2;
-      if (!full && (key > qi || key >= len)) v = -INFINITY;
-      sc[j] = v;
-      mt = fmaxf(mt, v);
+      for (int dt = 0; dt < 4; ++dt) {
+        const int sl = (4 * dt + tch) ^ vsw;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          vf[kk][dt][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + voff[hf] + 16 * kk * 256 + 16 * sl));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    // sc[j]: key kt*32 + 8 (j/4) + 4 g + j % 4 against query qi
+    if constexpr (decltype(masked)::value) {
+      const int rel = qi - kt * AK - 4 * g;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (8 * (j >> 2) + (j & 3) > rel) sc[j] = -INFINITY;
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 while m = -inf
+    float mt = sc[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sc[j]);
+    {
+      // lanes l and l + 32 hold the two key halves of one query
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mts = mt * sl2;  // scale > 0: the maximum commutes with it
+    if (__ballot(mts > m + kLazy)) {
+      const float mn = fmaxf(m, mts);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+      m = mn;
+    }
+    const float nm = -m;
     u32x4 pk[2];
     float ls = 0.f;
 #pragma unroll
@@ -311,31 +343,42 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
       uint32_t wd[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const uint32_t pp = pack_bf16x2(__builtin_amdgcn_exp2f(sc[8 * kk + e] - mn),
-                                        __builtin_amdgcn_exp2f(sc[8 * kk + e + 1] - mn));
-        ls += __uint_as_float(pp << 16) + __uint_as_float(pp & 0xffff0000u);
-        wd[e >> 1] = pp;
+        const f32x2 pf = {__builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * kk + e], sl2, nm)),
+                          __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * kk + e + 1], sl2, nm))};
+        const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes2, ls, false);  // the rounded numerators
+        wd[e >> 1] = __builtin_bit_cast(uint32_t, pb);
       }
       pk[kk] = u32x4{wd[0], wd[1], wd[2], wd[3]};
     }
-    l = l * alpha + ls;
-    m = mn;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
-    }
+    l += ls;
     // O^T[d][query] += V^T[d][keys] P^T[keys][query]
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int sl = (4 * dt + tch) ^ vsw;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + voff[0] + 16 * kk * 256 + 16 * sl));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + voff[1] + 16 * kk * 256 + 16 * sl));
+        const s16x4 lo = vf[kk][dt][0], hi = vf[kk][dt][1];
         const s16x8 av = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), as_bf16x8(pk[kk]), acc[dt], 0, 0, 0);
       }
+  };
+
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+    if (t < n_kt) issue(t);
+  // every wave takes part in all n_kt barriers and loads; it computes
+  // tiles 0 .. kt_last, of which only the last meets the diagonal
+  int kt = 0;
+  for (; kt < kt_last; ++kt) {
+    sync(kt);
+    tile(kt, std::false_type{});
   }
+  if (kt_last >= 0) {
+    sync(kt_last);
+    tile(kt_last, std::true_type{});
+    kt = kt_last + 1;
+  }
+  for (; kt < n_kt; ++kt) sync(kt);
 
   // out[query][h][d] = O^T[d][query] / l: staged as bf16 rows [query][128]
   // (16-byte slot (d / 8) ^ (query % 16)), then written in whole rows
