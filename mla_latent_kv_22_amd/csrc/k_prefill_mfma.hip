@@ -159,7 +159,7 @@ constexpr int AQ = 128;  // queries per work-group (4 waves x 32)
 constexpr int AK = 32;   // keys per tile
 constexpr int ST_KC = 0;                   // K_C tile: 32 rows x 256 bytes, slot c ^ (r % 16)
 constexpr int ST_KR = AK * PD * 2;         // k_R tile: 32 rows x 128 bytes, slot c ^ ((r >> 1) % 8)
-constexpr int ST_V = ST_KR + AK * PDR * 2;  // V tile: 32 rows x 256 bytes, slot c ^ 2 (r % 4)
+constexpr int ST_V = ST_KR + AK * PDR * 2;  // V tile: 32 rows x 256 bytes, slot c ^ 4 (r % 4)
 constexpr int ST_BYTES = ST_V + AK * PD * 2;  // 20480
 constexpr int NST = 4;
 constexpr int LPT = 5;  // loads per wave per tile (20 wave-wide loads)
@@ -205,6 +205,8 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
     const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(cu0 + (qvalid ? qi : q0)) * a.H + h) * (PD + PDR) + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks);
+    // lane l computes theta of pair l % 32 once; the lanes share them
+    const double th_l = rope_inv_freq(lane & 31, PDR, a.rope_base);
 #pragma unroll
     for (int ks = 8; ks < 12; ++ks) {
       uint32_t o[4];
@@ -213,7 +215,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
         const uint32_t pr = qf[ks][e];
         const float x0 = __uint_as_float(pr << 16), x1 = __uint_as_float(pr & 0xffff0000u);
         float c, sn;
-        rope_cs(qi, (16 * (ks - 8) + 8 * g) / 2 + e, PDR, a.rope_base, c, sn);
+        rope_cs_theta(qi, __shfl(th_l, (16 * (ks - 8) + 8 * g) / 2 + e), c, sn);
         o[e] = pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
       }
       qf[ks] = u32x4{o[0], o[1], o[2], o[3]};
@@ -227,10 +229,16 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   const char* __restrict__ v_base = (const char*)a.ws_v + ((size_t)h * N + cu0) * (PD * 2);
   const int32_t* __restrict__ bt = a.block_table + (size_t)s * a.max_pages_per_seq;
   const uint32_t lds0 = lds_addr_of(smem);
-  auto issue = [&](int kt) {
+  // the block-table entry of a tile is read one iteration before its loads
+  // are issued, so the scalar load never stalls the wave (P % 32 == 0: a
+  // tile lies in one page)
+  // (through the constant address space: a scalar load, counted by lgkmcnt
+  // and not by the vmcnt that tracks the tile loads)
+  const __attribute__((address_space(4))) int32_t* bt_c = (const __attribute__((address_space(4))) int32_t*)bt;
+  auto page_of = [&](int kt) { return bt_c[min(kt, n_kt - 1) * AK / a.P]; };
+  auto issue = [&](int kt, int page) {
     const int key0 = kt * AK;
     const int maxr = len - 1 - key0;
-    const int page = bt[key0 / a.P];
     const char* kr_base = (const char*)a.pool + ((size_t)page * a.P + key0 % a.P) * (size_t)R * 2 + a.d_c * 2;
     const uint32_t st = lds0 + (kt & (NST - 1)) * ST_BYTES;
 #pragma unroll
@@ -244,7 +252,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
         const int r = 8 * (u - 8) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
         dma16<0>(kr_base, (uint32_t)(min(r, maxr) * R * 2 + 16 * c), st + ST_KR + 1024 * (u - 8));
       } else {
-        const int r = 4 * (u - 12) + (lane >> 4), c = (lane & 15) ^ (2 * (r & 3));
+        const int r = 4 * (u - 12) + (lane >> 4), c = (lane & 15) ^ (4 * (r & 3));
         dma16<0>(v_base + (size_t)key0 * (PD * 2), (uint32_t)(min(r, maxr) * (PD * 2) + 16 * c),
                  st + ST_V + 1024 * (u - 12));
       }
@@ -260,7 +268,10 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   int voff[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) voff[hf] = ST_V + (trow + 8 * hf) * 256 + 8 * (jl & 1);
-  const int vsw = 2 * (jl >> 2);  // slot swizzle of these rows
+  // slot swizzle of these rows: the two 16-lane groups that share an LDS
+  // cycle read chunk pairs 4 dt + {0, 1} and 4 dt + {2, 3} of rows with
+  // r % 4 = 0..3; XOR by 4 (r % 4) spreads them over all 16 chunks (64 banks)
+  const int vsw = 4 * (jl >> 2);
 
   const float sl2 = a.scale * kLog2e;
   f32x16 acc[4];
@@ -272,6 +283,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   // finite so that a fully masked score never meets inf - inf.
   float m = kMInit, l = 0.f;
 
+  int next_page = page_of(3);
   auto sync = [&](int kt) {
     const int ahead = min(2, n_kt - 1 - kt);
     if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
@@ -279,7 +291,8 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();  // tile kt in LDS; tile kt-1's stage no longer read
     asm volatile("" ::: "memory");
-    if (kt + 3 < n_kt) issue(kt + 3);
+    if (kt + 3 < n_kt) issue(kt + 3, next_page);
+    next_page = page_of(kt + 4);
   };
 
   // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASKED is
@@ -365,7 +378,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
 
 #pragma unroll
   for (int t = 0; t < 3; ++t)
-    if (t < n_kt) issue(t);
+    if (t < n_kt) issue(t, page_of(t));
   // every wave takes part in all n_kt barriers and loads; it computes
   // tiles 0 .. kt_last, of which only the last meets the diagonal
   int kt = 0;

@@ -123,6 +123,12 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
 #pragma unroll
   for (int t = 0; t < TB4; ++t) part[w][t][lane] = acc[t];
   __syncthreads();
+  // rotary frequencies of this lane's two feature pairs (k_R rows only)
+  double th[2] = {0.0, 0.0};
+  if (r0 + 4 * (lane >> 4) >= a.d_c) {
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) th[pr] = rope_inv_freq((r0 + 4 * (lane >> 4) - a.d_c) / 2 + pr, a.d_r, a.rope_base);
+  }
   // epilogue: waves take token sub-blocks; fixed summation order over waves
 #pragma unroll
   for (int t = 0; t < TB4; ++t) {
@@ -137,7 +143,7 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         float c, s;
-        rope_cs(pos[t], (rf - a.d_c) / 2 + pr, a.d_r, a.rope_base, c, s);
+        rope_cs_theta(pos[t], th[pr], c, s);
         const float x0 = o[2 * pr], x1 = o[2 * pr + 1];
         o[2 * pr] = x0 * c - x1 * s;
         o[2 * pr + 1] = x0 * s + x1 * c;
@@ -209,13 +215,15 @@ __global__ void __launch_bounds__(256) k_absorb_mfma(AbsorbArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the rotation starts
   if (cb == 0) {
+    static_assert(256 % np == 0, "pair index fixed per thread");
+    const double th = rope_inv_freq(tid % np, AB_DR, a.rope_base);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int u = 256 * k + tid;
       const int nn = n0 + u / np, i = u % np;
       if (nn >= a.n_tokens) continue;
       float c, s;
-      rope_cs(ps[k], i, AB_DR, a.rope_base, c, s);
+      rope_cs_theta(ps[k], th, c, s);
       const float x0 = __uint_as_float(pr[k] << 16), x1 = __uint_as_float(pr[k] & 0xffff0000u);
       const uint32_t o = (uint32_t)f32_to_bf16(x0 * c - x1 * s) | ((uint32_t)f32_to_bf16(x0 * s + x1 * c) << 16);
       *(uint32_t*)(out + ((size_t)nn * H + h) * R + dc + 2 * i) = o;

@@ -66,16 +66,43 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
 }
 
 // ---------------------------------------------------------------- RoPE
-// Rotation of pair i of a d-wide vector at position pos: angle pos * base^(-2i/d).
-// The angle and its sine/cosine are taken in double so that large positions
-// (tens of thousands of radians for pair 0) keep full fp32 accuracy.
-__device__ __forceinline__ void rope_cs(int pos, int i, int d, float base, float& c, float& s) {
-  const double theta = exp(-(2.0 * (double)i / (double)d) * log((double)base));
+// Rotation of pair i of a d-wide vector at position pos: angle pos * theta_i,
+// theta_i = base^(-2i/d).
+//
+// theta_i, in double.
+__device__ __forceinline__ double rope_inv_freq(int i, int d, float base) {
+  return exp2(-(2.0 * (double)i / (double)d) * log2((double)base));
+}
+
+// cos and sin of pos * theta.  The angle is formed and reduced in double,
+// f = angle - k pi/2 with |f| <= pi/4 (pi/2 rounded to double is off by 6e-17,
+// so k pi/2 is off by k * 6e-17 rad), and sin f, cos f are then the fp32
+// Taylor series to f^9 and f^10 (the terms left out are below 2e-9 for
+// |f| <= pi/4); k mod 4 picks the quadrant.  This keeps full fp32 accuracy
+// at any position (pair 0 turns through tens of thousands of radians at long
+// positions) for a few double operations.
+__device__ __forceinline__ void rope_cs_theta(int pos, double theta, float& c, float& s) {
   const double ang = (double)pos * theta;
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+  const double k = rint(ang * 0.63661977236758134);         // 2 / pi
+  const float f = (float)fma(-k, 1.5707963267948966, ang);  // pi / 2
+  const float f2 = f * f;
+  float sp = fmaf(f2, 1.f / 362880.f, -1.f / 5040.f);  // 1/9!, -1/7!
+  sp = fmaf(sp, f2, 1.f / 120.f);
+  sp = fmaf(sp, f2, -1.f / 6.f);
+  const float sf = fmaf(f * f2, sp, f);
+  float cp = fmaf(f2, -1.f / 3628800.f, 1.f / 40320.f);  // -1/10!, 1/8!
+  cp = fmaf(cp, f2, -1.f / 720.f);
+  cp = fmaf(cp, f2, 1.f / 24.f);
+  cp = fmaf(cp, f2, -0.5f);
+  const float cf = fmaf(cp, f2, 1.f);
+  const int q = (int)(long long)k & 3;
+  const float cs = (q & 1) ? sf : cf, sn = (q & 1) ? cf : sf;
+  c = (q == 1 || q == 2) ? -cs : cs;
+  s = (q & 2) ? -sn : sn;
+}
+
+__device__ __forceinline__ void rope_cs(int pos, int i, int d, float base, float& c, float& s) {
+  rope_cs_theta(pos, rope_inv_freq(i, d, base), c, s);
 }
 
 // ---------------------------------------------------------------- decode work split
