@@ -50,9 +50,11 @@ __device__ __forceinline__ int swz(int r) { return (((r & 3) << 1) | ((r >> 2) &
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 // The score chain keeps its accumulator in VGPRs (inline asm) while the
@@ -133,10 +135,12 @@ __device__ __forceinline__ int p_off(int h, int kk, int g) { return 64 * h + 16 
 
 // Softmax numerators of one tile for head lane % 32: p = 2^(s sl2 - m_ref)
 // rounded to bf16, written to the P^T buffer; their sum goes to lsum.
-// Tokens at or past t1 (only in a ragged last tile) get p = 0.
+// Tokens at or past t1 (only in a ragged last tile) get p = 0; MAYBE_RAGGED
+// false is for tiles known to be full (every tile but an item's last).
+template <bool MAYBE_RAGGED>
 __device__ __forceinline__ void tile_softmax(const f32x16& sacc, int tok0, int t1, int g, float sl2, float m_ref,
                                              char* pbuf, int head_off, float& lsum, const ReadOffsets& o) {
-  const bool full = tok0 + TT <= t1;
+  const bool full = !MAYBE_RAGGED || tok0 + TT <= t1;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     uint32_t wds[4];
@@ -389,7 +393,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
       score_drain(sacc);
     }
     const float m_ref = tile_max(sacc, t0, t1, g) * sl2;  // fixed for the whole item
-    tile_softmax(sacc, t0, t1, g, sl2, m_ref, pbufs, head_off, lsum, ro);
+    if (ntiles > 1) tile_softmax<false>(sacc, t0, t1, g, sl2, m_ref, pbufs, head_off, lsum, ro);
+    else tile_softmax<true>(sacc, t0, t1, g, sl2, m_ref, pbufs, head_off, lsum, ro);
 
     // step it: latent update of tile it (P^T buffer it % 2) interleaved with the
     // scores of tile it+1, whose numerators go to P^T buffer (it+1) % 2
@@ -408,7 +413,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
       const char* nxt = tiles + ((it + 1) & 3) * TILE_BYTES;
       tile_step<NW, true>(sacc, nxt, qf, acc, cur, pbufs + (it & 1) * PBUF_BYTES, w, ro);
       const int tok1 = t0 + (it + 1) * TT;
-      tile_softmax(sacc, tok1, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum, ro);
+      if (it + 2 < ntiles) tile_softmax<false>(sacc, tok1, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum, ro);
+      else tile_softmax<true>(sacc, tok1, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum, ro);
     }
     // latent update of the last tile (its scores were taken in the last step)
     __builtin_amdgcn_s_barrier();
