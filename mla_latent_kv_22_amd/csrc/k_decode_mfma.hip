@@ -330,7 +330,10 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
     const int b = __builtin_amdgcn_readlane(d_b, rd);
     const int t0 = __builtin_amdgcn_readlane(d_t0, rd);
     const int t1 = __builtin_amdgcn_readlane(d_t1, rd);
-    const int32_t* __restrict__ btb = a.block_table + (size_t)b * a.max_pages_per_seq;
+    // block-table entries are read through the constant address space: scalar
+    // loads, counted by lgkmcnt, so they never wait for the tile loads in flight
+    const __attribute__((address_space(4))) int32_t* btb =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_table + (size_t)b * a.max_pages_per_seq);
     const int ntiles = (t1 - t0 + TT - 1) / TT;
     auto tile_ptr = [&](int tile, int& nvalid) {
       const int tok0 = t0 + tile * TT;
@@ -339,26 +342,26 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
       return pool + ((size_t)page * P + (tok0 % P)) * (RW * 2);
     };
 
-    // prologue: tile 0 first, so its bytes are on the way while the absorbed
-    // query fragments load (B operand of the score MFMA: head hq,
-    // k = 16 ks + 8 g .. +7), then tiles 1 and 2; the tile waits below count
-    // the loads issued after the ones they need
-    {
-      int nv;
-      const char* tp = tile_ptr(0, nv);
-      issue_tile<NW>(tp, nv, lds_tiles, w, lane, lane_off);
-    }
+    // prologue: the absorbed query fragments (B operand of the score MFMA:
+    // head hq, k = 16 ks + 8 g .. +7), then tiles 0, 1 and 2.  No wait for
+    // loads of this round may sit between the tile loads: in-order retirement
+    // would make it wait for the tiles as well.  The tile waits below count
+    // the loads issued after the ones they need.
     u32x4 qf[KS];
     {
-      const uint16_t* qp = (const uint16_t*)a.q_abs + ((size_t)b * a.H + (hvalid ? hq : 0)) * RW + 8 * g;
+      // uniform base plus a 32-bit lane offset, formed here (no 64-bit
+      // per-lane pointer kept alive across the item loop)
+      const char* qb = (const char*)a.q_abs + (size_t)b * a.H * (RW * 2);
+      uint32_t qo = (uint32_t)((hvalid ? hq : 0) * (RW * 2) + 16 * g);
+      asm volatile("" : "+v"(qo));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        u32x4 v = *(const u32x4*)(qp + 16 * ks);
+        u32x4 v = *(const u32x4*)(qb + qo + 32 * ks);
         qf[ks] = hvalid ? v : u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
-    for (int st = 1; st < 3; ++st) {
+    for (int st = 0; st < 3; ++st) {
       if (st < ntiles) {
         int nv;
         const char* tp = tile_ptr(st, nv);
