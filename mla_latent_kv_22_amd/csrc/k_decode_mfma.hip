@@ -242,6 +242,85 @@ __device__ __forceinline__ void tile_step(f32x16& sacc, const char* ts, const u3
   if constexpr (SCORES) score_drain(sacc);
 }
 
+// One step of the tile loop, fused: the 36 chained score MFMAs of tile it+1
+// with the first NPA latent MFMAs of tile it interleaved, then the softmax
+// numerators of tile it+1 (written to P^T buffer pbuf_wr, as tile_softmax;
+// tile it+1 must be full) in eight pieces with the remaining latent MFMAs
+// between them, so that the VALU work of the softmax runs beside MFMA work
+// instead of after it.  The latent MFMAs keep the order and operand reads of
+// tile_step.
+template <int NW>
+__device__ __forceinline__ void tile_step_fused(f32x16& sacc, const char* ts, const u32x4* qf, f32x16* acc,
+                                                const char* tp, const char* pbuf_rd, int w, const ReadOffsets& o,
+                                                int tok0, int g, float sl2, float m_ref, char* pbuf_wr, int head_off,
+                                                float& lsum) {
+  using S = Split<NW>;
+  constexpr int PF = 3;
+  // latent MFMAs beside the score chain: 36 + NPA MFMAs take about as long
+  // as the dependent chain alone; the other 12 run beside the softmax
+  constexpr int NPA = S::NPC - 12;
+  u32x4 kf[PF];
+#pragma unroll
+  for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x4*)(ts + o.s[ks & 3] + 4096 * (ks >> 2));
+  auto tr_a = [&](int kk, int fbl) {
+    const int fb = S::FBW * w + fbl;
+    const int imm = 4096 * (fb >> 1) + 2048 * kk;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][0] + imm));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp + o.t[fb & 1][1] + imm + 1024));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
+  auto p_frag = [&](int kk, int hb) { return *(const u32x4*)(pbuf_rd + 2048 * hb + o.p[kk]); };
+  u32x4 af[2], pf[S::HB];
+  af[0] = tr_a(0, 0);
+#pragma unroll
+  for (int hb = 0; hb < S::HB; ++hb) pf[hb] = p_frag(0, hb);
+  auto pv = [&](int op) {
+    const int kk = op / (S::FBW * S::HB), fbl = (op / S::HB) % S::FBW, hb = op % S::HB;
+    const int grp = op / S::HB;  // (kk, fbl) group index 0 .. 2 FBW - 1
+    if (hb == 0 && grp + 1 < 2 * S::FBW) af[(grp + 1) & 1] = tr_a((grp + 1) / S::FBW, (grp + 1) % S::FBW);
+    const u32x4 bv = pf[hb];
+    if (kk == 0 && fbl == S::FBW - 1) pf[hb] = p_frag(1, hb);  // last kk = 0 use of this slot
+    acc[fbl * S::HB + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[grp & 1]), as_bf16x8(bv),
+                                                                    acc[fbl * S::HB + hb], 0, 0, 0);
+  };
+#pragma unroll
+  for (int c = 0; c < KS; ++c) {
+    const u32x4 cur = kf[c % PF];
+    if (c + PF < KS) kf[c % PF] = *(const u32x4*)(ts + o.s[(c + PF) & 3] + 4096 * ((c + PF) >> 2));
+    if (c == 0) score_first(sacc, cur, qf[c]);
+    else score_next(sacc, cur, qf[c]);
+    // latent MFMAs c NPA / KS .. (c + 1) NPA / KS - 1 follow score MFMA c
+#pragma unroll
+    for (int op = c * NPA / KS; op < (c + 1) * NPA / KS; ++op) pv(op);
+  }
+  score_drain(sacc);
+  __builtin_amdgcn_sched_barrier(0);
+  (void)tok0;
+  (void)g;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    uint32_t wds[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int j = 8 * kk + e;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], sl2, -m_ref));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j + 1], sl2, -m_ref));
+      const uint32_t pk = pack_bf16x2(p0, p1);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                             lsum, false);
+      wds[e >> 1] = pk;
+      // piece k = 4 kk + e / 2 is followed by latent MFMAs NPA + 3 k / 2 ..;
+      // the scheduling barriers keep the VALU and MFMA work alternating
+      const int k = 4 * kk + (e >> 1);
+#pragma unroll
+      for (int op = NPA + 3 * k / 2; op < NPA + 3 * (k + 1) / 2; ++op) pv(op);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    *(u32x4*)(pbuf_wr + head_off + o.p[kk]) = u32x4{wds[0], wds[1], wds[2], wds[3]};
+  }
+}
+
 // LDS map (160 KiB, the whole LDS of a CU):
 //   [0, 147456)        four tile stages of 36864 bytes
 //   [147456, 163840)   two P^T buffers of NW * 2048 bytes (8192 for NW = 4)
@@ -401,7 +480,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
 
     // step it: latent update of tile it (P^T buffer it % 2) interleaved with the
     // scores of tile it+1, whose numerators go to P^T buffer (it+1) % 2
-    for (int it = 0; it + 1 < ntiles; ++it) {
+    auto step_sync = [&](int it) {
       int nv3 = 0;
       const char* tp3 = (it + 3 < ntiles) ? tile_ptr(it + 3, nv3) : nullptr;  // scalar page load, early
       // this wave's loads of tile it+1 are done once only tile it+2's remain
@@ -412,12 +491,26 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       if (it + 3 < ntiles) issue_tile<NW>(tp3, nv3, lds_tiles + ((it + 3) & 3) * TILE_BYTES, w, lane, lane_off);
+    };
+    // tile it+1 is full for it + 2 < ntiles: the fused step (softmax beside
+    // the latent MFMAs)
+    int it = 0;
+    for (; it + 2 < ntiles; ++it) {
+      step_sync(it);
+      const char* cur = tiles + (it & 3) * TILE_BYTES;
+      const char* nxt = tiles + ((it + 1) & 3) * TILE_BYTES;
+      const int tok1 = t0 + (it + 1) * TT;
+      tile_step_fused<NW>(sacc, nxt, qf, acc, cur, pbufs + (it & 1) * PBUF_BYTES, w, ro, tok1, g, sl2, m_ref,
+                          pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum);
+    }
+    // the item's last tile (maybe ragged): scores, then its numerators
+    if (it + 1 < ntiles) {
+      step_sync(it);
       const char* cur = tiles + (it & 3) * TILE_BYTES;
       const char* nxt = tiles + ((it + 1) & 3) * TILE_BYTES;
       tile_step<NW, true>(sacc, nxt, qf, acc, cur, pbufs + (it & 1) * PBUF_BYTES, w, ro);
       const int tok1 = t0 + (it + 1) * TT;
-      if (it + 2 < ntiles) tile_softmax<false>(sacc, tok1, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum, ro);
-      else tile_softmax<true>(sacc, tok1, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum, ro);
+      tile_softmax<true>(sacc, tok1, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES, head_off, lsum, ro);
     }
     // latent update of the last tile (its scores were taken in the last step)
     __builtin_amdgcn_s_barrier();
