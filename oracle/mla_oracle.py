@@ -34,6 +34,10 @@ Readings where the pages leave a step open (all pinned by tests/test_oracle_*):
     including its own row written in the same step ([arch] 2: project, then
     write, then read).
   * Prefill: query i of a fresh sequence sees rows t <= i.
+  * Prefill onto a cached prefix (the pages ask for prefill to be measured
+    under real serving shapes, [arch] 4; they do not spell out chunking): the
+    new tokens of a sequence follow ``prefix`` tokens already in the cache;
+    new query i sits at position prefix + i and sees rows t <= prefix + i.
 """
 from __future__ import annotations
 
@@ -233,13 +237,17 @@ def decode(q: np.ndarray, pool: np.ndarray, block_table: np.ndarray, seq_lens: n
 def prefill_one(q: np.ndarray, rows: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray,
                 d_c: int, sigma: float, base: float,
                 queries: Optional[Sequence[int]] = None,
-                heads: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """Causal prefill of one fresh sequence: query i (position i) sees rows
-    t <= i.  q [T, H, d_n + d_R], rows [T, R].  Returns o [T, H, d_v] and
-    lse [T, H]; entries outside ``queries`` x ``heads`` are NaN."""
+                heads: Optional[Sequence[int]] = None,
+                prefix: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Causal prefill of the T new tokens of one sequence that follow
+    ``prefix`` cached tokens (0: a fresh sequence): new query i sits at
+    position prefix + i and sees rows t <= prefix + i.  q [T, H, d_n + d_R],
+    rows [prefix + T, R] (all of the sequence's rows).  Returns o [T, H, d_v]
+    and lse [T, H]; entries outside ``queries`` x ``heads`` are NaN."""
     T, H, _ = q.shape
     d_n = w_uk.shape[1]
     d_v = w_uv.shape[1]
+    assert rows.shape[0] >= prefix + T
     C = rows[:, :d_c]
     KR = rows[:, d_c:]
     qi = np.arange(T) if queries is None else np.asarray(queries)
@@ -249,10 +257,11 @@ def prefill_one(q: np.ndarray, rows: np.ndarray, w_uk: np.ndarray, w_uv: np.ndar
         K_c = C @ w_uk[h].T
         V = C @ w_uv[h].T
         for i in qi.tolist():
+            p = prefix + i
             q_c = q[i, h, :d_n]
-            q_r = rope(q[i, h, d_n:], i, base)
-            s = sigma * (K_c[: i + 1] @ q_c + KR[: i + 1] @ q_r)
-            o[i, h], lse[i, h] = _attend(s, V[: i + 1])
+            q_r = rope(q[i, h, d_n:], p, base)
+            s = sigma * (K_c[: p + 1] @ q_c + KR[: p + 1] @ q_r)
+            o[i, h], lse[i, h] = _attend(s, V[: p + 1])
     return o, lse
 
 

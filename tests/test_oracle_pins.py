@@ -286,6 +286,66 @@ def test_causal_prefill_equals_sdpa_causal():
         assert _rel(o[:, i], ref) < 1e-12
 
 
+def _prefix_case(seed, P, L):
+    rng = np.random.default_rng(seed)
+    H, D, d_c, d_r, d_n, d_v = 3, 12, 8, 4, 6, 5
+    T = P + L
+    h = rng.standard_normal((T, D))
+    w_dkv, w_kr = rng.standard_normal((d_c, D)) * 0.3, rng.standard_normal((d_r, D)) * 0.3
+    w_uk, w_uv = rng.standard_normal((H, d_n, d_c)) * 0.3, rng.standard_normal((H, d_v, d_c)) * 0.3
+    q = rng.standard_normal((T, H, d_n + d_r))
+    base, sigma = 10000.0, 0.35
+    rows = O.latent_rows(h, w_dkv, w_kr, np.arange(T), base)
+    return dict(H=H, d_c=d_c, d_n=d_n, w_uk=w_uk, w_uv=w_uv, q=q, base=base, sigma=sigma, rows=rows)
+
+
+@pytest.mark.parametrize("P,L", [(7, 5), (0, 6), (13, 1)])
+def test_prefix_prefill_equals_sdpa_bottom_right_mask(P, L):
+    """Prefill onto a prefix of P cached tokens is attention of the L new
+    queries (positions P..P+L-1) over all P+L keys with the causal mask aligned
+    to the last key: torch's SDPA with that explicit boolean mask."""
+    c = _prefix_case(40 + P, P, L)
+    q, rows, d_c, d_n = c["q"][P:], c["rows"], c["d_c"], c["d_n"]
+    o, lse = O.prefill_one(q, rows, c["w_uk"], c["w_uv"], d_c, c["sigma"], c["base"], prefix=P)
+    mask = torch.tensor(np.arange(P + L)[None, :] <= (P + np.arange(L))[:, None])
+    for i in range(c["H"]):
+        K = np.concatenate([rows[:, :d_c] @ c["w_uk"][i].T, rows[:, d_c:]], 1)
+        V = rows[:, :d_c] @ c["w_uv"][i].T
+        Q = np.concatenate([q[:, i, :d_n], np.stack([O.rope(q[t, i, d_n:], P + t, c["base"]) for t in range(L)])], 1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(Q)[None, None], torch.tensor(K)[None, None], torch.tensor(V)[None, None],
+            attn_mask=mask, scale=c["sigma"])[0, 0].numpy()
+        assert _rel(o[:, i], ref) < 1e-12
+        s = c["sigma"] * (Q @ K.T)
+        s[~mask.numpy()] = -np.inf
+        lse_ref = np.log(np.sum(np.exp(s), axis=1))
+        assert np.max(np.abs(lse[:, i] - lse_ref)) < 1e-12
+
+
+def test_prefix_prefill_is_the_tail_of_a_full_prefill():
+    """Causal attention by position: the new rows of a prefill onto a prefix
+    equal the last rows of a prefill of the whole sequence."""
+    P, L = 9, 6
+    c = _prefix_case(50, P, L)
+    args = (c["w_uk"], c["w_uv"], c["d_c"], c["sigma"], c["base"])
+    o_full, lse_full = O.prefill_one(c["q"], c["rows"], *args)
+    o_tail, lse_tail = O.prefill_one(c["q"][P:], c["rows"], *args, prefix=P)
+    assert np.max(np.abs(o_tail - o_full[P:])) < 1e-12
+    assert np.max(np.abs(lse_tail - lse_full[P:])) < 1e-12
+
+
+def test_prefix_prefill_of_one_token_is_decode():
+    """One new token after P cached ones is the decode query at position P
+    over P + 1 rows."""
+    P = 11
+    c = _prefix_case(51, P, 1)
+    o_p, lse_p = O.prefill_one(c["q"][P:], c["rows"], c["w_uk"], c["w_uv"], c["d_c"], c["sigma"], c["base"],
+                               prefix=P)
+    o_d, lse_d = O.decode_one(c["q"][P], c["rows"], c["w_uk"], c["w_uv"], P, c["d_c"], c["sigma"], c["base"])
+    assert np.max(np.abs(o_p[0] - o_d)) < 1e-12
+    assert np.max(np.abs(lse_p[0] - lse_d)) < 1e-12
+
+
 # ---------------------------------------------------------------------------
 # invariants the pages state
 # ---------------------------------------------------------------------------
@@ -465,7 +525,7 @@ def _mut_decode_one(slip):
     return f
 
 
-def _mut_prefill_peek(q, rows, w_uk, w_uv, d_c, sigma, base, queries=None, heads=None):
+def _mut_prefill_peek(q, rows, w_uk, w_uv, d_c, sigma, base, queries=None, heads=None, prefix=0):
     """prefill that lets query i also see row i+1 (causal mask off by one)."""
     T, H, _ = q.shape
     d_n = w_uk.shape[1]
@@ -475,7 +535,27 @@ def _mut_prefill_peek(q, rows, w_uk, w_uv, d_c, sigma, base, queries=None, heads
         K = rows[:, :d_c] @ w_uk[h].T
         V = rows[:, :d_c] @ w_uv[h].T
         for i in (range(T) if queries is None else queries):
-            n = min(T, i + 2)
+            n = min(rows.shape[0], prefix + i + 2)
+            s = sigma * (K[:n] @ q[i, h, :d_n] + rows[:n, d_c:] @ O.rope(q[i, h, d_n:], prefix + i, base))
+            m = s.max()
+            w = np.exp(s - m)
+            o[i, h] = (w @ V[:n]) / w.sum()
+            lse[i, h] = m + math.log(w.sum())
+    return o, lse
+
+
+def _mut_prefill_prefix_position(q, rows, w_uk, w_uv, d_c, sigma, base, queries=None, heads=None, prefix=0):
+    """prefill onto a prefix that rotates the new queries as if they started at
+    position 0 (the prefix left out of the query position)."""
+    T, H, _ = q.shape
+    d_n = w_uk.shape[1]
+    o = np.full((T, H, w_uv.shape[1]), np.nan)
+    lse = np.full((T, H), np.nan)
+    for h in (range(H) if heads is None else heads):
+        K = rows[:, :d_c] @ w_uk[h].T
+        V = rows[:, :d_c] @ w_uv[h].T
+        for i in (range(T) if queries is None else queries):
+            n = prefix + i + 1
             s = sigma * (K[:n] @ q[i, h, :d_n] + rows[:n, d_c:] @ O.rope(q[i, h, d_n:], i, base))
             m = s.max()
             w = np.exp(s - m)
@@ -491,7 +571,7 @@ def _mut_attend_log2(scores, values):
 
 
 @pytest.mark.parametrize("mutation", ["rope_sign", "rope_pairing", "drop_kr", "sigma_content_only",
-                                      "causal_off_by_one", "lse_log2"])
+                                      "causal_off_by_one", "lse_log2", "prefix_position"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     import oracle.mla_oracle as M
 
@@ -509,10 +589,13 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
         patch("prefill_one", _mut_prefill_peek)
     elif mutation == "lse_log2":
         patch("_attend", _mut_attend_log2)
+    elif mutation == "prefix_position":
+        patch("prefill_one", _mut_prefill_prefix_position)
     pins = [test_rope_closed_forms, lambda: test_brute_force_decode(0), lambda: test_brute_force_prefill(0),
             test_absorbed_equals_sdpa_mqa, test_causal_prefill_equals_sdpa_causal,
             test_absorbed_and_nonabsorbed_logits_agree, test_single_token_context,
-            test_identity_weights_textbook_attention]
+            test_identity_weights_textbook_attention, lambda: test_prefix_prefill_equals_sdpa_bottom_right_mask(7, 5),
+            test_prefix_prefill_is_the_tail_of_a_full_prefill, test_prefix_prefill_of_one_token_is_decode]
     caught = 0
     for p in pins:
         try:
