@@ -113,12 +113,41 @@ def prefill_leg(steps=5):
     attn, proj = prefill_flops(cfg, inp["seq_lens"])
     tf = (attn + proj) / (a_ms * 1e-3) / 1e12
     wflops = 2.0 * cfg.row_width * cfg.hidden * float(np.sum(inp["seq_lens"]))
+
+    # chunked prefill: the second half of every sequence onto its cached first
+    # half (mla_prefill_kv); useful work counts the new queries' visible keys
+    # and the up-projection of every key
+    from mla_latent_kv_22_amd import mla
+    lens = inp["seq_lens"].astype(np.int64)
+    pre = lens // 2
+    new = lens - pre
+    cu = inp["cu_seqlens"].astype(np.int64)
+    idx = np.concatenate([np.arange(cu[b] + pre[b], cu[b + 1]) for b in range(len(lens))])
+    q_new = pf.q[torch.as_tensor(idx, device=pf.q.device)].contiguous()
+    cu_q = torch.as_tensor(np.concatenate([[0], np.cumsum(new)]).astype(np.int32), device=pf.q.device)
+    out_c = torch.empty((int(new.sum()),) + tuple(pf.out.shape[1:]), dtype=pf.out.dtype, device=pf.out.device)
+    lse_c = torch.empty((int(new.sum()), cfg.num_heads), dtype=torch.float32, device=pf.out.device)
+    ws_c = torch.empty(mla.prefill_workspace_size(pf.d, int(cu[-1])), dtype=torch.uint8, device=pf.q.device)
+
+    def chunk():
+        mla.prefill_kv(pf.d, q_new, pf.pool, pf.block_table, cu_q, pf.cu, int(cu[-1]), int(new.max()),
+                       int(lens.max()), pf.w_uk, pf.w_uv, out_c, lse_c, ws_c)
+    chunk()
+    torch.cuda.synchronize()
+    c_ms = timed(chunk)
+    c_pairs = float(sum(int(n) * int(p) + int(n) * (int(n) + 1) // 2 for n, p in zip(new, pre)))
+    c_attn = 2.0 * (cfg.qk_nope + cfg.d_r + cfg.v_head) * cfg.num_heads * c_pairs
+    c_proj = 2.0 * cfg.d_c * (cfg.qk_nope + cfg.v_head) * cfg.num_heads * float(lens.sum())
+    c_tf = (c_attn + c_proj) / (c_ms * 1e-3) / 1e12
     return {"workload": f"{cfg.name}: {cfg.batch} x {cfg.seq_len} tokens, H={cfg.num_heads}, d_n=d_v={cfg.qk_nope}, "
                         f"d_R={cfg.d_r}, d_c={cfg.d_c}, D={cfg.hidden}, bf16, page={cfg.page_size}",
             "prefill_ms": round(a_ms, 4), "useful_tflop": round((attn + proj) / 1e12, 4),
             "tflops": round(tf, 1), "mfma_frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "write_cache_ms": round(w_ms, 4),
-            "write_cache_tflops": round(wflops / (w_ms * 1e-3) / 1e12, 1)}
+            "write_cache_tflops": round(wflops / (w_ms * 1e-3) / 1e12, 1),
+            "chunked": {"workload": f"last {int(new[0])} tokens of each sequence onto its cached first {int(pre[0])}",
+                        "ms": round(c_ms, 4), "useful_tflop": round((c_attn + c_proj) / 1e12, 4),
+                        "tflops": round(c_tf, 1), "mfma_frac_of_bf16_peak": round(c_tf / BF16_PEAK_TFLOPS, 4)}}
 
 
 def main():

@@ -146,7 +146,8 @@ int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int3
                int32_t batch, int32_t max_seq_len, const void* w_uv, void* out, float* lse,
                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace mla_prefill needs for `total_tokens` query tokens. */
+/* Bytes of workspace mla_prefill needs for `total_tokens` query tokens, and
+ * mla_prefill_kv for `total_tokens` key tokens (pass its total_kv). */
 size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t total_tokens);
 
 /*
@@ -171,6 +172,34 @@ int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t
                 int32_t num_seqs, int32_t total_tokens, int32_t max_seq_len, const void* w_uk,
                 const void* w_uv, void* out, float* lse, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
+
+/*
+ * Prefill of new tokens onto sequences that may already hold a cached prefix
+ * (chunked prefill).  openarchlab section 4 asks for prefill to be measured
+ * under real serving shapes; the pages do not spell out chunking, and the
+ * reading taken is causal attention by position: sequence i has
+ * kv_len = cu_seqlens_kv[i+1] - cu_seqlens_kv[i] cached tokens in the pool
+ * (positions 0 .. kv_len-1, the new tokens' rows already written), of which
+ * the last q_len = cu_seqlens_q[i+1] - cu_seqlens_q[i] are the new tokens,
+ * rows cu_seqlens_q[i] .. of q/out.  New token j sits at position
+ * prefix + j, prefix = kv_len - q_len, and attends to cache positions
+ * 0 .. prefix + j, with the same K, V, score and LSE as mla_prefill.
+ *
+ *   cu_seqlens_q   [num_seqs + 1]  int32 (device), cu_q[num_seqs] = total_q
+ *   cu_seqlens_kv  [num_seqs + 1]  int32 (device), cu_kv[num_seqs] = total_kv,
+ *                                  kv_len >= q_len for every sequence
+ *   max_q_len, max_kv_len          bounds of q_len and kv_len (tiling and the
+ *                                  capacity check against max_pages_per_seq)
+ *   workspace                      mla_prefill_workspace_size(dims, total_kv)
+ * Other arguments, layouts and errors as mla_prefill; MLA_ERR_ARG also when
+ * total_kv < total_q or max_kv_len < max_q_len.  mla_prefill is this call
+ * with cu_seqlens_kv = cu_seqlens_q (no prefix).
+ */
+int mla_prefill_kv(const mla_dims_t* dims, const void* q, const void* pool, int32_t num_pages,
+                   const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* cu_seqlens_q,
+                   const int32_t* cu_seqlens_kv, int32_t num_seqs, int32_t total_q, int32_t total_kv,
+                   int32_t max_q_len, int32_t max_kv_len, const void* w_uk, const void* w_uv, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Ideal cache bytes of `tokens` tokens over `layers` layers:

@@ -196,8 +196,9 @@ __global__ void __launch_bounds__(128) k_decode_combine(DecodeArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// prefill: up-project K_C and V per head into an fp32 workspace, then causal
-// attention with one work-group per (query token, head).
+// prefill: up-project K_C and V per head into an fp32 workspace (every key
+// token: cached prefix and new tokens), then causal attention with one
+// work-group per (new query token, head).
 __device__ __forceinline__ int seq_of(const int32_t* cu, int num_seqs, int n) {
   int lo = 0, hi = num_seqs - 1;
   while (lo < hi) {
@@ -211,12 +212,12 @@ template <typename T>
 __global__ void __launch_bounds__(256) k_prefill_upproj(PrefillArgs a) {
   const int J = a.d_n + a.d_v;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long long)a.total * a.H * J) return;
+  if (idx >= (long long)a.total_kv * a.H * J) return;
   const int j = (int)(idx % J);
   const long long nh = idx / J;
-  const int h = (int)(nh % a.H), n = (int)(nh / a.H);
-  const int sq = seq_of(a.cu_seqlens, a.num_seqs, n);
-  const int t = n - a.cu_seqlens[sq];
+  const int h = (int)(nh % a.H), n = (int)(nh / a.H);  // n: key token (prefix and new)
+  const int sq = seq_of(a.cu_kv, a.num_seqs, n);
+  const int t = n - a.cu_kv[sq];
   const int R = a.d_c + a.d_r;
   const T* row = (const T*)a.pool +
                  ((size_t)a.block_table[(size_t)sq * a.max_pages_per_seq + t / a.P] * a.P + t % a.P) * R;
@@ -235,9 +236,10 @@ __global__ void __launch_bounds__(128) k_prefill_attn(PrefillArgs a) {
   float* ps = qs + a.d_n + a.d_r;      // 128
   float* red = ps + 128;               // 4
   const int n = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int sq = seq_of(a.cu_seqlens, a.num_seqs, n);
-  const int base = a.cu_seqlens[sq];
-  const int i = n - base;  // position of this query in its sequence
+  const int sq = seq_of(a.cu_q, a.num_seqs, n);
+  const int base = a.cu_kv[sq];  // first key token of the sequence in the workspace
+  const int prefix = max(0, (a.cu_kv[sq + 1] - base) - (a.cu_q[sq + 1] - a.cu_q[sq]));
+  const int i = prefix + n - a.cu_q[sq];  // position of this query in its sequence
   const int R = a.d_c + a.d_r;
   const T* qv = (const T*)a.q + ((size_t)n * a.H + h) * (a.d_n + a.d_r);
   for (int k = tid; k < a.d_n; k += 128) qs[k] = ld(qv, k);
@@ -339,7 +341,7 @@ hipError_t decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s) {
 
 hipError_t prefill_generic(const PrefillArgs& a, bool bf16, hipStream_t s) {
   if (a.total == 0) return hipSuccess;
-  const long long n = (long long)a.total * a.H * (a.d_n + a.d_v);
+  const long long n = (long long)a.total_kv * a.H * (a.d_n + a.d_v);
   const size_t lds = (size_t)(a.d_n + a.d_r + 128 + 4) * sizeof(float);
   if (bf16) {
     hipLaunchKernelGGL(k_prefill_upproj<uint16_t>, dim3(blocks_for(n, 256)), dim3(256), 0, s, a);

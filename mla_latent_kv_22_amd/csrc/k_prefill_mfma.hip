@@ -8,12 +8,14 @@
 // instead of 2 (576 + 512) in the absorbed order.
 //
 // 1. k_prefill_proj: K_C[h][n] = W_UK,h c_n and V[h][n] = W_UV,h c_n for every
-//    token, a GEMM [tokens x d_c] x [d_c x 128] per head (32x32x16 MFMA).
+//    key token (a sequence's cached prefix and its new tokens), a GEMM
+//    [tokens x d_c] x [d_c x 128] per head (32x32x16 MFMA).
 //    Latent rows come from the paged pool; outputs go to the workspace as
 //    bf16, head-major ([H][tokens][128]) so that one head's keys of one
 //    sequence are contiguous.
 // 2. k_prefill_attn_mfma: causal flash attention per (sequence, head,
-//    128-query block).  Each wave owns 32 queries.  Scores are computed
+//    128-query block of its new tokens; new token j sits at position
+//    prefix + j and sees keys 0 .. prefix + j).  Each wave owns 32 queries.  Scores are computed
 //    transposed, S^T = K Q^T, so that a lane holds all its scores for one
 //    query: the softmax numerators then feed the P.V MFMA straight from
 //    registers as its B operand, and the V^T operand comes from LDS transpose
@@ -74,7 +76,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_proj(PrefillArgs a) {
   const int n0 = blockIdx.x * XT, h = blockIdx.y, which = blockIdx.z;  // 0: K_C, 1: V
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
-  const int N = a.total, R = a.d_c + a.d_r;
+  const int N = a.total_kv, R = a.d_c + a.d_r;  // every key token: cached prefix and new
   const char* __restrict__ Wh = (const char*)(which ? a.w_uv : a.w_uk) + (size_t)h * PD * a.d_c * 2;
   const uint32_t lds0 = lds_addr_of(smem);
 
@@ -88,8 +90,8 @@ __global__ void __launch_bounds__(256, 2) k_prefill_proj(PrefillArgs a) {
     const int r = 8 * ((w + 4 * i) & 15) + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int n = min(n0 + r, N - 1);
-    const int s = seq_of(a.cu_seqlens, a.num_seqs, n);
-    const int t = n - a.cu_seqlens[s];
+    const int s = seq_of(a.cu_kv, a.num_seqs, n);
+    const int t = n - a.cu_kv[s];
     const int page = a.block_table[(size_t)s * a.max_pages_per_seq + t / a.P];
     crow[i] = (const char*)a.pool + ((size_t)page * a.P + t % a.P) * (size_t)R * 2;
     cchunk[i] = 16u * c;
@@ -184,25 +186,34 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   }
   const int qb = nqb - 1 - qr;
   const int s = pair / a.H, h = pair % a.H;
-  const int cu0 = a.cu_seqlens[s], len = a.cu_seqlens[s + 1] - cu0;
-  const int q0 = qb * AQ;
+  // new tokens cu0 .. cu0 + len - 1 of q / out; the sequence's keys (a cached
+  // prefix, then the new tokens) are key tokens ck0 .. ck0 + klen - 1 of the
+  // workspace and positions 0 .. klen - 1 of the cache
+  const int cu0 = a.cu_q[s], len = a.cu_q[s + 1] - cu0;
+  const int ck0 = a.cu_kv[s], klen = a.cu_kv[s + 1] - ck0;
+  const int prefix = max(0, klen - len);
+  const int q0 = qb * AQ;  // query block, in new-token indices
   if (q0 >= len) return;
   const int qend = min(len, q0 + AQ);
-  const int n_kt = (qend + AK - 1) / AK;
+  const int n_kt = (prefix + qend + AK - 1) / AK;
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
-  const int N = a.total, R = a.d_c + a.d_r;
-  const int qi = q0 + 32 * w + r32;  // this lane's query (position in its sequence)
-  const bool qvalid = qi < qend;
-  const int w_last = min(qend - 1, q0 + 32 * w + 31);
-  const int kt_last = q0 + 32 * w < qend ? w_last / AK : -1;  // last tile this wave computes
+  const int N = a.total_kv, R = a.d_c + a.d_r;
+  const int ql_lane = q0 + 32 * w + r32;  // this lane's query (new-token index)
+  const bool qvalid = ql_lane < qend;
+  const int qi = prefix + ql_lane;        // its position in the sequence
+  const int w_last = prefix + min(qend - 1, q0 + 32 * w + 31);
+  const bool w_any = q0 + 32 * w < qend;
+  const int kt_last = w_any ? w_last / AK : -1;  // last tile this wave computes
+  // tiles before kt_mask hold only keys at or before the wave's first query
+  const int kt_mask = w_any ? min(kt_last + 1, (prefix + q0 + 32 * w + 1) / AK) : 0;
 
   // query fragments (B operand of S^T = K Q^T): query = lane % 32,
   // k = 16 ks + 8 g .. +7; ks < 8: q_C, ks >= 8: RoPE(q_R, qi) rounded to bf16
   u32x4 qf[12];
   {
-    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(cu0 + (qvalid ? qi : q0)) * a.H + h) * (PD + PDR) + 8 * g;
+    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(cu0 + (qvalid ? ql_lane : q0)) * a.H + h) * (PD + PDR) + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks);
     // lane l computes theta of pair l % 32 once; the lanes share them
@@ -225,8 +236,8 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   // tile loads: wave w issues loads u = w + 4 i (i < 5) of the 20:
   // u < 8 K_C rows 4 u .. +3; u < 12 k_R rows 8 (u - 8) .. +7; else V rows 4 (u - 12) .. +3.
   // Rows past the sequence end repeat its last key (masked in the scores).
-  const char* __restrict__ kc_base = (const char*)a.ws_k + ((size_t)h * N + cu0) * (PD * 2);
-  const char* __restrict__ v_base = (const char*)a.ws_v + ((size_t)h * N + cu0) * (PD * 2);
+  const char* __restrict__ kc_base = (const char*)a.ws_k + ((size_t)h * N + ck0) * (PD * 2);
+  const char* __restrict__ v_base = (const char*)a.ws_v + ((size_t)h * N + ck0) * (PD * 2);
   const int32_t* __restrict__ bt = a.block_table + (size_t)s * a.max_pages_per_seq;
   const uint32_t lds0 = lds_addr_of(smem);
   // the block-table entry of a tile is read one iteration before its loads
@@ -238,7 +249,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   auto page_of = [&](int kt) { return bt_c[min(kt, n_kt - 1) * AK / a.P]; };
   auto issue = [&](int kt, int page) {
     const int key0 = kt * AK;
-    const int maxr = len - 1 - key0;
+    const int maxr = klen - 1 - key0;
     const char* kr_base = (const char*)a.pool + ((size_t)page * a.P + key0 % a.P) * (size_t)R * 2 + a.d_c * 2;
     const uint32_t st = lds0 + (kt & (NST - 1)) * ST_BYTES;
 #pragma unroll
@@ -380,16 +391,17 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   for (int t = 0; t < 3; ++t)
     if (t < n_kt) issue(t, page_of(t));
   // every wave takes part in all n_kt barriers and loads; it computes
-  // tiles 0 .. kt_last, of which only the last meets the diagonal
+  // tiles 0 .. kt_last, of which those from kt_mask on meet the diagonal (one
+  // tile for a fresh sequence, at most two after a prefix that is not a
+  // multiple of 32)
   int kt = 0;
-  for (; kt < kt_last; ++kt) {
+  for (; kt < kt_mask; ++kt) {
     sync(kt);
     tile(kt, std::false_type{});
   }
-  if (kt_last >= 0) {
-    sync(kt_last);
-    tile(kt_last, std::true_type{});
-    kt = kt_last + 1;
+  for (; kt <= kt_last; ++kt) {
+    sync(kt);
+    tile(kt, std::true_type{});
   }
   for (; kt < n_kt; ++kt) sync(kt);
 
@@ -397,7 +409,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   // (16-byte slot (d / 8) ^ (query % 16)), then written in whole rows
   const float lt = l + __shfl_xor(l, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qvalid && g == 0 && a.lse) a.lse[(size_t)(cu0 + qi) * a.H + h] = (m + log2f(lt)) * kLn2;
+  if (qvalid && g == 0 && a.lse) a.lse[(size_t)(cu0 + ql_lane) * a.H + h] = (m + log2f(lt)) * kLn2;
   __syncthreads();  // every wave is done with the tile stages
   uint16_t* ot = (uint16_t*)smem;
   const int ql = 32 * w + r32;
@@ -428,7 +440,7 @@ bool prefill_mfma_supported(int d_n, int d_v, int d_r, int d_c, int P) {
 
 hipError_t prefill_mfma(const PrefillArgs& a, hipStream_t s) {
   if (a.total == 0 || a.num_seqs == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_prefill_proj, dim3((a.total + XT - 1) / XT, a.H, 2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_prefill_proj, dim3((a.total_kv + XT - 1) / XT, a.H, 2), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.max_seq_len + AQ - 1) / AQ;

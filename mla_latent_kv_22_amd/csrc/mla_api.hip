@@ -210,27 +210,32 @@ size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t total_tokens) 
   return prefill_ws_bytes(dims, total_tokens);
 }
 
-int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t num_pages,
-                const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* cu_seqlens,
-                int32_t num_seqs, int32_t total_tokens, int32_t max_seq_len, const void* w_uk, const void* w_uv,
-                void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int mla_prefill_kv(const mla_dims_t* dims, const void* q, const void* pool, int32_t num_pages,
+                   const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* cu_seqlens_q,
+                   const int32_t* cu_seqlens_kv, int32_t num_seqs, int32_t total_q, int32_t total_kv,
+                   int32_t max_q_len, int32_t max_kv_len, const void* w_uk, const void* w_uv, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (num_seqs < 0 || total_tokens < 0 || max_seq_len < 0 || num_pages < 0 || max_pages_per_seq < 0)
+  if (num_seqs < 0 || total_q < 0 || total_kv < 0 || max_q_len < 0 || max_kv_len < 0 || num_pages < 0 ||
+      max_pages_per_seq < 0)
     return MLA_ERR_ARG;
+  if (total_kv < total_q || max_kv_len < max_q_len) return MLA_ERR_ARG;
   if (dims->v_head > 256) return MLA_ERR_DIMS;
-  if (num_seqs == 0 || total_tokens == 0) return MLA_OK;
-  if (!q || !pool || !block_table || !cu_seqlens || !w_uk || !w_uv || !out || !workspace) return MLA_ERR_NULL;
-  if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * dims->page_size) return MLA_ERR_CAPACITY;
-  if (workspace_bytes < prefill_ws_bytes(dims, total_tokens)) return MLA_ERR_WORKSPACE;
-  size_t kb = (size_t)total_tokens * dims->num_heads * dims->qk_nope * sizeof(float);
+  if (num_seqs == 0 || total_q == 0) return MLA_OK;
+  if (!q || !pool || !block_table || !cu_seqlens_q || !cu_seqlens_kv || !w_uk || !w_uv || !out || !workspace)
+    return MLA_ERR_NULL;
+  if ((int64_t)max_kv_len > (int64_t)max_pages_per_seq * dims->page_size) return MLA_ERR_CAPACITY;
+  if (workspace_bytes < prefill_ws_bytes(dims, total_kv)) return MLA_ERR_WORKSPACE;
+  size_t kb = (size_t)total_kv * dims->num_heads * dims->qk_nope * sizeof(float);
   kb = (kb + 255) & ~(size_t)255;
   PrefillArgs a;
   memset(&a, 0, sizeof a);
   a.q = q;
   a.pool = pool;
   a.block_table = block_table;
-  a.cu_seqlens = cu_seqlens;
+  a.cu_q = cu_seqlens_q;
+  a.cu_kv = cu_seqlens_kv;
   a.w_uk = w_uk;
   a.w_uv = w_uv;
   a.out = out;
@@ -238,8 +243,9 @@ int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t
   a.ws_k = workspace;
   a.ws_v = (char*)workspace + kb;
   a.num_seqs = num_seqs;
-  a.total = total_tokens;
-  a.max_seq_len = max_seq_len;
+  a.total = total_q;
+  a.total_kv = total_kv;
+  a.max_seq_len = max_q_len;
   a.H = dims->num_heads;
   a.d_n = dims->qk_nope;
   a.d_r = dims->d_r;
@@ -251,6 +257,16 @@ int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t
   a.scale = dims->softmax_scale;
   if (prefill_fast(dims)) return launched(prefill_mfma(a, stream));
   return launched(prefill_generic(a, dims->dtype == MLA_BF16, stream));
+}
+
+int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t num_pages,
+                const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* cu_seqlens,
+                int32_t num_seqs, int32_t total_tokens, int32_t max_seq_len, const void* w_uk, const void* w_uv,
+                void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // fresh sequences: the keys are exactly the new tokens
+  return mla_prefill_kv(dims, q, pool, num_pages, block_table, max_pages_per_seq, cu_seqlens, cu_seqlens, num_seqs,
+                        total_tokens, total_tokens, max_seq_len, max_seq_len, w_uk, w_uv, out, lse, workspace,
+                        workspace_bytes, stream);
 }
 
 }  // extern "C"

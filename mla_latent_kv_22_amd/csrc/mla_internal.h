@@ -59,14 +59,15 @@ struct PrefillArgs {
   const void* q;
   const void* pool;
   const int32_t* block_table;
-  const int32_t* cu_seqlens;
+  const int32_t* cu_q;   // [num_seqs + 1] new (query) tokens per sequence
+  const int32_t* cu_kv;  // [num_seqs + 1] all tokens per sequence (prefix + new), keys
   const void* w_uk;
   const void* w_uv;
   void* out;
   float* lse;
-  void* ws_k;  // up-projected K_C: fp32 [total, H, d_n] (generic) or bf16 [H, total, d_n] (MFMA)
-  void* ws_v;  // up-projected V:   fp32 [total, H, d_v] (generic) or bf16 [H, total, d_v] (MFMA)
-  int num_seqs, total, max_seq_len, H, d_n, d_r, d_c, d_v, P, max_pages_per_seq;
+  void* ws_k;  // up-projected K_C: fp32 [total_kv, H, d_n] (generic) or bf16 [H, total_kv, d_n] (MFMA)
+  void* ws_v;  // up-projected V:   fp32 [total_kv, H, d_v] (generic) or bf16 [H, total_kv, d_v] (MFMA)
+  int num_seqs, total, total_kv, max_seq_len, H, d_n, d_r, d_c, d_v, P, max_pages_per_seq;
   float rope_base, scale;
 };
 

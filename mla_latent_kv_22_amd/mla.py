@@ -22,8 +22,8 @@ FLAG_GENERIC = 1
 OP_WRITE_CACHE, OP_ABSORB_Q, OP_DECODE, OP_PREFILL = 0, 1, 2, 3
 
 _SYMBOLS = ("mla_write_cache", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode",
-            "mla_prefill_workspace_size", "mla_prefill", "mla_cache_bytes", "mla_status_string",
-            "mla_uses_fast_path")
+            "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_kv", "mla_cache_bytes",
+            "mla_status_string", "mla_uses_fast_path")
 
 
 class Dims(ctypes.Structure):
@@ -59,12 +59,15 @@ def lib() -> ctypes.CDLL:
         L.mla_prefill_workspace_size.argtypes = [dp, i32]
         L.mla_prefill_workspace_size.restype = sz
         L.mla_prefill.argtypes = [dp, vp, vp, i32, vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.mla_prefill_kv.argtypes = [dp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                     vp, sz, vp]
         L.mla_cache_bytes.argtypes = [dp, i64, i32]
         L.mla_cache_bytes.restype = sz
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_uses_fast_path.argtypes = [dp, i32]
-        for f in ("mla_write_cache", "mla_absorb_q", "mla_decode", "mla_prefill", "mla_uses_fast_path"):
+        for f in ("mla_write_cache", "mla_absorb_q", "mla_decode", "mla_prefill", "mla_prefill_kv",
+                  "mla_uses_fast_path"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -158,6 +161,22 @@ def prefill(d: Dims, q, pool, block_table, cu_seqlens, max_seq_len: int, w_uk, w
                              _ptr(out, "out", dt), _ptr(lse, "lse", torch.float32),
                              _ptr(workspace, "workspace", torch.uint8),
                              0 if workspace is None else workspace.numel(), _stream(stream)), "mla_prefill")
+
+
+def prefill_kv(d: Dims, q, pool, block_table, cu_seqlens_q, cu_seqlens_kv, total_kv: int, max_q_len: int,
+               max_kv_len: int, w_uk, w_uv, out, lse, workspace, stream=None) -> None:
+    """Prefill of the new tokens (q rows) onto sequences with a cached prefix:
+    sequence i's keys are its cu_seqlens_kv[i+1] - cu_seqlens_kv[i] cached
+    tokens, the last q_len of them new."""
+    dt = _torch_dtype(d)
+    _check(lib().mla_prefill_kv(ctypes.byref(d), _ptr(q, "q", dt), _ptr(pool, "pool", dt), int(pool.shape[0]),
+                                _ptr(block_table, "block_table", torch.int32), int(block_table.shape[1]),
+                                _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+                                _ptr(cu_seqlens_kv, "cu_seqlens_kv", torch.int32), int(cu_seqlens_q.shape[0]) - 1,
+                                int(q.shape[0]), int(total_kv), int(max_q_len), int(max_kv_len),
+                                _ptr(w_uk, "w_uk", dt), _ptr(w_uv, "w_uv", dt), _ptr(out, "out", dt),
+                                _ptr(lse, "lse", torch.float32), _ptr(workspace, "workspace", torch.uint8),
+                                0 if workspace is None else workspace.numel(), _stream(stream)), "mla_prefill_kv")
 
 
 def cache_bytes(d: Dims, tokens: int, layers: int) -> int:

@@ -114,6 +114,18 @@ def test_null_and_count_errors():
                          1 << 30, None) == -1
     assert L.mla_prefill(ctypes.byref(d), None, None, 0, None, 0, None, 0, 0, 0, None, None, None, None, None, 0,
                          None) == 0
+    # prefill onto a prefix: keys fewer than queries; null kv offsets; kv
+    # capacity; workspace sized for the keys; empty is a no-op
+    kv = lambda cuq, cukv, tq, tkv, mq, mkv, ws: L.mla_prefill_kv(  # noqa: E731
+        ctypes.byref(d), FAKE, FAKE, 4, FAKE, 4, cuq, cukv, 2, tq, tkv, mq, mkv, FAKE, FAKE, FAKE, None, FAKE, ws, None)
+    assert kv(FAKE, FAKE, 64, 32, 32, 32, 1 << 30) == -7
+    assert kv(FAKE, FAKE, 32, 64, 64, 32, 1 << 30) == -7
+    assert kv(FAKE, None, 32, 64, 32, 64, 1 << 30) == -1
+    assert kv(FAKE, FAKE, 32, 512, 32, 257, 1 << 30) == -5
+    assert kv(FAKE, FAKE, 32, 512, 32, 256, mla.lib().mla_prefill_workspace_size(ctypes.byref(d), 511)) == -4
+    assert kv(FAKE, FAKE, 32, 512, 32, 256, mla.lib().mla_prefill_workspace_size(ctypes.byref(d), 512) - 1) == -4
+    assert L.mla_prefill_kv(ctypes.byref(d), None, None, 0, None, 0, None, None, 0, 0, 0, 0, 0, None, None, None,
+                            None, None, 0, None) == 0
     d.v_head = 512
     assert L.mla_prefill(ctypes.byref(d), FAKE, FAKE, 4, FAKE, 4, FAKE, 2, 64, 64, FAKE, FAKE, FAKE, None, FAKE,
                          1 << 30, None) == -2
