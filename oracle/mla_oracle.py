@@ -34,6 +34,10 @@ Readings where the pages leave a step open (all pinned by tests/test_oracle_*):
     including its own row written in the same step ([arch] 2: project, then
     write, then read).
   * Prefill: query i of a fresh sequence sees rows t <= i.
+  * 8-bit cache rows ([blog] "MLA ve diger optimizasyonlarla iliskisi"
+    allows 8-bit storage of the cached vector; [arch] 3 mentions its scales):
+    E4M3 codes of the bf16 row over one power-of-two scale per row, nearest
+    code with ties to even; see the section "8-bit cache rows" below.
   * Prefill onto a cached prefix (the pages ask for prefill to be measured
     under real serving shapes, [arch] 4; they do not spell out chunking): the
     new tokens of a sequence follow ``prefix`` tokens already in the cache;
@@ -169,6 +173,129 @@ def gather_rows(pool: np.ndarray, block_table_row: np.ndarray, length: int) -> n
     for t in range(length):
         out[t] = pool[int(block_table_row[t // P]), t % P]
     return out
+
+
+# --------------------------------------------------------------------------
+# 8-bit cache rows ([blog] "MLA ve diger optimizasyonlarla iliskisi": the
+# cached vector may be stored with 8 bits per value, MLA and quantization
+# combine; [arch] 3: the cache formula leaves out the quantization scales)
+#
+# Readings (the pages name neither format nor scale granularity):
+#   * 8-bit values are E4M3 floats: sign, 4 exponent bits (bias 7), 3 mantissa
+#     bits; exponent field 0 holds the subnormals m * 2^-9; code S.1111.111 is
+#     NaN and the largest finite magnitude is 448 (S.1111.110).  There is no
+#     infinity.
+#   * One scale per cached row (token), a power of two 2^e: the smallest e
+#     with amax <= 448 * 2^e, where amax is the largest magnitude of the
+#     row, and e >= -126; an all-zero row takes e = 0.
+#   * The row is first rounded to bf16 (the values a bf16 cache would hold),
+#     then every value x becomes the E4M3 code nearest to x / 2^e, ties to
+#     the even code; a result of -0 is stored as +0 (code 0).
+#   * Stored value = E4M3 value of the code times 2^e.
+#   * Page layout: the P rows of R codes, then P float32 scales (little
+#     endian), so a page holds P * (R + 4) bytes.
+# --------------------------------------------------------------------------
+
+
+def e4m3_value(code) -> np.ndarray:
+    """Float64 value of E4M3 codes (NaN for the two NaN codes)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def quantize_e4m3(x) -> np.ndarray:
+    """E4M3 code of each value of x (float64, |x| <= 448): the nearest finite
+    code, ties to the code with an even mantissa; zero results get code 0.
+
+    Written from the format: below 2^-6 the grid is the multiples of 2^-9;
+    above, a binade [2^k, 2^(k+1)) holds 8 values spaced 2^(k-3).  The value
+    is scaled so that the grid spacing becomes 1, rounded half-even to an
+    integer, and re-encoded."""
+    x = np.asarray(x, dtype=np.float64)
+    assert np.all(np.abs(x) <= 448.0), "value outside the E4M3 range"
+    a = np.abs(x)
+    _, k = np.frexp(a)                       # a = f 2^k, 0.5 <= f < 1  (k = floor(log2 a) + 1)
+    k = np.where(a > 0, k - 1, -10)          # floor(log2 a)
+    k = np.maximum(k, -6)                    # subnormal range shares the 2^-6 binade spacing
+    step = np.exp2(k - 3.0)                  # grid spacing in this binade
+    n = np.round(a / step)                   # half-even integer count of steps (exact division)
+    # n = 16 means the value rounded up into the next binade
+    up = n >= 16
+    k = np.where(up, k + 1, k)
+    n = np.where(up, n / 2, n)
+    sub = (k == -6) & (n < 8)                # subnormal: exponent field 0, mantissa n
+    ef = np.where(sub, 0, k + 7)
+    mf = np.where(sub, n, n - 8)
+    code = (ef.astype(np.int64) << 3) | mf.astype(np.int64)
+    code = np.where(np.signbit(x) & (code != 0), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def row_scale_exponent(amax: float) -> int:
+    """Smallest e >= -126 with amax <= 448 * 2^e (0 for amax = 0)."""
+    if amax == 0.0:
+        return 0
+    e = -126
+    while amax > 448.0 * 2.0 ** e:
+        e += 1
+    return e
+
+
+def quantize_row_fp8(row) -> Tuple[np.ndarray, float]:
+    """One cached row -> (R codes, scale 2^e).  The row is rounded to bf16
+    first; the scale comes from the bf16 row's largest magnitude."""
+    r = round_bf16(np.asarray(row, dtype=np.float64))
+    e = row_scale_exponent(float(np.max(np.abs(r))) if r.size else 0.0)
+    return quantize_e4m3(r / 2.0 ** e), 2.0 ** e
+
+
+def dequantize_rows_fp8(codes, scales) -> np.ndarray:
+    """Stored values: E4M3 value of each code times its row's scale."""
+    return e4m3_value(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def pack_fp8_pages(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """codes [num_pages, P, R] uint8 and scales [num_pages, P] -> page bytes
+    [num_pages, P * (R + 4)]: the P rows, then the P float32 scales."""
+    npg, P, R = codes.shape
+    out = np.empty((npg, P * (R + 4)), dtype=np.uint8)
+    out[:, :P * R] = codes.reshape(npg, P * R)
+    out[:, P * R:] = np.asarray(scales, dtype="<f4").reshape(npg, P).view(np.uint8).reshape(npg, 4 * P)
+    return out
+
+
+def unpack_fp8_pages(pages: np.ndarray, P: int, R: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Inverse of pack_fp8_pages: (codes [num_pages, P, R], scales [num_pages, P] float64)."""
+    pages = np.asarray(pages, dtype=np.uint8)
+    npg = pages.shape[0]
+    codes = pages[:, :P * R].reshape(npg, P, R)
+    scales = np.ascontiguousarray(pages[:, P * R:P * (R + 4)]).view("<f4").reshape(npg, P).astype(np.float64)
+    return codes, scales
+
+
+def write_rows_fp8(pages: np.ndarray, rows: np.ndarray, slots, P: int) -> np.ndarray:
+    """Quantize each row and store codes and scale at its slot of the page
+    bytes (a copy is returned; slot -1 is skipped)."""
+    R = rows.shape[1]
+    codes, scales = unpack_fp8_pages(pages, P, R)
+    codes, scales = codes.copy(), scales.copy()
+    for n, s in enumerate(np.asarray(slots).tolist()):
+        if s < 0:
+            continue
+        codes[s // P, s % P], scales[s // P, s % P] = quantize_row_fp8(rows[n])
+    return pack_fp8_pages(codes, scales)
+
+
+def fp8_pool_values(pages: np.ndarray, P: int, R: int) -> np.ndarray:
+    """Float64 pool [num_pages, P, R] of the stored values of page bytes; the
+    decode and prefill functions below read it like any other pool."""
+    codes, scales = unpack_fp8_pages(pages, P, R)
+    return dequantize_rows_fp8(codes, scales)
 
 
 # --------------------------------------------------------------------------

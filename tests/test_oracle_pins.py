@@ -474,6 +474,148 @@ def test_decode_batch_uses_block_table():
 
 
 # ---------------------------------------------------------------------------
+# 8-bit cache rows: E4M3 codes with one power-of-two scale per row
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3_codes(x):
+    """torch's own float -> float8_e4m3fn conversion (round to nearest even),
+    with -0 folded into +0 as the oracle stores it."""
+    c = torch.as_tensor(np.asarray(x, np.float64)).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    return np.where(c == 0x80, 0, c)
+
+
+def test_e4m3_values_match_torch_float8():
+    codes = np.arange(256)
+    ours = O.e4m3_value(codes)
+    ref = torch.as_tensor(codes.astype(np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)) and int(np.isnan(ours).sum()) == 2
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    # facts of the format: 448 is the largest finite value, 2^-9 the smallest
+    # positive, 2^-6 the smallest normal, and codes 0x00..0x7E increase
+    assert np.nanmax(ours) == 448.0 and ours[1] == 2.0 ** -9 and ours[8] == 2.0 ** -6
+    assert np.all(np.diff(ours[:0x7F]) > 0)
+
+
+def test_e4m3_quantize_matches_torch_cast():
+    rng = np.random.default_rng(5)
+    # float32 inputs (torch converts through float32; the cache's inputs are
+    # bf16 values over a power of two, so float32 holds them exactly)
+    grid = O.e4m3_value(np.arange(0x7F)).astype(np.float32)
+    mids = (grid[1:] + grid[:-1]) / 2                     # exact ties
+    x = np.concatenate([grid, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1000)),
+                        rng.uniform(-448, 448, 20000).astype(np.float32),
+                        np.exp2(rng.uniform(-14, np.log2(448), 20000)).astype(np.float32),
+                        np.array([0.0, 2.0 ** -11, 3 * 2.0 ** -11, 448.0], np.float32)]).astype(np.float64)
+    x = np.concatenate([x, -x])
+    assert np.array_equal(O.quantize_e4m3(x).astype(np.int64), _torch_e4m3_codes(x))
+
+
+def test_e4m3_quantize_inverts_decode():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)])
+    assert np.array_equal(O.quantize_e4m3(O.e4m3_value(codes)).astype(np.int64), codes)
+
+
+@pytest.mark.parametrize("amax", [0.0, 2.0 ** -130, 1e-30, 0.37, 1.0, 224.0, 224.0001, 448.0, 448.5, 3.0e5, 1e30])
+def test_row_scale_exponent_bounds(amax):
+    e = O.row_scale_exponent(amax)
+    if amax == 0.0:
+        assert e == 0
+        return
+    assert amax <= 448.0 * 2.0 ** e
+    assert e == -126 or amax > 448.0 * 2.0 ** (e - 1)
+
+
+def test_quantize_row_error_bound_and_scale():
+    rng = np.random.default_rng(6)
+    for mag in (1e-3, 1.0, 37.0, 1e4):
+        row = rng.standard_normal(576) * mag
+        codes, scale = O.quantize_row_fp8(row)
+        bf = O.round_bf16(row)
+        assert math.log2(scale) == int(math.log2(scale))            # a power of two
+        amax = float(np.max(np.abs(bf)))
+        assert 224.0 < amax / scale <= 448.0
+        deq = O.e4m3_value(codes) * scale
+        # nearest grid point: at most half a step, 2^-4 of the value's binade
+        # base for normals, 2^-10 scale for subnormals
+        half = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(bf) / scale, 2.0 ** -6))) - 4), 2.0 ** -10) * scale
+        assert np.all(np.abs(deq - bf) <= half)
+        assert np.array_equal(codes.astype(np.int64), _torch_e4m3_codes(bf / scale))
+
+
+def test_fp8_pages_layout_and_roundtrip():
+    rng = np.random.default_rng(7)
+    P, R, npg = 4, 6, 3
+    codes = rng.integers(0, 0x7F, size=(npg, P, R)).astype(np.uint8)
+    scales = np.exp2(rng.integers(-5, 5, size=(npg, P))).astype(np.float64)
+    pages = O.pack_fp8_pages(codes, scales)
+    assert pages.shape == (npg, P * (R + 4))
+    # row t of page g starts at byte R t; its scale is the little-endian
+    # float32 at byte P R + 4 t
+    g, t = 2, 3
+    assert bytes(pages[g, R * t:R * t + R]) == bytes(codes[g, t])
+    assert np.frombuffer(bytes(pages[g, P * R + 4 * t:P * R + 4 * t + 4]), "<f4")[0] == scales[g, t]
+    c2, s2 = O.unpack_fp8_pages(pages, P, R)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+
+
+def test_fp8_write_one_hot_rows_and_skip():
+    # selection weights and position 0: the row is the chosen hidden values
+    # exactly, so its codes are torch's E4M3 casts of those values over the
+    # row's scale; slot -1 leaves the pages unchanged
+    rng = np.random.default_rng(8)
+    D, d_c, d_r, P = 12, 6, 2, 4
+    h = O.round_bf16(rng.standard_normal((3, D)) * 3.0)
+    sel = rng.permutation(D)[:d_c + d_r]
+    w = np.zeros((d_c + d_r, D))
+    w[np.arange(d_c + d_r), sel] = 1.0
+    rows = O.latent_rows(h, w[:d_c], w[d_c:], np.zeros(3), 10000.0)
+    assert np.array_equal(rows, h[:, sel])
+    pages0 = np.full((2, P * (d_c + d_r + 4)), 0x5A, dtype=np.uint8)
+    pages = O.write_rows_fp8(pages0, rows, np.array([5, -1, 2]), P)
+    codes, scales = O.unpack_fp8_pages(pages, P, d_c + d_r)
+    for n, slot in ((0, 5), (2, 2)):
+        sc = scales[slot // P, slot % P]
+        assert sc == 2.0 ** O.row_scale_exponent(float(np.max(np.abs(rows[n]))))
+        assert np.array_equal(codes[slot // P, slot % P].astype(np.int64), _torch_e4m3_codes(rows[n] / sc))
+    c0, s0 = O.unpack_fp8_pages(pages0, P, d_c + d_r)
+    untouched = [(g, t) for g in range(2) for t in range(P) if g * P + t not in (5, 2)]
+    for g, t in untouched:
+        assert np.array_equal(codes[g, t], c0[g, t])
+        assert s0[g, t] == scales[g, t] or (np.isnan(s0[g, t]) and np.isnan(scales[g, t]))
+
+
+def test_fp8_pool_decode_equals_decode_of_its_values():
+    # a pool whose codes all have scale 1 holds E4M3 values, which bf16 holds
+    # exactly: decoding the 8-bit pool equals decoding those values
+    rng = np.random.default_rng(9)
+    B, H, T, P, d_c, d_r, d_n, d_v = 2, 3, 9, 4, 8, 4, 5, 6
+    R = d_c + d_r
+    npg = B * ((T + P - 1) // P)
+    codes = rng.integers(0, 0x7F, size=(npg, P, R)).astype(np.uint8)
+    codes ^= (rng.integers(0, 2, size=codes.shape) << 7).astype(np.uint8)  # random signs
+    codes[codes == 0xFF] = 0x7E
+    scales = np.exp2(rng.integers(-9, -4, size=(npg, P))).astype(np.float64)
+    pages = O.pack_fp8_pages(codes, scales)
+    vals = O.fp8_pool_values(pages, P, R)
+    assert np.array_equal(O.round_bf16(vals), vals)
+    bt = rng.permutation(npg).reshape(B, -1).astype(np.int32)
+    q = rng.standard_normal((B, H, d_n + d_r))
+    w_uk = rng.standard_normal((H, d_n, d_c)) * 0.3
+    w_uv = rng.standard_normal((H, d_v, d_c)) * 0.3
+    lens = np.array([T, T - 3])
+    o8, l8 = O.decode(q, vals, bt, lens, w_uk, w_uv, d_c, 0.4, 10000.0)
+    # the same values written out element by element from codes and scales
+    manual = np.empty_like(vals)
+    for g in range(npg):
+        for t in range(P):
+            manual[g, t] = [float(torch.tensor([int(c)], dtype=torch.uint8).view(torch.float8_e4m3fn).double())
+                            * scales[g, t] for c in codes[g, t]]
+    o_ref, l_ref = O.decode(q, manual, bt, lens, w_uk, w_uv, d_c, 0.4, 10000.0)
+    assert np.array_equal(o8, o_ref) and np.array_equal(l8, l_ref)
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: a copy of the oracle with one plausible slip must fail a pin
 # ---------------------------------------------------------------------------
 
@@ -570,8 +712,39 @@ def _mut_attend_log2(scores, values):
     return (w @ values) / w.sum(), m + math.log2(w.sum())
 
 
+def _mut_quantize_ties_away(x):
+    # round half away from zero instead of half to even
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, k = np.frexp(a)
+    k = np.maximum(np.where(a > 0, k - 1, -10), -6)
+    step = np.exp2(k - 3.0)
+    n = np.floor(a / step + 0.5)
+    up = n >= 16
+    k = np.where(up, k + 1, k)
+    n = np.where(up, n / 2, n)
+    sub = (k == -6) & (n < 8)
+    code = (np.where(sub, 0, k + 7).astype(np.int64) << 3) | np.where(sub, n, n - 8).astype(np.int64)
+    code = np.where(np.signbit(x) & (code != 0), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def _mut_scale_exponent_plus_one(amax):
+    import oracle.mla_oracle as M
+    return M._orig_row_scale_exponent(amax) + (1 if amax > 0 else 0)
+
+
+def _mut_unpack_scales_first(pages, P, R):
+    pages = np.asarray(pages, dtype=np.uint8)
+    npg = pages.shape[0]
+    scales = np.ascontiguousarray(pages[:, :4 * P]).view("<f4").reshape(npg, P).astype(np.float64)
+    codes = pages[:, 4 * P:4 * P + P * R].reshape(npg, P, R)
+    return codes, scales
+
+
 @pytest.mark.parametrize("mutation", ["rope_sign", "rope_pairing", "drop_kr", "sigma_content_only",
-                                      "causal_off_by_one", "lse_log2", "prefix_position"])
+                                      "causal_off_by_one", "lse_log2", "prefix_position",
+                                      "fp8_ties_away", "fp8_scale_exponent", "fp8_scales_first"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     import oracle.mla_oracle as M
 
@@ -591,11 +764,21 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
         patch("_attend", _mut_attend_log2)
     elif mutation == "prefix_position":
         patch("prefill_one", _mut_prefill_prefix_position)
+    elif mutation == "fp8_ties_away":
+        patch("quantize_e4m3", _mut_quantize_ties_away)
+    elif mutation == "fp8_scale_exponent":
+        monkeypatch.setattr(M, "_orig_row_scale_exponent", M.row_scale_exponent, raising=False)
+        patch("row_scale_exponent", _mut_scale_exponent_plus_one)
+    elif mutation == "fp8_scales_first":
+        patch("unpack_fp8_pages", _mut_unpack_scales_first)
     pins = [test_rope_closed_forms, lambda: test_brute_force_decode(0), lambda: test_brute_force_prefill(0),
             test_absorbed_equals_sdpa_mqa, test_causal_prefill_equals_sdpa_causal,
             test_absorbed_and_nonabsorbed_logits_agree, test_single_token_context,
             test_identity_weights_textbook_attention, lambda: test_prefix_prefill_equals_sdpa_bottom_right_mask(7, 5),
-            test_prefix_prefill_is_the_tail_of_a_full_prefill, test_prefix_prefill_of_one_token_is_decode]
+            test_prefix_prefill_is_the_tail_of_a_full_prefill, test_prefix_prefill_of_one_token_is_decode,
+            test_e4m3_quantize_matches_torch_cast, test_e4m3_quantize_inverts_decode,
+            lambda: test_row_scale_exponent_bounds(0.37), test_quantize_row_error_bound_and_scale,
+            test_fp8_pages_layout_and_roundtrip, test_fp8_write_one_hot_rows_and_skip]
     caught = 0
     for p in pins:
         try:
