@@ -61,9 +61,25 @@ typedef enum {
 
 enum { MLA_F32 = 0, MLA_BF16 = 1 };
 
-/* flags: MLA_FLAG_GENERIC forces the plain (VALU, any-shape) kernels even
- * where the MFMA kernels apply; used to cross-check the two on one input. */
-enum { MLA_FLAG_GENERIC = 1 };
+/* flags (bitwise or):
+ *   MLA_FLAG_GENERIC forces the plain (VALU, any-shape) kernels even where
+ *   the MFMA kernels apply; used to cross-check the two on one input.
+ *   MLA_FLAG_FP8_CACHE selects the 8-bit cache (yapayzekasozluk.tr, section
+ *   "MLA ve diger optimizasyonlarla iliskisi": the cached vector may be stored
+ *   with 8 bits per value; openarchlab section 3 names the quantization
+ *   scales that the ideal-size formula leaves out).  Requires dtype MLA_BF16
+ *   (h, weights, queries and outputs stay bf16).  A page then holds, for its
+ *   P tokens, first the P rows of d_c + d_r E4M3 codes (1 sign, 4 exponent
+ *   bits with bias 7, 3 mantissa bits; 448 is the largest value), then P
+ *   float32 row scales: page bytes = P * (d_c + d_r + 4), see
+ *   mla_page_bytes.  A row stores value x as the E4M3 code nearest to
+ *   x / 2^e (ties to even, -0 stored as +0), where 2^e is the row's scale:
+ *   the smallest power of two, at least 2^-126, with max |x| <= 448 * 2^e,
+ *   taken over the row after rounding it to bf16.  The stored value is
+ *   E4M3(code) * 2^e.  mla_write_cache_ws writes such rows, mla_decode reads
+ *   them; prefill does not read an 8-bit pool (MLA_ERR_DTYPE).  Rows whose
+ *   largest magnitude is at or above 2^126 or below 2^-117 lose range. */
+enum { MLA_FLAG_GENERIC = 1, MLA_FLAG_FP8_CACHE = 2 };
 
 typedef struct {
   int32_t hidden;      /* D: width of h                                         */
@@ -76,7 +92,7 @@ typedef struct {
   int32_t dtype;       /* MLA_F32 or MLA_BF16                                   */
   float rope_base;     /* RoPE base (10000 in the pages' models)                */
   float softmax_scale; /* sigma, multiplies every score                         */
-  int32_t flags;       /* 0 or MLA_FLAG_GENERIC                                 */
+  int32_t flags;       /* 0 or MLA_FLAG_* bits                                  */
 } mla_dims_t;
 
 /*
@@ -99,6 +115,30 @@ typedef struct {
 int mla_write_cache(const mla_dims_t* dims, const void* h, const void* w_dkr,
                     const int32_t* positions, const int64_t* slot_mapping, int32_t n_tokens,
                     void* pool, int32_t num_pages, hipStream_t stream);
+
+/* Bytes of workspace mla_write_cache_ws needs for n_tokens rows: 0 for bf16
+ * and fp32 caches, n_tokens * (d_c + d_r) * 2 for the 8-bit cache. */
+size_t mla_write_cache_workspace_size(const mla_dims_t* dims, int32_t n_tokens);
+
+/*
+ * mla_write_cache with a workspace, for every cache format.  With
+ * MLA_FLAG_FP8_CACHE the rows are computed as in mla_write_cache (bf16,
+ * round to nearest even) into the workspace, then each row with
+ * slot_mapping[n] >= 0 is quantized (see MLA_FLAG_FP8_CACHE) and its codes
+ * and scale are stored at its slot of the 8-bit pool.  mla_write_cache is
+ * this call with no workspace, so it returns MLA_ERR_WORKSPACE for an 8-bit
+ * cache.
+ *   workspace  >= mla_write_cache_workspace_size(dims, n_tokens) bytes
+ *              (may be NULL when that size is 0)
+ */
+int mla_write_cache_ws(const mla_dims_t* dims, const void* h, const void* w_dkr,
+                       const int32_t* positions, const int64_t* slot_mapping, int32_t n_tokens,
+                       void* pool, int32_t num_pages, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Bytes of one cache page: P * (d_c + d_r) * element bytes, or
+ * P * (d_c + d_r + 4) for the 8-bit cache (0 for invalid dims). */
+size_t mla_page_bytes(const mla_dims_t* dims);
 
 /*
  * Query absorption (openarchlab sections 1 and 6: W_UK folded into the query).
@@ -127,7 +167,10 @@ size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t 
  * Empty sequences give out = 0, lse = -inf.
  *
  *   q_abs       [batch, H, d_c + d_r]           dtype
- *   pool        [num_pages, P, d_c + d_r]       dtype
+ *   pool        [num_pages, P, d_c + d_r]       dtype, or num_pages 8-bit
+ *                                               pages (MLA_FLAG_FP8_CACHE);
+ *                                               row_t is then the stored
+ *                                               value E4M3(code) * scale
  *   block_table [batch, max_pages_per_seq]      int32
  *   seq_lens    [batch]                         int32 (device); lengths above
  *                                                max_seq_len are clamped to it
@@ -205,7 +248,8 @@ int mla_prefill_kv(const mla_dims_t* dims, const void* q, const void* pool, int3
  * Ideal cache bytes of `tokens` tokens over `layers` layers:
  * layers x tokens x (d_c + d_r) x element bytes (openarchlab section 3;
  * LLMScale "Multi-head latent attention (MLA)": the head count drops out).
- * Returns 0 for invalid dims.
+ * The 8-bit cache counts one byte per value; like the pages' formula, the
+ * figure leaves out the scales.  Returns 0 for invalid dims.
  */
 size_t mla_cache_bytes(const mla_dims_t* dims, int64_t tokens, int32_t layers);
 

@@ -2,6 +2,8 @@
 // They are the library's path for shapes the MFMA kernels do not cover (for
 // example the fp32 workloads) and a second implementation to cross-check the
 // MFMA kernels on the same inputs.  Arithmetic is fp32 throughout.
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -17,7 +19,7 @@ __global__ void __launch_bounds__(256) k_write_cache(WriteCacheArgs a) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)a.n_tokens * J) return;
   const int n = (int)(idx / J), j = (int)(idx % J);
-  const long long slot = a.slots[n];
+  const long long slot = a.dense ? (long long)n : a.slots[n];
   if (slot < 0) return;
   const int R = a.d_c + a.d_r;
   const T* h = (const T*)a.h + (size_t)n * a.D;
@@ -76,7 +78,11 @@ __global__ void __launch_bounds__(256) k_absorb(AbsorbArgs a) {
 // decode pass 1: one wave per (work item, head).  Online softmax over the
 // item's token range in tiles of 64 tokens (one score per lane), latent
 // accumulator in LDS.  Emits (m, l, acc) in log2 units.
-template <typename T>
+// With F8 the pool is 8-bit (queries stay T = bf16): a row's score is its
+// code values' dot product times the row scale, and the row scale rides with
+// the numerator into the latent sum (p 2^e times the code values), while the
+// softmax sum takes p itself.
+template <typename T, bool F8 = false>
 __global__ void __launch_bounds__(64) k_decode_split(DecodeArgs a) {
   extern __shared__ float dyn[];
   int* s_len = (int*)dyn;
@@ -86,7 +92,8 @@ __global__ void __launch_bounds__(64) k_decode_split(DecodeArgs a) {
   float* q_s = (float*)(red + 16);
   float* p_s = q_s + R;
   float* acc = p_s + 64;
-  const T** rows = (const T**)(acc + a.d_c + (a.d_c & 1));  // 8-byte aligned: all sizes above are ints
+  typedef typename std::conditional<F8, uint8_t, T>::type RowT;
+  const RowT** rows = (const RowT**)(acc + a.d_c + (a.d_c & 1));  // 8-byte aligned: all sizes above are ints
 
   const int cap = a.len_cap;
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk, a.ovh_tokens,
@@ -103,17 +110,24 @@ __global__ void __launch_bounds__(64) k_decode_split(DecodeArgs a) {
   for (int c = lane; c < a.d_c; c += 64) acc[c] = 0.f;
   __syncthreads();
   float m = -INFINITY, l = 0.f;
-  const T* pool = (const T*)a.pool;
   const int32_t* bt = a.block_table + (size_t)b * a.max_pages_per_seq;
   for (int tb = t0; tb < t1; tb += 64) {
     const int t = tb + lane;
     const bool valid = t < t1;
-    float s = -INFINITY;
-    const T* row = nullptr;
+    float s = -INFINITY, rscale = 1.f;
+    const RowT* row = nullptr;
     if (valid) {
-      row = pool + ((size_t)bt[t / a.P] * a.P + (t % a.P)) * R;
+      const long long slot = (long long)bt[t / a.P] * a.P + (t % a.P);
       float dot = 0.f;
-      for (int r = 0; r < R; ++r) dot += q_s[r] * ld(row, r);
+      if constexpr (F8) {
+        row = fp8_row(a.pool, slot, a.P, R);
+        rscale = fp8_scale(a.pool, slot, a.P, R);
+        for (int r = 0; r < R; ++r) dot += q_s[r] * e4m3_to_f32(row[r]);
+        dot *= rscale;
+      } else {
+        row = (const T*)a.pool + (size_t)slot * R;
+        for (int r = 0; r < R; ++r) dot += q_s[r] * ld(row, r);
+      }
       s = dot * a.scale_log2;
     }
     float mt = s;
@@ -125,13 +139,17 @@ __global__ void __launch_bounds__(64) k_decode_split(DecodeArgs a) {
     for (int o = 32; o > 0; o >>= 1) ps += __shfl_xor(ps, o);
     l = l * alpha + ps;
     m = m_new;
-    p_s[lane] = p;
+    p_s[lane] = valid ? p * rscale : 0.f;
     rows[lane] = row;
     __syncthreads();
     const int nt = min(64, t1 - tb);
     for (int c = lane; c < a.d_c; c += 64) {
       float v = acc[c] * alpha;
-      for (int k = 0; k < nt; ++k) v += p_s[k] * ld(rows[k], c);
+      if constexpr (F8) {
+        for (int k = 0; k < nt; ++k) v += p_s[k] * e4m3_to_f32(rows[k][c]);
+      } else {
+        for (int k = 0; k < nt; ++k) v += p_s[k] * ld(rows[k], c);
+      }
       acc[c] = v;
     }
     __syncthreads();
@@ -301,6 +319,40 @@ __global__ void __launch_bounds__(128) k_prefill_attn(PrefillArgs a) {
   if (a.lse && tid == 0) a.lse[(size_t)n * a.H + h] = (m + log2f(l)) * kLn2;
 }
 
+// --------------------------------------------------------------------------
+// 8-bit cache rows: one wave per token.  amax = largest |x| of the bf16 row;
+// scale 2^e with e the smallest exponent >= -126 such that amax <= 448 2^e
+// (amax = f 2^k with 1 <= f < 2 and 448 = 1.75 2^8: e = k - 8, plus one when
+// f > 1.75); codes = E4M3 nearest x / 2^e (the hardware conversion rounds to
+// nearest even; x / 2^e is exact), a -0 result stored as +0.
+__global__ void __launch_bounds__(256) k_quantize_rows(const uint16_t* __restrict__ rows,
+                                                       const int64_t* __restrict__ slots, uint8_t* __restrict__ pool8,
+                                                       int n_tokens, int R, int P) {
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (n >= n_tokens) return;
+  const long long slot = slots[n];
+  if (slot < 0) return;
+  const uint16_t* row = rows + (size_t)n * R;
+  float amax = 0.f;
+  for (int c = lane; c < R; c += 64) amax = fmaxf(amax, fabsf(bf16_to_f32(row[c])));
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  int e = 0;
+  if (amax > 0.f) {
+    const uint32_t bits = __float_as_uint(amax);
+    const int k = (int)(bits >> 23) - 127;  // a subnormal amax gives k = -127: clamped below
+    e = max(k - 8 + ((bits & 0x7fffffu) > 0x600000u ? 1 : 0), -126);
+  }
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-126, 120]
+  uint8_t* page = pool8 + (size_t)(slot / P) * fp8_page_bytes(P, R);
+  const int t = (int)(slot % P);
+  for (int c = lane; c < R; c += 64) {
+    uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(bf16_to_f32(row[c]) * inv, 0.f, 0, false) & 0xffu;
+    if (code == 0x80u) code = 0u;
+    page[(size_t)t * R + c] = (uint8_t)code;
+  }
+  if (lane == 0) *(float*)(page + (size_t)P * R + 4 * t) = __uint_as_float((uint32_t)(127 + e) << 23);
+}
+
 inline unsigned blocks_for(long long n, int per) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
@@ -311,6 +363,14 @@ hipError_t write_cache_generic(const WriteCacheArgs& a, bool bf16, hipStream_t s
   if (n == 0) return hipSuccess;
   if (bf16) hipLaunchKernelGGL(k_write_cache<uint16_t>, dim3(blocks_for(n, 256)), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_write_cache<float>, dim3(blocks_for(n, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t quantize_rows_fp8(const uint16_t* rows, const int64_t* slots, void* pool8, int n_tokens, int R, int P,
+                             hipStream_t s) {
+  if (n_tokens == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize_rows, dim3(blocks_for(n_tokens, 4)), dim3(256), 0, s, rows, slots, (uint8_t*)pool8,
+                     n_tokens, R, P);
   return hipGetLastError();
 }
 
@@ -329,7 +389,10 @@ hipError_t decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s) {
                            64 * sizeof(void*) + 8;
   const size_t comb_lds = plan_bytes + (size_t)(a.d_c + 2) * sizeof(float);
   const dim3 g1(a.max_items, a.H), g2(a.batch, a.H);
-  if (bf16) {
+  if (a.fp8) {
+    hipLaunchKernelGGL((k_decode_split<uint16_t, true>), g1, dim3(64), split_lds, s, a);
+    hipLaunchKernelGGL(k_decode_combine<uint16_t>, g2, dim3(128), comb_lds, s, a);
+  } else if (bf16) {
     hipLaunchKernelGGL(k_decode_split<uint16_t>, g1, dim3(64), split_lds, s, a);
     hipLaunchKernelGGL(k_decode_combine<uint16_t>, g2, dim3(128), comb_lds, s, a);
   } else {

@@ -91,7 +91,7 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
       for (int t = 0; t < TB4; ++t) {
         const int n = n0 + 16 * t + m;
         const int nc = min(n, a.n_tokens - 1);
-        const long long sl = a.slots[nc];
+        const long long sl = a.dense ? (long long)nc : a.slots[nc];
         pos[t] = a.positions[nc];
         slot[t] = ((t % NWV) == w && n < a.n_tokens) ? sl : -1;
       }

@@ -14,15 +14,25 @@ namespace {
 
 int elem_bytes(int dtype) { return dtype == MLA_BF16 ? 2 : 4; }
 
+bool fp8_cache(const mla_dims_t* d) { return (d->flags & MLA_FLAG_FP8_CACHE) != 0; }
+
+// bytes of one cached value
+int cache_elem_bytes(const mla_dims_t* d) { return fp8_cache(d) ? 1 : elem_bytes(d->dtype); }
+
 int check_dims(const mla_dims_t* d) {
   if (!d) return MLA_ERR_NULL;
   if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_ERR_DTYPE;
-  if (d->flags != 0 && d->flags != MLA_FLAG_GENERIC) return MLA_ERR_ARG;
+  if (d->flags & ~(MLA_FLAG_GENERIC | MLA_FLAG_FP8_CACHE)) return MLA_ERR_ARG;
   if (d->hidden < 1 || d->num_heads < 1 || d->d_c < 2 || d->d_r < 2 || d->qk_nope < 1 || d->v_head < 1 ||
       d->page_size < 1)
     return MLA_ERR_DIMS;
   if ((d->d_c & 1) || (d->d_r & 1)) return MLA_ERR_DIMS;
   if (!(d->rope_base > 0.f) || !isfinite(d->rope_base) || !isfinite(d->softmax_scale)) return MLA_ERR_ARG;
+  if (fp8_cache(d)) {
+    if (d->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+    // the float32 scales after the rows of a page stay 4-byte aligned
+    if (((long long)d->page_size * (d->d_c + d->d_r)) % 4 != 0) return MLA_ERR_DIMS;
+  }
   return MLA_OK;
 }
 
@@ -55,7 +65,7 @@ bool prefill_fast(const mla_dims_t* d) {
 }
 
 bool decode_fast(const mla_dims_t* d, int batch) {
-  return d->dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC) &&
+  return d->dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC) && !fp8_cache(d) &&
          decode_mfma_supported(d->num_heads, d->d_c, d->d_r, d->v_head, d->page_size, batch);
 }
 
@@ -110,7 +120,18 @@ const char* mla_status_string(int status) {
 
 size_t mla_cache_bytes(const mla_dims_t* dims, int64_t tokens, int32_t layers) {
   if (check_dims(dims) != MLA_OK || tokens < 0 || layers < 0) return 0;
-  return (size_t)layers * (size_t)tokens * (size_t)(dims->d_c + dims->d_r) * (size_t)elem_bytes(dims->dtype);
+  return (size_t)layers * (size_t)tokens * (size_t)(dims->d_c + dims->d_r) * (size_t)cache_elem_bytes(dims);
+}
+
+size_t mla_page_bytes(const mla_dims_t* dims) {
+  if (check_dims(dims) != MLA_OK) return 0;
+  const size_t R = (size_t)(dims->d_c + dims->d_r);
+  return (size_t)dims->page_size * (fp8_cache(dims) ? R + 4 : R * (size_t)elem_bytes(dims->dtype));
+}
+
+size_t mla_write_cache_workspace_size(const mla_dims_t* dims, int32_t n_tokens) {
+  if (check_dims(dims) != MLA_OK || n_tokens < 0) return 0;
+  return fp8_cache(dims) ? (size_t)n_tokens * (size_t)(dims->d_c + dims->d_r) * 2 : 0;
 }
 
 int mla_uses_fast_path(const mla_dims_t* dims, int32_t op) {
@@ -120,23 +141,37 @@ int mla_uses_fast_path(const mla_dims_t* dims, int32_t op) {
     case 0: return write_fast(dims) ? 1 : 0;
     case 1: return absorb_fast(dims) ? 1 : 0;
     case 2: return decode_fast(dims, 1) ? 1 : 0;
-    case 3: return prefill_fast(dims) ? 1 : 0;
+    case 3: return (prefill_fast(dims) && !fp8_cache(dims)) ? 1 : 0;
     default: return MLA_ERR_ARG;
   }
 }
 
-int mla_write_cache(const mla_dims_t* dims, const void* h, const void* w_dkr, const int32_t* positions,
-                    const int64_t* slot_mapping, int32_t n_tokens, void* pool, int32_t num_pages,
-                    hipStream_t stream) {
+int mla_write_cache_ws(const mla_dims_t* dims, const void* h, const void* w_dkr, const int32_t* positions,
+                       const int64_t* slot_mapping, int32_t n_tokens, void* pool, int32_t num_pages, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (n_tokens < 0 || num_pages < 0) return MLA_ERR_ARG;
   if (n_tokens == 0) return MLA_OK;
   if (!h || !w_dkr || !positions || !slot_mapping || !pool) return MLA_ERR_NULL;
-  WriteCacheArgs a{h, w_dkr, positions, slot_mapping, pool, n_tokens, dims->hidden, dims->d_c, dims->d_r,
-                   dims->page_size, dims->rope_base};
-  if (write_fast(dims)) return launched(write_cache_mfma(a, stream));
-  return launched(write_cache_generic(a, dims->dtype == MLA_BF16, stream));
+  const size_t need = mla_write_cache_workspace_size(dims, n_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  const bool f8 = fp8_cache(dims);
+  // 8-bit cache: the bf16 rows go to the workspace (row n at row n), then
+  // each is quantized into its slot
+  WriteCacheArgs a{h, w_dkr, positions, slot_mapping, f8 ? workspace : pool, n_tokens, dims->hidden, dims->d_c,
+                   dims->d_r, dims->page_size, dims->rope_base, f8 ? 1 : 0};
+  hipError_t e = write_fast(dims) ? write_cache_mfma(a, stream)
+                                  : write_cache_generic(a, dims->dtype == MLA_BF16, stream);
+  if (e != hipSuccess || !f8) return launched(e);
+  return launched(quantize_rows_fp8((const uint16_t*)workspace, slot_mapping, pool, n_tokens, dims->d_c + dims->d_r,
+                                    dims->page_size, stream));
+}
+
+int mla_write_cache(const mla_dims_t* dims, const void* h, const void* w_dkr, const int32_t* positions,
+                    const int64_t* slot_mapping, int32_t n_tokens, void* pool, int32_t num_pages,
+                    hipStream_t stream) {
+  return mla_write_cache_ws(dims, h, w_dkr, positions, slot_mapping, n_tokens, pool, num_pages, nullptr, 0, stream);
 }
 
 int mla_absorb_q(const mla_dims_t* dims, const void* q, const void* w_uk, const int32_t* positions,
@@ -198,15 +233,16 @@ int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int3
   a.min_chunk = 256;
   // partial (m, l, acc) written and read back, in cache-row equivalents
   a.ovh_tokens = (int)((2.0 * dims->num_heads * (dims->d_c + 2) * 4.0) /
-                       ((double)(dims->d_c + dims->d_r) * elem_bytes(dims->dtype)));
+                       ((double)(dims->d_c + dims->d_r) * cache_elem_bytes(dims)));
   a.scale_log2 = dims->softmax_scale * kLog2e;
+  a.fp8 = fp8_cache(dims) ? 1 : 0;
   // the MFMA path addresses partials with 32-bit offsets
   if (decode_fast(dims, batch) && L.acc_bytes < ((size_t)1 << 32)) return launched(decode_mfma(a, stream));
   return launched(decode_generic(a, dims->dtype == MLA_BF16, stream));
 }
 
 size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t total_tokens) {
-  if (check_dims(dims) != MLA_OK || total_tokens < 0) return 0;
+  if (check_dims(dims) != MLA_OK || fp8_cache(dims) || total_tokens < 0) return 0;
   return prefill_ws_bytes(dims, total_tokens);
 }
 
@@ -217,6 +253,7 @@ int mla_prefill_kv(const mla_dims_t* dims, const void* q, const void* pool, int3
                    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
+  if (fp8_cache(dims)) return MLA_ERR_DTYPE;  // prefill reads bf16 / fp32 pools only
   if (num_seqs < 0 || total_q < 0 || total_kv < 0 || max_q_len < 0 || max_kv_len < 0 || num_pages < 0 ||
       max_pages_per_seq < 0)
     return MLA_ERR_ARG;

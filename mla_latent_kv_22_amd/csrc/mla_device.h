@@ -28,6 +28,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// ---------------------------------------------------------------- 8-bit cache
+// E4M3 code (low byte) -> float, exact (the two NaN codes give NaN).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false)[0];
+}
+// 8-bit pool page: P rows of R codes, then P float32 row scales.
+__device__ __forceinline__ size_t fp8_page_bytes(int P, int R) { return (size_t)P * (size_t)(R + 4); }
+__device__ __forceinline__ const uint8_t* fp8_row(const void* pool, long long slot, int P, int R) {
+  return (const uint8_t*)pool + (size_t)(slot / P) * fp8_page_bytes(P, R) + (size_t)(slot % P) * R;
+}
+__device__ __forceinline__ float fp8_scale(const void* pool, long long slot, int P, int R) {
+  return *(const float*)((const uint8_t*)pool + (size_t)(slot / P) * fp8_page_bytes(P, R) + (size_t)P * R +
+                         4 * (size_t)(slot % P));
+}
+
 __device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
 __device__ __forceinline__ float ld(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
 __device__ __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }

@@ -25,6 +25,7 @@ struct WriteCacheArgs {
   void* pool;
   int n_tokens, D, d_c, d_r, P;
   float rope_base;
+  int dense;  // 1: row n goes to row n of `pool` (a [n_tokens][R] staging buffer), slots unused
 };
 
 struct AbsorbArgs {
@@ -53,6 +54,7 @@ struct DecodeArgs {
   int max_items;    // capacity of the partial buffers
   int min_chunk, ovh_tokens;
   float scale_log2; // softmax_scale * log2(e)
+  int fp8;          // 1: 8-bit pool (E4M3 rows + float32 row scales per page)
 };
 
 struct PrefillArgs {
@@ -71,10 +73,15 @@ struct PrefillArgs {
   float rope_base, scale;
 };
 
+// 8-bit cache: quantize the bf16 rows of a [n_tokens][R] staging buffer into
+// their slots of an 8-bit pool
+hipError_t quantize_rows_fp8(const uint16_t* rows, const int64_t* slots, void* pool8, int n_tokens, int R, int P,
+                             hipStream_t s);
+
 // generic kernels (any shape, fp32 or bf16 storage)
 hipError_t write_cache_generic(const WriteCacheArgs& a, bool bf16, hipStream_t s);
 hipError_t absorb_generic(const AbsorbArgs& a, bool bf16, hipStream_t s);
-hipError_t decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s);
+hipError_t decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s);  // a.fp8: bf16 queries, 8-bit pool
 hipError_t prefill_generic(const PrefillArgs& a, bool bf16, hipStream_t s);
 
 // MFMA projection kernels (bf16)

@@ -192,6 +192,30 @@ def make(cfg: Config, seed: int = 0, with_rows: bool = True,
                 q=q, q_positions=q_positions, cu_seqlens=cu)
 
 
+def fp8_pages(num_pages: int, P: int, R: int, rng: np.random.Generator) -> np.ndarray:
+    """Random 8-bit cache pages [num_pages, P * (R + 4)] for decode inputs:
+    per page, P rows of R E4M3 codes (random sign, exponent field 4..7 so the
+    values lie between 1/8 and 15/8, any mantissa; one code in 32 is zero and
+    one in 32 a subnormal), then P float32 row scales 2^k with k drawn from
+    -1..1 (stored values of the order of N(0, 1) rows).  A plain random draw
+    of the stored format, not a quantization."""
+    shape = (num_pages, P, R)
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << np.uint8(7)
+    ef = rng.integers(4, 8, size=shape, dtype=np.uint8)
+    mf = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    kind = rng.integers(0, 32, size=shape)
+    ef = np.where(kind == 0, 0, ef).astype(np.uint8)                 # subnormal (or zero when mf = 0)
+    mf = np.where(kind == 1, 0, mf).astype(np.uint8)
+    ef = np.where(kind == 1, 0, ef).astype(np.uint8)                 # zero
+    codes = (sign | (ef << np.uint8(3)) | mf).astype(np.uint8)
+    codes = np.where(codes == 0x80, 0, codes).astype(np.uint8)
+    scales = np.exp2(rng.integers(-1, 2, size=(num_pages, P))).astype("<f4")
+    out = np.empty((num_pages, P * (R + 4)), dtype=np.uint8)
+    out[:, :P * R] = codes.reshape(num_pages, P * R)
+    out[:, P * R:] = scales.view(np.uint8).reshape(num_pages, 4 * P)
+    return out
+
+
 def digest(arrays: Dict[str, np.ndarray]) -> str:
     """sha256 over the raw bytes of every array (determinism check)."""
     m = hashlib.sha256()

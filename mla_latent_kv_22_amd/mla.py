@@ -19,11 +19,12 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 
 F32, BF16 = 0, 1
 FLAG_GENERIC = 1
+FLAG_FP8_CACHE = 2
 OP_WRITE_CACHE, OP_ABSORB_Q, OP_DECODE, OP_PREFILL = 0, 1, 2, 3
 
-_SYMBOLS = ("mla_write_cache", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode",
-            "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_kv", "mla_cache_bytes",
-            "mla_status_string", "mla_uses_fast_path")
+_SYMBOLS = ("mla_write_cache", "mla_write_cache_ws", "mla_write_cache_workspace_size", "mla_absorb_q",
+            "mla_decode_workspace_size", "mla_decode", "mla_prefill_workspace_size", "mla_prefill",
+            "mla_prefill_kv", "mla_cache_bytes", "mla_page_bytes", "mla_status_string", "mla_uses_fast_path")
 
 
 class Dims(ctypes.Structure):
@@ -52,6 +53,11 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         dp = ctypes.POINTER(Dims)
         L.mla_write_cache.argtypes = [dp, vp, vp, vp, vp, i32, vp, i32, vp]
+        L.mla_write_cache_ws.argtypes = [dp, vp, vp, vp, vp, i32, vp, i32, vp, sz, vp]
+        L.mla_write_cache_workspace_size.argtypes = [dp, i32]
+        L.mla_write_cache_workspace_size.restype = sz
+        L.mla_page_bytes.argtypes = [dp]
+        L.mla_page_bytes.restype = sz
         L.mla_absorb_q.argtypes = [dp, vp, vp, vp, i32, vp, vp]
         L.mla_decode_workspace_size.argtypes = [dp, i32, i32]
         L.mla_decode_workspace_size.restype = sz
@@ -66,8 +72,8 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_uses_fast_path.argtypes = [dp, i32]
-        for f in ("mla_write_cache", "mla_absorb_q", "mla_decode", "mla_prefill", "mla_prefill_kv",
-                  "mla_uses_fast_path"):
+        for f in ("mla_write_cache", "mla_write_cache_ws", "mla_absorb_q", "mla_decode", "mla_prefill",
+                  "mla_prefill_kv", "mla_uses_fast_path"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -87,6 +93,11 @@ def make_dims(hidden, num_heads, d_c, d_r, qk_nope, v_head, page_size, dtype, ro
 
 def _torch_dtype(d: Dims):
     return torch.bfloat16 if d.dtype == BF16 else torch.float32
+
+
+def _pool_dtype(d: Dims):
+    """8-bit pools are byte tensors [num_pages, page_bytes]."""
+    return torch.uint8 if d.flags & FLAG_FP8_CACHE else _torch_dtype(d)
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
@@ -114,14 +125,27 @@ def _check(status: int, what: str) -> None:
 
 # --------------------------------------------------------------------------- calls
 
-def write_cache(d: Dims, h, w_dkr, positions, slot_mapping, pool, stream=None) -> None:
+def write_cache(d: Dims, h, w_dkr, positions, slot_mapping, pool, stream=None, workspace=None) -> None:
+    """mla_write_cache, or mla_write_cache_ws when a workspace is given (the
+    8-bit cache needs one: write_cache_workspace_size bytes)."""
     dt = _torch_dtype(d)
     n = 0 if h is None else int(h.shape[0])
     num_pages = int(pool.shape[0])
-    _check(lib().mla_write_cache(ctypes.byref(d), _ptr(h, "h", dt), _ptr(w_dkr, "w_dkr", dt),
-                                 _ptr(positions, "positions", torch.int32),
-                                 _ptr(slot_mapping, "slot_mapping", torch.int64), n,
-                                 _ptr(pool, "pool", dt), num_pages, _stream(stream)), "mla_write_cache")
+    args = (ctypes.byref(d), _ptr(h, "h", dt), _ptr(w_dkr, "w_dkr", dt), _ptr(positions, "positions", torch.int32),
+            _ptr(slot_mapping, "slot_mapping", torch.int64), n, _ptr(pool, "pool", _pool_dtype(d)), num_pages)
+    if workspace is None:
+        _check(lib().mla_write_cache(*args, _stream(stream)), "mla_write_cache")
+    else:
+        _check(lib().mla_write_cache_ws(*args, _ptr(workspace, "workspace", torch.uint8), workspace.numel(),
+                                        _stream(stream)), "mla_write_cache_ws")
+
+
+def write_cache_workspace_size(d: Dims, n_tokens: int) -> int:
+    return int(lib().mla_write_cache_workspace_size(ctypes.byref(d), int(n_tokens)))
+
+
+def page_bytes(d: Dims) -> int:
+    return int(lib().mla_page_bytes(ctypes.byref(d)))
 
 
 def absorb_q(d: Dims, q, w_uk, positions, q_abs, stream=None) -> None:
@@ -138,7 +162,7 @@ def decode_workspace_size(d: Dims, batch: int, max_seq_len: int) -> int:
 def decode(d: Dims, q_abs, pool, block_table, seq_lens, max_seq_len: int, w_uv, out, lse, workspace,
            stream=None) -> None:
     dt = _torch_dtype(d)
-    _check(lib().mla_decode(ctypes.byref(d), _ptr(q_abs, "q_abs", dt), _ptr(pool, "pool", dt),
+    _check(lib().mla_decode(ctypes.byref(d), _ptr(q_abs, "q_abs", dt), _ptr(pool, "pool", _pool_dtype(d)),
                             int(pool.shape[0]), _ptr(block_table, "block_table", torch.int32),
                             int(block_table.shape[1]), _ptr(seq_lens, "seq_lens", torch.int32),
                             int(seq_lens.shape[0]), int(max_seq_len), _ptr(w_uv, "w_uv", dt),

@@ -137,3 +137,34 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         mla.absorb_q(d, torch.zeros(1, 1, 4), torch.zeros(1, 2, 4), torch.zeros(1, dtype=torch.int32),
                      torch.zeros(1, 1, 6))
+
+
+def test_fp8_cache_sizes_and_errors():
+    L = mla.lib()
+    d8 = _dims(flags=mla.FLAG_FP8_CACHE)
+    # page: 64 rows of 576 codes, then 64 float32 scales
+    assert mla.page_bytes(d8) == 64 * (576 + 4)
+    assert mla.page_bytes(_dims()) == 64 * 576 * 2
+    assert mla.page_bytes(_dims(dtype="f32")) == 64 * 576 * 4
+    # one byte per value; the formula leaves the scales out, as the pages' does
+    assert mla.cache_bytes(d8, 8192, 61) == 575668224 // 2
+    assert mla.write_cache_workspace_size(d8, 64) == 64 * 576 * 2
+    assert mla.write_cache_workspace_size(_dims(), 64) == 0
+    # fp8 needs bf16 everywhere else; scales stay 4-byte aligned
+    bad = _dims(flags=mla.FLAG_FP8_CACHE, dtype="f32")
+    assert L.mla_write_cache(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, None) == -3
+    assert L.mla_decode(ctypes.byref(bad), FAKE, FAKE, 4, FAKE, 4, FAKE, 2, 64, FAKE, FAKE, None, FAKE, 1 << 30,
+                        None) == -3
+    assert mla.page_bytes(_dims(flags=mla.FLAG_FP8_CACHE, d_c=4, d_r=2, page_size=3)) == 0
+    # the 8-bit write needs its workspace
+    assert L.mla_write_cache(ctypes.byref(d8), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, None) == -4
+    assert L.mla_write_cache_ws(ctypes.byref(d8), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, FAKE, 4 * 576 * 2 - 1,
+                                None) == -4
+    assert L.mla_write_cache_ws(ctypes.byref(d8), FAKE, FAKE, FAKE, FAKE, 4, None, 4, FAKE, 1 << 20, None) == -1
+    assert L.mla_write_cache_ws(ctypes.byref(d8), None, None, None, None, 0, None, 0, None, 0, None) == 0
+    # prefill does not read an 8-bit pool
+    assert L.mla_prefill(ctypes.byref(d8), FAKE, FAKE, 4, FAKE, 4, FAKE, 2, 64, 64, FAKE, FAKE, FAKE, None, FAKE,
+                         1 << 30, None) == -3
+    assert mla.prefill_workspace_size(d8, 64) == 0
+    assert mla.uses_fast_path(d8, mla.OP_PREFILL) == 0
+    assert mla.uses_fast_path(_dims(flags=mla.FLAG_FP8_CACHE | mla.FLAG_GENERIC), mla.OP_DECODE) == 0
