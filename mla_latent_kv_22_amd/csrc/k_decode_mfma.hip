@@ -548,15 +548,387 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
   }
 }
 
+// ============================================================================
+// 8-bit cache (MLA_FLAG_FP8_CACHE: E4M3 codes, one float32 power-of-two scale
+// per row).  Same plan, item loop, ring of four stages and step order as
+// k_split; what changes is the tile and how its operands are read:
+//   * a tile is 32 rows of 576 codes (18432 bytes) plus the 32 row scales
+//     (two 128-byte copies): 18 wave-wide row loads and one scale load;
+//   * score operand: 8 codes of one row per lane (ds_read_b64), converted to
+//     bf16 with that row's scale (v_cvt_scalef32_pk_bf16_fp8; exact, the
+//     scale is a power of two), so the scores are those of the stored values;
+//   * latent operand: 8 codes of one feature for 8 tokens through the 8-bit
+//     LDS transpose read (ds_read_b64_tr_b8), converted with scale 1; the row
+//     scale rides with the numerator instead: P^T holds p 2^e (exact), while
+//     the softmax sum takes p itself.
+// Tile layout: 9 column groups of 64 codes; group cg holds 32 rows x 64 bytes
+// with 16-byte chunk slots XOR-swizzled by bits 2 and 3 of the row:
+//   byte(r, c) = 2048 (c >> 2) + 64 r + 16 ((c & 3) ^ swz8(r))
+// A transpose read (rows {0..3, 8..11} + 4 j, two chunks per 32 lanes) then
+// hits every bank once; a score read (32 rows of one chunk, 8 bytes each)
+// needs two passes, the least its 8-byte width allows.
+constexpr int T8_ROWS = TT * RW;            // 18432 bytes of codes
+constexpr int T8_SCALES = T8_ROWS;          // two 128-byte copies of the row scales
+constexpr int TILE8_BYTES = T8_ROWS + 256;  // 18688
+constexpr int LOADS8 = T8_ROWS / 1024;      // 18 wave-wide row loads
+__device__ __forceinline__ int swz8(int r) { return (((r >> 3) & 1) << 1) | ((r >> 2) & 1); }
+
+// loads per wave per tile: row loads i = w, w + NW, ... < 18, plus scale
+// loads so that every wave issues the same count (the tile waits count loads)
+template <int NW>
+struct Load8 {
+  static constexpr int LPW = NW == 4 ? 5 : (NW == 2 ? 10 : 19);
+  // with four waves, waves 2 and 3 (four row loads each) load the scales
+  static __device__ __forceinline__ bool scales(int w) { return NW == 4 ? w >= 2 : true; }
+  static __device__ __forceinline__ int copy(int w) { return NW == 4 ? w - 2 : w; }
+};
+
+// source byte offset of lane `lane` in row load i (row half rh = i & 1),
+// relative to the tile's first row
+__device__ __forceinline__ uint32_t load8_lane_off(int lane, int rh) {
+  const int r = 16 * rh + (lane >> 2);
+  return (uint32_t)(r * RW + (((lane & 3) ^ swz8(r)) << 4));
+}
+
+// Load i fills LDS bytes [1024 i, +1024) = column group i >> 1, rows
+// 16 (i & 1) .. +15: lane l takes row 16 (i & 1) + l / 4 and the chunk whose
+// swizzled slot is l % 4.  The scale load uses lanes 0-7 (128 bytes).
+template <int NW>
+__device__ __forceinline__ void issue_tile8(const char* __restrict__ rows, const char* __restrict__ scales, int nvalid,
+                                            uint32_t lds0, int w, int lane, const uint32_t* lane_off) {
+  if (nvalid == TT) {
+#pragma unroll
+    for (int i0 = 0; i0 < LOADS8; i0 += NW) {
+      const int i = i0 + w;
+      if (i < LOADS8) dma16<0>(rows + 64 * (i >> 1), lane_off[i & 1], lds0 + 1024 * i);
+    }
+  } else {
+    // ragged tail: rows past the last valid token repeat it (their p is 0)
+#pragma unroll
+    for (int i0 = 0; i0 < LOADS8; i0 += NW) {
+      const int i = i0 + w;
+      if (i < LOADS8) {
+        const int r = 16 * (i & 1) + (lane >> 2);
+        const int rr = r < nvalid ? r : nvalid - 1;
+        const uint32_t off = (uint32_t)(rr * RW + 64 * (i >> 1) + (((lane & 3) ^ swz8(r)) << 4));
+        dma16<0>(rows, off, lds0 + 1024 * i);
+      }
+    }
+  }
+  if (Load8<NW>::scales(w) && lane < 8) dma16<0>(scales, 16u * lane, lds0 + T8_SCALES + 128 * Load8<NW>::copy(w));
+}
+
+struct ReadOffsets8 {
+  int s[4];  // score operand (row lane % 32, chunk ks, half g): + 2048 (ks / 4)
+  int t[2];  // transpose reads [fb parity]: + 2048 (fb / 2) + 1024 kk
+};
+
+// 8 E4M3 codes -> 8 bf16 values times sc (a power of two: exact)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 v, float sc) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, true);
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
+}
+
+// The score MFMAs are inline asm, so the compiler's hazard checks do not see
+// them.  A VALU write of a VGPR that an MFMA then reads as a source needs
+// wait states the hardware does not insert (without them the scores of the
+// pipelined tiles came out wrong); the converted operand passes through
+// five of them before the MFMA that reads it.
+__device__ __forceinline__ void valu_to_mfma(u32x4& v) { asm volatile("s_nop 4" : "+v"(v)); }
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// Latent update of one tile from an 8-bit tile (op order and P^T reads as
+// tile_step); with SCORES the 36 score MFMAs of the next tile (ts, lane row
+// scale ksc) are interleaved one for one.
+template <int NW, bool SCORES>
+__device__ __forceinline__ void tile_step8(f32x16& sacc, const char* ts, float ksc, const u32x4* qf, f32x16* acc,
+                                           const char* tp, const char* pbuf, int w, const ReadOffsets8& o,
+                                           const ReadOffsets& op) {
+  using S = Split<NW>;
+  constexpr int PF = 3;
+  u32x2 kf[PF];
+  if constexpr (SCORES) {
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x2*)(ts + o.s[ks & 3] + 2048 * (ks >> 2));
+  }
+  auto tr_a = [&](int kk, int fbl) {
+    const int fb = S::FBW * w + fbl;
+    const u32x2 v = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tp + o.t[fb & 1] + 2048 * (fb >> 1) + 1024 * kk)));
+    return fp8x8_to_bf16(v, 1.f);
+  };
+  auto p_frag = [&](int kk, int hb) { return *(const u32x4*)(pbuf + 2048 * hb + op.p[kk]); };
+  u32x4 af[2], pf[S::HB];
+  af[0] = tr_a(0, 0);
+#pragma unroll
+  for (int hb = 0; hb < S::HB; ++hb) pf[hb] = p_frag(0, hb);
+  constexpr int NOPS = SCORES ? KS : S::NPC;
+#pragma unroll
+  for (int c = 0; c < NOPS; ++c) {
+    if constexpr (SCORES) {
+      u32x4 cur = fp8x8_to_bf16(kf[c % PF], ksc);
+      valu_to_mfma(cur);
+      if (c + PF < KS) kf[c % PF] = *(const u32x2*)(ts + o.s[(c + PF) & 3] + 2048 * ((c + PF) >> 2));
+      if (c == 0) score_first(sacc, cur, qf[c]);
+      else score_next(sacc, cur, qf[c]);
+    }
+    if (c < S::NPC) {
+      const int kk = c / (S::FBW * S::HB), fbl = (c / S::HB) % S::FBW, hb = c % S::HB;
+      const int grp = c / S::HB;
+      if (hb == 0 && grp + 1 < 2 * S::FBW) af[(grp + 1) & 1] = tr_a((grp + 1) / S::FBW, (grp + 1) % S::FBW);
+      const u32x4 bv = pf[hb];
+      if (kk == 0 && fbl == S::FBW - 1) pf[hb] = p_frag(1, hb);
+      acc[fbl * S::HB + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[grp & 1]), as_bf16x8(bv),
+                                                                      acc[fbl * S::HB + hb], 0, 0, 0);
+    }
+  }
+  if constexpr (SCORES) score_drain(sacc);
+}
+
+// Softmax numerators of an 8-bit tile for head lane % 32: p = 2^(s sl2 - m_ref),
+// the sum takes bf16(p), P^T takes bf16(p) times the token's row scale.
+// scl: the tile's row scales in LDS.  Tokens at or past t1 get p = 0.
+template <bool MAYBE_RAGGED>
+__device__ __forceinline__ void tile_softmax8(const f32x16& sacc, int tok0, int t1, int g, float sl2, float m_ref,
+                                              char* pbuf, int head_off, float& lsum, const ReadOffsets& o,
+                                              const char* scl) {
+  const bool full = !MAYBE_RAGGED || tok0 + TT <= t1;
+  f32x4 sc4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sc4[q] = *(const f32x4*)(scl + 4 * (8 * q + 4 * g));
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    uint32_t wds[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int j = 8 * kk + e;
+      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], sl2, -m_ref));
+      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j + 1], sl2, -m_ref));
+      float s0 = sc4[j >> 2][j & 3], s1 = sc4[j >> 2][(j & 3) + 1];
+      if (!full) {
+        const int t = 8 * (j >> 2) + 4 * g + (j & 3);
+        if (tok0 + t >= t1) p0 = s0 = 0.f;
+        if (tok0 + t + 1 >= t1) p1 = s1 = 0.f;
+      }
+      const uint32_t pk = pack_bf16x2(p0, p1);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                             lsum, false);
+      // bf16(p) 2^e = bf16(p 2^e): the scale is a power of two
+      wds[e >> 1] = pack_bf16x2(p0 * s0, p1 * s1);
+    }
+    *(u32x4*)(pbuf + head_off + o.p[kk]) = u32x4{wds[0], wds[1], wds[2], wds[3]};
+  }
+}
+
+// LDS map of k_split8: four tile stages of 18688 bytes, the two P^T buffers,
+// then the planner's per-sequence arrays.
+constexpr int LDS8_PBUF = NSTAGE * TILE8_BYTES;            // 74752
+constexpr int LDS8_PLAN = LDS8_PBUF + 2 * PBUF_BYTES;      // 91136
+constexpr int LDS8_BYTES = LDS8_PLAN + PLAN_INTS * 4;
+static_assert(LDS8_BYTES <= 163840, "LDS budget");
+
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
+  using S = Split<NW>;
+  __shared__ __attribute__((aligned(16))) char smem[LDS8_BYTES];
+  char* tiles = smem;
+  char* pbufs = smem + LDS8_PBUF;
+  int* s_len = (int*)(smem + LDS8_PLAN);
+  int* s_items = s_len + (kMaxDecodeBatch + 1);
+  int* red = s_items + (kMaxDecodeBatch + 1);
+
+  const int cap = a.len_cap;
+  const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
+                                           a.ovh_tokens, s_len, s_items, red);
+  const int n_items = plan.n_items;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i <= a.batch; i += blockDim.x) a.plan[i] = s_items[i];
+    for (int i = threadIdx.x; i < a.batch; i += blockDim.x) a.plan[a.batch + 1 + i] = s_len[i];
+    if (threadIdx.x == 0) a.plan[2 * a.batch + 1] = plan.chunk;
+  }
+  const int G = gridDim.x;
+  const int rounds = (int)blockIdx.x < n_items ? (n_items - 1 - (int)blockIdx.x) / G + 1 : 0;
+  int d_item = 0, d_b = 0, d_t0 = 0, d_t1 = 0;
+  if (lane < rounds) {
+    const int idx = blockIdx.x + lane * G;
+    const int item = ((n_items & 7) == 0 && (G & 7) == 0) ? (idx & 7) * (n_items >> 3) + (idx >> 3) : idx;
+    const int b = item_seq(s_items, a.batch, item);
+    d_item = item;
+    d_b = b;
+    d_t0 = (item - s_items[b]) * plan.chunk;
+    d_t1 = min(s_len[b], d_t0 + plan.chunk);
+  }
+
+  const int g = lane >> 5, hl = lane & 31;
+  const int hq = w * 32 + hl;
+  const bool hvalid = hq < a.H;
+  const int P = a.P;
+  const size_t page8 = (size_t)P * (RW + 4);
+  const char* __restrict__ pool = (const char*)a.pool;
+  const uint32_t lds_tiles = lds_addr_of(tiles);
+  uint32_t lane_off[2];
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh) lane_off[rh] = load8_lane_off(lane, NW == 1 ? rh : (w & 1));
+  ReadOffsets8 r8;
+  ReadOffsets ro;
+  {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r8.s[q] = 64 * hl + 16 * (q ^ swz8(hl)) + 8 * g;
+    const int grp = lane >> 4, s = lane & 15, e = s >> 1;
+    const int trow = 8 * (e >> 2) + 4 * (grp >> 1) + (e & 3);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) r8.t[par] = 64 * trow + 16 * ((2 * par + (grp & 1)) ^ swz8(trow)) + 8 * (s & 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) ro.p[kk] = p_off(hl, kk, g);
+  }
+  const int head_off = 2048 * w;
+  const float sl2 = a.scale_log2;
+  constexpr int LPW = Load8<NW>::LPW;
+  __syncthreads();  // planner arrays read
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int item = __builtin_amdgcn_readlane(d_item, rd);
+    const int b = __builtin_amdgcn_readlane(d_b, rd);
+    const int t0 = __builtin_amdgcn_readlane(d_t0, rd);
+    const int t1 = __builtin_amdgcn_readlane(d_t1, rd);
+    const __attribute__((address_space(4))) int32_t* btb =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_table + (size_t)b * a.max_pages_per_seq);
+    const int ntiles = (t1 - t0 + TT - 1) / TT;
+    auto tile_src = [&](int tile, int& nvalid, const char*& scales) {
+      const int tok0 = t0 + tile * TT;
+      nvalid = min(TT, t1 - tok0);
+      const char* pg = pool + (size_t)btb[tok0 / P] * page8;
+      scales = pg + (size_t)P * RW + 4 * (tok0 % P);
+      return pg + (size_t)(tok0 % P) * RW;
+    };
+    auto stage = [&](int tile) { return tiles + (tile & 3) * TILE8_BYTES; };
+    // lane row scale of a tile for the score operand (1 for rows past the end)
+    auto row_scale = [&](int tile) {
+      const float sc = *(const float*)(stage(tile) + T8_SCALES + 4 * hl);
+      return t0 + tile * TT + hl < t1 ? sc : 1.f;
+    };
+
+    u32x4 qf[KS];
+    {
+      const char* qb = (const char*)a.q_abs + (size_t)b * a.H * (RW * 2);
+      uint32_t qo = (uint32_t)((hvalid ? hq : 0) * (RW * 2) + 16 * g);
+      asm volatile("" : "+v"(qo));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = *(const u32x4*)(qb + qo + 32 * ks);
+        qf[ks] = hvalid ? v : u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+      if (st < ntiles) {
+        int nv;
+        const char* sc;
+        const char* tp = tile_src(st, nv, sc);
+        issue_tile8<NW>(tp, sc, nv, lds_tiles + st * TILE8_BYTES, w, lane, lane_off);
+      }
+    }
+
+    f32x16 acc[FB];
+#pragma unroll
+    for (int i = 0; i < FB; ++i) acc[i] = f32x16{};
+    float lsum = 0.f;
+
+    if (ntiles >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW));
+    else if (ntiles == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    f32x16 sacc;
+    {
+      constexpr int PF = 3;
+      const float ksc = row_scale(0);
+      u32x2 kf[PF];
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x2*)(tiles + r8.s[ks & 3] + 2048 * (ks >> 2));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 cur = fp8x8_to_bf16(kf[ks % PF], ksc);
+        valu_to_mfma(cur);
+        if (ks + PF < KS) kf[ks % PF] = *(const u32x2*)(tiles + r8.s[(ks + PF) & 3] + 2048 * ((ks + PF) >> 2));
+        if (ks == 0) score_first(sacc, cur, qf[ks]);
+        else score_next(sacc, cur, qf[ks]);
+      }
+      score_drain(sacc);
+    }
+    const float m_ref = tile_max(sacc, t0, t1, g) * sl2;
+    if (ntiles > 1) tile_softmax8<false>(sacc, t0, t1, g, sl2, m_ref, pbufs, head_off, lsum, ro, tiles + T8_SCALES);
+    else tile_softmax8<true>(sacc, t0, t1, g, sl2, m_ref, pbufs, head_off, lsum, ro, tiles + T8_SCALES);
+
+    auto step_sync = [&](int it) {
+      int nv3 = 0;
+      const char* sc3 = nullptr;
+      const char* tp3 = (it + 3 < ntiles) ? tile_src(it + 3, nv3, sc3) : nullptr;
+      if (it + 2 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (it + 3 < ntiles) issue_tile8<NW>(tp3, sc3, nv3, lds_tiles + ((it + 3) & 3) * TILE8_BYTES, w, lane, lane_off);
+    };
+    int it = 0;
+    for (; it + 2 < ntiles; ++it) {
+      step_sync(it);
+      tile_step8<NW, true>(sacc, stage(it + 1), row_scale(it + 1), qf, acc, stage(it), pbufs + (it & 1) * PBUF_BYTES,
+                           w, r8, ro);
+      tile_softmax8<false>(sacc, t0 + (it + 1) * TT, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES,
+                           head_off, lsum, ro, stage(it + 1) + T8_SCALES);
+    }
+    if (it + 1 < ntiles) {
+      step_sync(it);
+      tile_step8<NW, true>(sacc, stage(it + 1), row_scale(it + 1), qf, acc, stage(it), pbufs + (it & 1) * PBUF_BYTES,
+                           w, r8, ro);
+      tile_softmax8<true>(sacc, t0 + (it + 1) * TT, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES,
+                          head_off, lsum, ro, stage(it + 1) + T8_SCALES);
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    tile_step8<NW, false>(sacc, tiles, 1.f, qf, acc, stage(ntiles - 1), pbufs + ((ntiles - 1) & 1) * PBUF_BYTES, w,
+                          r8, ro);
+
+    lsum += __shfl_xor(lsum, 32);
+    const bool overflow = !(lsum < 0x1p100f);
+    if (hvalid && g == 0) {
+      a.part_ml[((size_t)item * a.H + hq) * 2 + 0] = overflow ? INFINITY : m_ref;
+      a.part_ml[((size_t)item * a.H + hq) * 2 + 1] = lsum;
+    }
+#pragma unroll
+    for (int fbl = 0; fbl < S::FBW; ++fbl)
+#pragma unroll
+      for (int hb = 0; hb < S::HB; ++hb) {
+        const int h = 32 * hb + hl;
+        if (h >= a.H) continue;
+        float* pa = a.part_acc + ((size_t)item * a.H + h) * DC + 32 * (S::FBW * w + fbl) + 4 * g;
+        const f32x16& v = acc[fbl * S::HB + hb];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(f32x4*)(pa + 8 * q4) = f32x4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+      }
+    __syncthreads();
+  }
+}
+
 // --------------------------------------------------------------------------
 // Exact two-pass partial (m, l, acc) of one (item, head) in fp32, used only for
 // partials the split pass flagged.  scratch: >= 576 + 256 floats of LDS.
 // The arguments are plain values (no pointer to the kernel's argument block,
 // which would force that block into scratch memory in the caller).
-__device__ __noinline__ void recompute_partial(const uint16_t* __restrict__ pool, const int32_t* __restrict__ bt,
+// f8: the pool is 8-bit (row values E4M3(code) * row scale).
+__device__ __noinline__ void recompute_partial(const void* __restrict__ pool, const int32_t* __restrict__ bt,
                                                const uint16_t* __restrict__ qa, float* __restrict__ pa,
                                                float* __restrict__ pml, int P, float scale_log2, int t0, int t1,
-                                               float* scratch, int* red) {
+                                               float* scratch, int* red, int f8) {
   // blockDim.x in {256, 512}: thread tid keeps latent columns tid (+ blockDim.x)
   const int nth = blockDim.x;
   float* q = scratch;          // 576
@@ -565,10 +937,15 @@ __device__ __noinline__ void recompute_partial(const uint16_t* __restrict__ pool
   __syncthreads();
   for (int f = tid; f < RW; f += nth) q[f] = bf16_to_f32(qa[f]);
   __syncthreads();
+  // value f of token t's row
+  auto val = [&](int t, int f) {
+    const long long slot = (long long)bt[t / P] * P + t % P;
+    return f8 ? e4m3_to_f32(fp8_row(pool, slot, P, RW)[f]) * fp8_scale(pool, slot, P, RW)
+              : bf16_to_f32(((const uint16_t*)pool)[(size_t)slot * RW + f]);
+  };
   auto score = [&](int t) {
-    const uint16_t* row = pool + ((size_t)bt[t / P] * P + t % P) * RW;
     float d = 0.f;
-    for (int f = 0; f < RW; ++f) d += q[f] * bf16_to_f32(row[f]);
+    for (int f = 0; f < RW; ++f) d += q[f] * val(t, f);
     return d * scale_log2;
   };
   float m = -INFINITY;
@@ -588,11 +965,10 @@ __device__ __noinline__ void recompute_partial(const uint16_t* __restrict__ pool
     const int nt = min(nth, t1 - tb);
     for (int k = 0; k < nt; ++k) {
       const int tt = tb + k;
-      const uint16_t* row = pool + ((size_t)bt[tt / P] * P + tt % P) * RW;
       const float pk = p[k];
       l += pk;  // every thread keeps the full sum
-      acc0 += pk * bf16_to_f32(row[c0]);
-      if (c1 < DC) acc1 += pk * bf16_to_f32(row[c1]);
+      acc0 += pk * val(tt, c0);
+      if (c1 < DC) acc1 += pk * val(tt, c1);
     }
   }
   pa[c0] = acc0;
@@ -700,9 +1076,9 @@ __global__ void __launch_bounds__(64 * CNW, 4) k_combine(DecodeArgs a) {
         const int t0 = (i - s_items[bl]) * s_chunk;
         const int t1 = min(s_len[bl], t0 + s_chunk);
         const size_t ih = (size_t)i * a.H + h;
-        recompute_partial((const uint16_t*)a.pool, a.block_table + (size_t)b * a.max_pages_per_seq,
+        recompute_partial(a.pool, a.block_table + (size_t)b * a.max_pages_per_seq,
                           (const uint16_t*)a.q_abs + ((size_t)b * a.H + h) * RW, a.part_acc + ih * DC,
-                          a.part_ml + ih * 2, a.P, a.scale_log2, t0, t1, (float*)lat_hi, red);
+                          a.part_ml + ih * 2, a.P, a.scale_log2, t0, t1, (float*)lat_hi, red, a.fp8);
       }
     }
     __syncthreads();
@@ -795,10 +1171,18 @@ int decode_mfma_grid(int slots, int max_items) {
 hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   const dim3 g1(decode_mfma_grid(a.slots, a.max_items));
-  switch (split_waves(a.H)) {
-    case 1: hipLaunchKernelGGL(k_split<1>, g1, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_split<2>, g1, dim3(128), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_split<4>, g1, dim3(256), 0, s, a); break;
+  if (a.fp8) {
+    switch (split_waves(a.H)) {
+      case 1: hipLaunchKernelGGL(k_split8<1>, g1, dim3(64), 0, s, a); break;
+      case 2: hipLaunchKernelGGL(k_split8<2>, g1, dim3(128), 0, s, a); break;
+      default: hipLaunchKernelGGL(k_split8<4>, g1, dim3(256), 0, s, a); break;
+    }
+  } else {
+    switch (split_waves(a.H)) {
+      case 1: hipLaunchKernelGGL(k_split<1>, g1, dim3(64), 0, s, a); break;
+      case 2: hipLaunchKernelGGL(k_split<2>, g1, dim3(128), 0, s, a); break;
+      default: hipLaunchKernelGGL(k_split<4>, g1, dim3(256), 0, s, a); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

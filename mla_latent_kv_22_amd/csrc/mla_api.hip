@@ -65,7 +65,7 @@ bool prefill_fast(const mla_dims_t* d) {
 }
 
 bool decode_fast(const mla_dims_t* d, int batch) {
-  return d->dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC) && !fp8_cache(d) &&
+  return d->dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC) &&
          decode_mfma_supported(d->num_heads, d->d_c, d->d_r, d->v_head, d->page_size, batch);
 }
 
