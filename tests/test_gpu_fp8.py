@@ -143,3 +143,107 @@ def test_fp8_decode_parity(cfg, flags, lens):
     e_o, e_l = rel_err(out, o_ref), lse_err(lse, l_ref)
     print(f"  fast={mla.uses_fast_path(d, mla.OP_DECODE)} out rel err {e_o:.3e}  lse err {e_l:.3e}", flush=True)
     assert e_o < TOL["bf16"] and e_l < TOL["bf16"]
+
+
+def _e4m3_code(v):
+    """Code of an exactly representable E4M3 magnitude v (test constant)."""
+    codes = np.arange(0x7F)
+    vals = O.e4m3_value(codes)
+    return int(codes[np.argmin(np.abs(vals - v))])
+
+
+@pytest.mark.parametrize("flags,mag,scale", [(0, 448.0, 2.0), (mla.FLAG_GENERIC, 448.0, 2.0), (0, 5.0, 1.0)],
+                         ids=["mfma_flagged", "generic", "mfma_below_bound"])
+def test_fp8_score_spike_far_above_first_tile(flags, mag, scale):
+    """One 8-bit row of sequence 1, signed like head 0's absorbed query, with
+    magnitude mag times its row scale: at 448 x 2 its score lies thousands
+    (log2 units) above the rest of its work item, so the split pass flags the
+    (item, head) and the combine recomputes it from the 8-bit rows; at 5 x 1
+    (about 90 above) it is computed in place with huge numerators."""
+    need_gpu()
+    _case(f"fp8 score spike flags={flags} mag={mag} scale={scale}")
+    cfg = I.scaled(I.RAGGED, batch=3, seq_len=2100, min_seq_len=1)
+    lens = [700, 2100, 64]
+    rng = np.random.default_rng(31)
+    inp = I.make(cfg, 31, with_rows=False, lengths=lens)
+    P, R = cfg.page_size, cfg.row_width
+    pages = I.fp8_pages(int(inp["num_pages"]), P, R, rng)
+    q = O.from_storage(inp["q"], "bf16")
+    qa = O.absorb_query(q, O.from_storage(inp["w_uk"], "bf16"), inp["q_positions"], cfg.qk_nope, cfg.rope_base)
+    code = _e4m3_code(mag)
+    row = np.where(qa[1, 0] >= 0, code, code | 0x80).astype(np.uint8)
+    t_spike = 1000
+    pg, off = int(inp["block_table"][1, t_spike // P]), t_spike % P
+    pages[pg, off * R:(off + 1) * R] = row
+    pages[pg, P * R + 4 * off:P * R + 4 * off + 4] = np.array([scale], "<f4").view(np.uint8)
+    st = harness.DecodeStep(cfg, inp, flags=flags | mla.FLAG_FP8_CACHE, pool=torch.from_numpy(pages).to("cuda"))
+    st.absorb()
+    st.attend()
+    torch.cuda.synchronize()
+    out = O.from_storage(harness.to_host_bits(st.out), "bf16")
+    lse = st.lse.cpu().numpy().astype(np.float64)
+    o_ref, l_ref = O.decode(q, O.fp8_pool_values(pages, P, R), inp["block_table"], inp["seq_lens"],
+                            O.from_storage(inp["w_uk"], "bf16"), O.from_storage(inp["w_uv"], "bf16"), cfg.d_c,
+                            cfg.softmax_scale, cfg.rope_base)
+    e_o, e_l = rel_err(out, o_ref), lse_err(lse, l_ref)
+    print(f"  out rel err {e_o:.3e}  lse err {e_l:.3e}", flush=True)
+    assert e_o < TOL["bf16"] and e_l < TOL["bf16"]
+
+
+def test_fp8_page_permutation_bit_invariance_and_determinism():
+    need_gpu()
+    _case("fp8 page permutation invariance")
+    cfg = I.scaled(I.RAGGED, batch=6, seq_len=3000, min_seq_len=200)
+    rng = np.random.default_rng(41)
+    inp = I.make(cfg, 41, with_rows=False)
+    P, R = cfg.page_size, cfg.row_width
+    pages = I.fp8_pages(int(inp["num_pages"]), P, R, rng)
+    st = harness.DecodeStep(cfg, inp, flags=mla.FLAG_FP8_CACHE, pool=torch.from_numpy(pages).to("cuda"))
+    assert mla.uses_fast_path(st.d, mla.OP_DECODE) == 1
+    st.absorb()
+    st.attend()
+    torch.cuda.synchronize()
+    out1, lse1 = harness.to_host_bits(st.out).copy(), st.lse.cpu().numpy().copy()
+    st.attend()
+    torch.cuda.synchronize()
+    assert np.array_equal(harness.to_host_bits(st.out), out1), "two runs differ"
+    perm = np.random.default_rng(9).permutation(pages.shape[0])
+    moved = np.empty_like(pages)
+    moved[perm] = pages
+    st.block_table = harness.to_device(perm[inp["block_table"]].astype(np.int32), "i32")
+    st.attend(pool=torch.from_numpy(moved).to("cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(harness.to_host_bits(st.out), out1), "page placement changed the result"
+    assert np.array_equal(st.lse.cpu().numpy(), lse1)
+
+
+@pytest.mark.slow
+def test_fp8_decode_v3_full_size():
+    """B=64, T=8192, H=128 over random 8-bit pages, in the launch
+    configuration the benchmark times: sequence 0 over all heads and
+    sequence 63 over 16 heads against the oracle."""
+    need_gpu()
+    _case("fp8 decode v3 full size")
+    cfg = I.V3
+    rng = np.random.default_rng(51)
+    inp = I.make(cfg, 51, with_rows=False)
+    P, R = cfg.page_size, cfg.row_width
+    pages = I.fp8_pages(int(inp["num_pages"]), P, R, rng)
+    st = harness.DecodeStep(cfg, inp, flags=mla.FLAG_FP8_CACHE, pool=torch.from_numpy(pages).to("cuda"))
+    st.absorb()
+    st.attend()
+    torch.cuda.synchronize()
+    out = O.from_storage(harness.to_host_bits(st.out), "bf16")
+    lse = st.lse.cpu().numpy().astype(np.float64)
+    q = O.from_storage(inp["q"], "bf16")
+    w_uk, w_uv = O.from_storage(inp["w_uk"], "bf16"), O.from_storage(inp["w_uv"], "bf16")
+    for b, heads in ((0, None), (63, list(range(0, 128, 8)))):
+        L = int(inp["seq_lens"][b])
+        codes, scales = O.unpack_fp8_pages(pages[inp["block_table"][b, : (L + P - 1) // P]], P, R)
+        rows = O.dequantize_rows_fp8(codes, scales).reshape(-1, R)[:L]
+        o_ref, l_ref = O.decode_one(q[b], rows, w_uk, w_uv, L - 1, cfg.d_c, cfg.softmax_scale, cfg.rope_base,
+                                    heads=heads)
+        hs = list(range(cfg.num_heads)) if heads is None else heads
+        e_o, e_l = rel_err(out[b, hs], o_ref[hs]), lse_err(lse[b, hs], l_ref[hs])
+        print(f"  seq {b}: out rel err {e_o:.3e}  lse err {e_l:.3e}", flush=True)
+        assert e_o < TOL["bf16"] and e_l < TOL["bf16"]
