@@ -554,9 +554,16 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
 // k_split; what changes is the tile and how its operands are read:
 //   * a tile is 32 rows of 576 codes (18432 bytes) plus the 32 row scales
 //     (two 128-byte copies): 18 wave-wide row loads and one scale load;
-//   * score operand: 8 codes of one row per lane (ds_read_b64), converted to
-//     bf16 with that row's scale (v_cvt_scalef32_pk_bf16_fp8; exact, the
-//     scale is a power of two), so the scores are those of the stored values;
+//   * scores: the block-scaled 8-bit MFMA (v_mfma_scale_f32_32x32x64_f8f6f4)
+//     takes the codes straight from LDS, 32 per lane (64 features per step),
+//     with the row scale as the A-side scale (an E8M0 byte is the exponent
+//     field of the float32 scale); the absorbed query enters as two E4M3
+//     parts, hi = E4M3(q / 2^e) and lo = E4M3((q - hi 2^e) / 2^(e-4)), with
+//     one exponent e per head (the smallest with max |q| <= 448 2^e).  The
+//     bf16 query has 8 significant bits; hi holds the top 4 and lo the rest,
+//     so hi 2^e + lo 2^(e-4) reproduces it except for elements some 2^13
+//     below the head's largest, and 18 MFMAs (hi and lo for 9 steps) give
+//     the scores of the stored values;
 //   * latent operand: 8 codes of one feature for 8 tokens through the 8-bit
 //     LDS transpose read (ds_read_b64_tr_b8), converted with scale 1; the row
 //     scale rides with the numerator instead: P^T holds p 2^e (exact), while
@@ -565,8 +572,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
 // with 16-byte chunk slots XOR-swizzled by bits 2 and 3 of the row:
 //   byte(r, c) = 2048 (c >> 2) + 64 r + 16 ((c & 3) ^ swz8(r))
 // A transpose read (rows {0..3, 8..11} + 4 j, two chunks per 32 lanes) then
-// hits every bank once; a score read (32 rows of one chunk, 8 bytes each)
-// needs two passes, the least its 8-byte width allows.
+// hits every bank once, and so does each 16-byte score read (16 rows, one
+// chunk slot each).
 constexpr int T8_ROWS = TT * RW;            // 18432 bytes of codes
 constexpr int T8_SCALES = T8_ROWS;          // two 128-byte copies of the row scales
 constexpr int TILE8_BYTES = T8_ROWS + 256;  // 18688
@@ -619,76 +626,111 @@ __device__ __forceinline__ void issue_tile8(const char* __restrict__ rows, const
 }
 
 struct ReadOffsets8 {
-  int s[4];  // score operand (row lane % 32, chunk ks, half g): + 2048 (ks / 4)
+  int s[2];  // score operand: row lane % 32, chunks 2 g and 2 g + 1 of the step's group: + 2048 kb
   int t[2];  // transpose reads [fb parity]: + 2048 (fb / 2) + 1024 kk
 };
 
-// 8 E4M3 codes -> 8 bf16 values times sc (a power of two: exact)
-__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 v, float sc) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, true);
+// 8 E4M3 codes -> 8 bf16 values (exact)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 v) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.f, true);
   return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
                __builtin_bit_cast(uint32_t, d)};
 }
 
-// The score MFMAs are inline asm, so the compiler's hazard checks do not see
-// them.  A VALU write of a VGPR that an MFMA then reads as a source needs
-// wait states the hardware does not insert (without them the scores of the
-// pipelined tiles came out wrong); the converted operand passes through
-// five of them before the MFMA that reads it.
-__device__ __forceinline__ void valu_to_mfma(u32x4& v) { asm volatile("s_nop 4" : "+v"(v)); }
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int KB8 = RW / 64;  // 9 score steps of 64 features
+
+// Score MFMAs of the 8-bit path, inline asm like score_first / score_next
+// (the accumulator stays in VGPRs).  a: 32 codes of the lane's row, b: 32
+// codes of the lane's head, sa / sb: E8M0 scale bytes (bits 0-7).
+__device__ __forceinline__ void score8_first(f32x16& acc, const i32x8& a, const i32x8& b, int sa, int sb) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+               : "=&v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+__device__ __forceinline__ void score8_next(f32x16& acc, const i32x8& a, const i32x8& b, int sa, int sb) {
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+// A VALU result read by an asm MFMA needs wait states the compiler does not
+// add for asm (without them the scores of pipelined tiles came out wrong):
+// the per-tile A-side scale passes through five before its first MFMA.
+__device__ __forceinline__ void valu_to_mfma(int& v) { asm volatile("s_nop 4" : "+v"(v)); }
+
+// 32 codes of one row for score step kb (two 16-byte chunks)
+__device__ __forceinline__ i32x8 kfrag8(const char* ts, const ReadOffsets8& o, int kb) {
+  const u32x4 x = *(const u32x4*)(ts + o.s[0] + 2048 * kb);
+  const u32x4 y = *(const u32x4*)(ts + o.s[1] + 2048 * kb);
+  return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+}
+
+// 18 chained score MFMAs of one tile: for each step the hi then the lo part.
+// The next step's fragment is read into the same registers once both MFMAs
+// of a step have issued (they read their operands at issue).
+__device__ __forceinline__ void score_tile8(f32x16& sacc, const char* ts, const ReadOffsets8& o, const i32x8* qh,
+                                            const i32x8* ql, int sa, int sbh, int sbl) {
+  i32x8 kf = kfrag8(ts, o, 0);
+#pragma unroll
+  for (int kb = 0; kb < KB8; ++kb) {
+    if (kb == 0) score8_first(sacc, kf, qh[kb], sa, sbh);
+    else score8_next(sacc, kf, qh[kb], sa, sbh);
+    score8_next(sacc, kf, ql[kb], sa, sbl);
+    if (kb + 1 < KB8) kf = kfrag8(ts, o, kb + 1);
+  }
+  score_drain(sacc);
+}
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 // Latent update of one tile from an 8-bit tile (op order and P^T reads as
-// tile_step); with SCORES the 36 score MFMAs of the next tile (ts, lane row
-// scale ksc) are interleaved one for one.
+// tile_step).  With SCORES the 18 score MFMAs of the next tile (ts) run
+// first and the latent MFMAs fill the wait for each step's operands.
 template <int NW, bool SCORES>
-__device__ __forceinline__ void tile_step8(f32x16& sacc, const char* ts, float ksc, const u32x4* qf, f32x16* acc,
-                                           const char* tp, const char* pbuf, int w, const ReadOffsets8& o,
-                                           const ReadOffsets& op) {
+__device__ __forceinline__ void tile_step8(f32x16& sacc, const char* ts, int sa, const i32x8* qh, const i32x8* ql,
+                                           int sbh, int sbl, f32x16* acc, const char* tp, const char* pbuf, int w,
+                                           const ReadOffsets8& o, const ReadOffsets& op) {
   using S = Split<NW>;
-  constexpr int PF = 3;
-  u32x2 kf[PF];
-  if constexpr (SCORES) {
-#pragma unroll
-    for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x2*)(ts + o.s[ks & 3] + 2048 * (ks >> 2));
-  }
   auto tr_a = [&](int kk, int fbl) {
     const int fb = S::FBW * w + fbl;
     const u32x2 v = __builtin_bit_cast(
         u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(tp + o.t[fb & 1] + 2048 * (fb >> 1) + 1024 * kk)));
-    return fp8x8_to_bf16(v, 1.f);
+    return fp8x8_to_bf16(v);
   };
   auto p_frag = [&](int kk, int hb) { return *(const u32x4*)(pbuf + 2048 * hb + op.p[kk]); };
   u32x4 af[2], pf[S::HB];
   af[0] = tr_a(0, 0);
 #pragma unroll
   for (int hb = 0; hb < S::HB; ++hb) pf[hb] = p_frag(0, hb);
-  constexpr int NOPS = SCORES ? KS : S::NPC;
+  i32x8 kf;
+  if constexpr (SCORES) kf = kfrag8(ts, o, 0);
+  auto pv = [&](int c) {
+    const int kk = c / (S::FBW * S::HB), fbl = (c / S::HB) % S::FBW, hb = c % S::HB;
+    const int grp = c / S::HB;
+    if (hb == 0 && grp + 1 < 2 * S::FBW) af[(grp + 1) & 1] = tr_a((grp + 1) / S::FBW, (grp + 1) % S::FBW);
+    const u32x4 bv = pf[hb];
+    if (kk == 0 && fbl == S::FBW - 1) pf[hb] = p_frag(1, hb);
+    acc[fbl * S::HB + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[grp & 1]), as_bf16x8(bv),
+                                                                    acc[fbl * S::HB + hb], 0, 0, 0);
+  };
+  if constexpr (SCORES) {
+    // score step kb (two MFMAs) followed by latent MFMAs kb * NPC / KB8 ..
 #pragma unroll
-  for (int c = 0; c < NOPS; ++c) {
-    if constexpr (SCORES) {
-      u32x4 cur = fp8x8_to_bf16(kf[c % PF], ksc);
-      valu_to_mfma(cur);
-      if (c + PF < KS) kf[c % PF] = *(const u32x2*)(ts + o.s[(c + PF) & 3] + 2048 * ((c + PF) >> 2));
-      if (c == 0) score_first(sacc, cur, qf[c]);
-      else score_next(sacc, cur, qf[c]);
+    for (int kb = 0; kb < KB8; ++kb) {
+      if (kb == 0) score8_first(sacc, kf, qh[kb], sa, sbh);
+      else score8_next(sacc, kf, qh[kb], sa, sbh);
+      score8_next(sacc, kf, ql[kb], sa, sbl);
+      if (kb + 1 < KB8) kf = kfrag8(ts, o, kb + 1);
+#pragma unroll
+      for (int c = kb * S::NPC / KB8; c < (kb + 1) * S::NPC / KB8; ++c) pv(c);
     }
-    if (c < S::NPC) {
-      const int kk = c / (S::FBW * S::HB), fbl = (c / S::HB) % S::FBW, hb = c % S::HB;
-      const int grp = c / S::HB;
-      if (hb == 0 && grp + 1 < 2 * S::FBW) af[(grp + 1) & 1] = tr_a((grp + 1) / S::FBW, (grp + 1) % S::FBW);
-      const u32x4 bv = pf[hb];
-      if (kk == 0 && fbl == S::FBW - 1) pf[hb] = p_frag(1, hb);
-      acc[fbl * S::HB + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[grp & 1]), as_bf16x8(bv),
-                                                                      acc[fbl * S::HB + hb], 0, 0, 0);
-    }
+    score_drain(sacc);
+  } else {
+#pragma unroll
+    for (int c = 0; c < S::NPC; ++c) pv(c);
   }
-  if constexpr (SCORES) score_drain(sacc);
 }
 
 // Softmax numerators of an 8-bit tile for head lane % 32: p = 2^(s sl2 - m_ref),
@@ -780,7 +822,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
   ReadOffsets ro;
   {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r8.s[q] = 64 * hl + 16 * (q ^ swz8(hl)) + 8 * g;
+    for (int h2 = 0; h2 < 2; ++h2) r8.s[h2] = 64 * hl + 16 * ((2 * g + h2) ^ swz8(hl));
     const int grp = lane >> 4, s = lane & 15, e = s >> 1;
     const int trow = 8 * (e >> 2) + 4 * (grp >> 1) + (e & 3);
 #pragma unroll
@@ -809,22 +851,74 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
       return pg + (size_t)(tok0 % P) * RW;
     };
     auto stage = [&](int tile) { return tiles + (tile & 3) * TILE8_BYTES; };
-    // lane row scale of a tile for the score operand (1 for rows past the end)
+    // E8M0 scale byte of the lane's row in a tile (the exponent field of the
+    // float32 power of two; 127 = 1 for rows past the end)
     auto row_scale = [&](int tile) {
-      const float sc = *(const float*)(stage(tile) + T8_SCALES + 4 * hl);
-      return t0 + tile * TT + hl < t1 ? sc : 1.f;
+      const uint32_t bits = *(const uint32_t*)(stage(tile) + T8_SCALES + 4 * hl);
+      int sa = t0 + tile * TT + hl < t1 ? (int)((bits >> 23) & 0xffu) : 127;
+      valu_to_mfma(sa);
+      return sa;
     };
 
-    u32x4 qf[KS];
+    // absorbed query of head hq: features 64 kb + 32 g + 8 j .. +7 (bf16) for
+    // kb = 0..8, j = 0..3, split into the E4M3 parts hi and lo; a first pass
+    // over the loads finds the head maximum, the second converts
+    i32x8 qh[KB8], ql[KB8];
+    int sbh, sbl;
     {
       const char* qb = (const char*)a.q_abs + (size_t)b * a.H * (RW * 2);
-      uint32_t qo = (uint32_t)((hvalid ? hq : 0) * (RW * 2) + 16 * g);
+      uint32_t qo = (uint32_t)((hvalid ? hq : 0) * (RW * 2) + 64 * g);
       asm volatile("" : "+v"(qo));
+      auto qload = [&](int kb, int j) {
+        const u32x4 v = *(const u32x4*)(qb + qo + 128 * kb + 16 * j);
+        return hvalid ? v : u32x4{0, 0, 0, 0};
+      };
+      // head maximum over both lane halves -> exponent e (smallest with
+      // amax <= 448 2^e, at least -123 so that e - 4 stays an E8M0 value)
+      float amax = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 v = *(const u32x4*)(qb + qo + 32 * ks);
-        qf[ks] = hvalid ? v : u32x4{0, 0, 0, 0};
+      for (int kb = 0; kb < KB8; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 v = qload(kb, j);
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2)
+            amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(v[e2] << 16)), fabsf(__uint_as_float(v[e2] & 0xffff0000u))));
+        }
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      int e = 0;
+      if (amax > 0.f) {
+        const uint32_t bits = __float_as_uint(amax);
+        e = max((int)(bits >> 23) - 127 - 8 + ((bits & 0x7fffffu) > 0x600000u ? 1 : 0), -123);
       }
+      const float inv_hi = __uint_as_float((uint32_t)(127 - e) << 23);      // 2^-e
+      const float inv_lo = __uint_as_float((uint32_t)(127 - e + 4) << 23);  // 2^(4-e)
+      const float sc_hi = __uint_as_float((uint32_t)(127 + e) << 23);       // 2^e
+#pragma unroll
+      for (int kb = 0; kb < KB8; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 v = qload(kb, j);
+#pragma unroll
+          for (int p2 = 0; p2 < 2; ++p2) {
+            const uint32_t u0 = v[2 * p2], u1 = v[2 * p2 + 1];
+            const float x0 = __uint_as_float(u0 << 16), x1 = __uint_as_float(u0 & 0xffff0000u);
+            const float x2 = __uint_as_float(u1 << 16), x3 = __uint_as_float(u1 & 0xffff0000u);
+            int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0 * inv_hi, x1 * inv_hi, 0, false);
+            h = __builtin_amdgcn_cvt_pk_fp8_f32(x2 * inv_hi, x3 * inv_hi, h, true);
+            const f32x2 d01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false), d23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+            // residuals are exact: bf16 minus its top 4 significant bits
+            int l = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - d01[0] * sc_hi) * inv_lo, (x1 - d01[1] * sc_hi) * inv_lo, 0,
+                                                    false);
+            l = __builtin_amdgcn_cvt_pk_fp8_f32((x2 - d23[0] * sc_hi) * inv_lo, (x3 - d23[1] * sc_hi) * inv_lo, l,
+                                                true);
+            qh[kb][2 * j + p2] = h;
+            ql[kb][2 * j + p2] = l;
+          }
+        }
+      }
+      sbh = 127 + e;
+      sbl = 127 + e - 4;
     }
 #pragma unroll
     for (int st = 0; st < 3; ++st) {
@@ -847,22 +941,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     f32x16 sacc;
-    {
-      constexpr int PF = 3;
-      const float ksc = row_scale(0);
-      u32x2 kf[PF];
-#pragma unroll
-      for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x2*)(tiles + r8.s[ks & 3] + 2048 * (ks >> 2));
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 cur = fp8x8_to_bf16(kf[ks % PF], ksc);
-        valu_to_mfma(cur);
-        if (ks + PF < KS) kf[ks % PF] = *(const u32x2*)(tiles + r8.s[(ks + PF) & 3] + 2048 * ((ks + PF) >> 2));
-        if (ks == 0) score_first(sacc, cur, qf[ks]);
-        else score_next(sacc, cur, qf[ks]);
-      }
-      score_drain(sacc);
-    }
+    score_tile8(sacc, tiles, r8, qh, ql, row_scale(0), sbh, sbl);
     const float m_ref = tile_max(sacc, t0, t1, g) * sl2;
     if (ntiles > 1) tile_softmax8<false>(sacc, t0, t1, g, sl2, m_ref, pbufs, head_off, lsum, ro, tiles + T8_SCALES);
     else tile_softmax8<true>(sacc, t0, t1, g, sl2, m_ref, pbufs, head_off, lsum, ro, tiles + T8_SCALES);
@@ -880,22 +959,22 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
     int it = 0;
     for (; it + 2 < ntiles; ++it) {
       step_sync(it);
-      tile_step8<NW, true>(sacc, stage(it + 1), row_scale(it + 1), qf, acc, stage(it), pbufs + (it & 1) * PBUF_BYTES,
-                           w, r8, ro);
+      tile_step8<NW, true>(sacc, stage(it + 1), row_scale(it + 1), qh, ql, sbh, sbl, acc, stage(it),
+                           pbufs + (it & 1) * PBUF_BYTES, w, r8, ro);
       tile_softmax8<false>(sacc, t0 + (it + 1) * TT, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES,
                            head_off, lsum, ro, stage(it + 1) + T8_SCALES);
     }
     if (it + 1 < ntiles) {
       step_sync(it);
-      tile_step8<NW, true>(sacc, stage(it + 1), row_scale(it + 1), qf, acc, stage(it), pbufs + (it & 1) * PBUF_BYTES,
-                           w, r8, ro);
+      tile_step8<NW, true>(sacc, stage(it + 1), row_scale(it + 1), qh, ql, sbh, sbl, acc, stage(it),
+                           pbufs + (it & 1) * PBUF_BYTES, w, r8, ro);
       tile_softmax8<true>(sacc, t0 + (it + 1) * TT, t1, g, sl2, m_ref, pbufs + ((it + 1) & 1) * PBUF_BYTES,
                           head_off, lsum, ro, stage(it + 1) + T8_SCALES);
     }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    tile_step8<NW, false>(sacc, tiles, 1.f, qf, acc, stage(ntiles - 1), pbufs + ((ntiles - 1) & 1) * PBUF_BYTES, w,
-                          r8, ro);
+    tile_step8<NW, false>(sacc, tiles, 127, qh, ql, sbh, sbl, acc, stage(ntiles - 1),
+                          pbufs + ((ntiles - 1) & 1) * PBUF_BYTES, w, r8, ro);
 
     lsum += __shfl_xor(lsum, 32);
     const bool overflow = !(lsum < 0x1p100f);

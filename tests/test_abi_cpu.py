@@ -168,3 +168,5 @@ def test_fp8_cache_sizes_and_errors():
     assert mla.prefill_workspace_size(d8, 64) == 0
     assert mla.uses_fast_path(d8, mla.OP_PREFILL) == 0
     assert mla.uses_fast_path(_dims(flags=mla.FLAG_FP8_CACHE | mla.FLAG_GENERIC), mla.OP_DECODE) == 0
+    assert mla.uses_fast_path(d8, mla.OP_DECODE) == 1
+    assert mla.uses_fast_path(d8, mla.OP_WRITE_CACHE) == 1
