@@ -150,6 +150,48 @@ def prefill_leg(steps=5):
                         "tflops": round(c_tf, 1), "mfma_frac_of_bf16_peak": round(c_tf / BF16_PEAK_TFLOPS, 4)}}
 
 
+def fp8_leg(steps=20):
+    """The same decode step over the 8-bit cache (MLA_FLAG_FP8_CACHE): random
+    E4M3 pages with power-of-two row scales, the step's B new rows quantized
+    by the cache write.  Cache bytes per token: 576 codes + 4 scale bytes."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_22_amd import harness, inputs as I, mla
+    cfg = I.V3
+    inp = I.make(cfg, 0, with_rows=False)
+    pages = I.fp8_pages(int(inp["num_pages"]), cfg.page_size, cfg.row_width, np.random.default_rng(0))
+    st = harness.DecodeStep(cfg, inp, flags=mla.FLAG_FP8_CACHE, pool=torch.from_numpy(pages).to("cuda"))
+    pools = [st.pool, st.pool.clone()]
+    ws = torch.empty(mla.write_cache_workspace_size(st.d, cfg.batch), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def write(i):
+        mla.write_cache(st.d, st.h, st.w_dkr, st.positions, st.slots, pools[i % 2], workspace=ws)
+
+    def timed(fn, n):
+        for i in range(3):
+            fn(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    dec_ms = timed(lambda i: st.attend(pool=pools[i % 2]), steps)
+    step_ms = timed(lambda i: (write(i), st.absorb(), st.attend(pool=pools[i % 2])), steps)
+    tokens = int(np.sum(inp["seq_lens"].astype(np.int64)))
+    cache_bytes = tokens * (cfg.row_width + 4)
+    return {"workload": f"{cfg.name} over an 8-bit cache: B={cfg.batch} T={cfg.seq_len} H={cfg.num_heads}, "
+                        f"E4M3 rows + float32 row scales, page={cfg.page_size}",
+            "cache_bytes_per_call": cache_bytes,
+            "decode_ms": round(dec_ms, 5), "decode_gbs": round(cache_bytes / (dec_ms * 1e-3) / 1e9, 1),
+            "decode_tokens_per_s": round(cfg.batch / (dec_ms * 1e-3), 1),
+            "step_ms": round(step_ms, 5), "step_tokens_per_s": round(cfg.batch / (step_ms * 1e-3), 1),
+            "launch": "eager, one stream"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +200,7 @@ def main():
     ap.add_argument("--workload", default="v3_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache leg")
     ap.add_argument("--no-graph", action="store_true", help="launch the step's kernels eagerly")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -170,6 +213,11 @@ def main():
     from mla_latent_kv_22_amd import harness, inputs as I, mla
 
     mla.lib()
+    if args.workload == "v3_decode_fp8":
+        # 8-bit cache leg only (profiling runs): one JSON line
+        print(json.dumps({"metric": "MLA decode over an 8-bit latent cache", "n_gpus": 1, **fp8_leg(args.steps)}),
+              flush=True)
+        return
     cfg = I.CONFIGS[args.workload]
     if cfg.prefill:
         # prefill only (profiling runs): one JSON line for the prefill leg
@@ -276,6 +324,8 @@ def main():
     }
     if not args.no_prefill:
         res["prefill"] = prefill_leg()
+    if not args.no_fp8:
+        res["fp8_cache"] = fp8_leg()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, inp)
