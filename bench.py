@@ -179,6 +179,7 @@ def fp8_leg(steps=20):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    st.absorb()
     dec_ms = timed(lambda i: st.attend(pool=pools[i % 2]), steps)
     step_ms = timed(lambda i: (write(i), st.absorb(), st.attend(pool=pools[i % 2])), steps)
     tokens = int(np.sum(inp["seq_lens"].astype(np.int64)))
