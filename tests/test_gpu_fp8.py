@@ -66,11 +66,12 @@ def test_fp8_write_one_hot_is_bit_exact(flags):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("flags", [0, mla.FLAG_GENERIC], ids=["mfma_rows", "generic_rows"])
-def test_fp8_write_random_rows_within_half_step(flags):
+@pytest.mark.parametrize("flags,seq_len", [(0, 300), (mla.FLAG_GENERIC, 300), (0, 700)],
+                         ids=["mfma_rows", "generic_rows", "mfma_rows_2100_tokens"])
+def test_fp8_write_random_rows_within_half_step(flags, seq_len):
     need_gpu()
-    _case(f"fp8 write random rows flags={flags}")
-    cfg = I.scaled(I.PREFILL, hidden=512, batch=3, seq_len=300)
+    _case(f"fp8 write random rows flags={flags} seq_len={seq_len}")
+    cfg = I.scaled(I.PREFILL, hidden=512, batch=3, seq_len=seq_len)
     inp = I.make(cfg, 13)
     slots = inp["slots"].copy()
     slots[::7] = -1
