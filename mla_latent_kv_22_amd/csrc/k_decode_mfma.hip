@@ -1060,16 +1060,20 @@ __device__ __noinline__ void recompute_partial(const void* __restrict__ pool, co
 }
 
 // --------------------------------------------------------------------------
-// combine: grid (H, ceil(batch / 16)), 512 threads (8 waves).  Work-group
-// (h, sequences b0 .. b0+15): merge the partials of every item of those
+// combine: grid (H, ceil(batch / CB)), 512 threads (8 waves).  Work-group
+// (h, sequences b0 .. b0+CB-1): merge the partials of every item of those
 // sequences into the latent output (fp32), then o = W_UV,h lat with MFMA.
-constexpr int CB = 16;   // sequences per combine work-group
+// CB = 16 with CNB = 2 item loads in flight per sequence when the grid fills
+// the GPU; for small H x batch (few work-groups, many items per sequence)
+// CB = 4 with CNB = 8 gives four times the work-groups and a quarter of the
+// dependent load rounds.
 constexpr int CNW = 8;   // waves per combine work-group
-constexpr int CNB = 2;   // items per sequence whose loads are in flight together
+template <int CB, int CNB>
 __global__ void __launch_bounds__(64 * CNW, 4) k_combine(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lat_hi[CB * DC];  // [seq][512], 16-byte slot p ^ seq
-  __shared__ __attribute__((aligned(16))) uint16_t lat_lo[CB * DC];
-  __shared__ __attribute__((aligned(16))) uint16_t o_st[CB * 256];   // output rows (d_v <= 256)
+  constexpr int CBR = CB > 16 ? CB : 16;  // rows of the W_UV product (16-row MFMA blocks)
+  __shared__ __attribute__((aligned(16))) uint16_t lat_hi[CBR * DC];  // [seq][512], 16-byte slot p ^ seq
+  __shared__ __attribute__((aligned(16))) uint16_t lat_lo[CBR * DC];
+  __shared__ __attribute__((aligned(16))) uint16_t o_st[CBR * 256];   // output rows (d_v <= 256)
   __shared__ int s_items[CB + 1], s_len[CB];
   __shared__ int red[16];
   __shared__ int s_chunk;
@@ -1265,7 +1269,10 @@ hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_combine, dim3(a.H, (a.batch + CB - 1) / CB), dim3(64 * CNW), 0, s, a);
+  if ((long long)a.H * ((a.batch + 15) / 16) >= 2LL * a.slots)
+    hipLaunchKernelGGL((k_combine<16, 2>), dim3(a.H, (a.batch + 15) / 16), dim3(64 * CNW), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_combine<4, 8>), dim3(a.H, (a.batch + 3) / 4), dim3(64 * CNW), 0, s, a);
   return hipGetLastError();
 }
 
