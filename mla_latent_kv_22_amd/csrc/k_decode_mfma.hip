@@ -549,6 +549,174 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
 }
 
 // ============================================================================
+// Few heads (H <= 32): k_split's work-group is a single wave, and with the
+// four-stage ring holding all of a CU's LDS only one SIMD of four would work.
+// k_split2s keeps two 36 KiB stages (74 KiB with its P^T buffer), so two
+// work-groups share a CU.  Its loop is not pipelined across tiles: tile it
+// is scored, its numerators written and its latent update done in one step
+// while tile it+1 loads into the other stage; tile it+2 is requested once
+// the step has read its stage.  Plan, item loop, operands, softmax and the
+// partials are those of k_split.
+constexpr int LDS2S_BYTES = 2 * TILE_BYTES + PBUF_BYTES / 4;
+static_assert(PLAN_INTS * 4 <= TILE_BYTES, "planner arrays must fit in one stage");
+
+__global__ void __launch_bounds__(64, 1) k_split2s(DecodeArgs a) {
+  using S = Split<1>;
+  __shared__ __attribute__((aligned(16))) char smem[LDS2S_BYTES];
+  char* tiles = smem;
+  char* pbuf = smem + 2 * TILE_BYTES;
+  int* s_len = (int*)(tiles + TILE_BYTES);
+  int* s_items = s_len + (kMaxDecodeBatch + 1);
+  int* red = s_items + (kMaxDecodeBatch + 1);
+
+  const int cap = a.len_cap;
+  const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
+                                           a.ovh_tokens, s_len, s_items, red);
+  const int n_items = plan.n_items;
+  const int lane = threadIdx.x & 63;
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i <= a.batch; i += blockDim.x) a.plan[i] = s_items[i];
+    for (int i = threadIdx.x; i < a.batch; i += blockDim.x) a.plan[a.batch + 1 + i] = s_len[i];
+    if (threadIdx.x == 0) a.plan[2 * a.batch + 1] = plan.chunk;
+  }
+  const int G = gridDim.x;
+  const int rounds = (int)blockIdx.x < n_items ? (n_items - 1 - (int)blockIdx.x) / G + 1 : 0;
+  int d_item = 0, d_b = 0, d_t0 = 0, d_t1 = 0;
+  if (lane < rounds) {
+    const int idx = blockIdx.x + lane * G;
+    const int item = ((n_items & 7) == 0 && (G & 7) == 0) ? (idx & 7) * (n_items >> 3) + (idx >> 3) : idx;
+    const int b = item_seq(s_items, a.batch, item);
+    d_item = item;
+    d_b = b;
+    d_t0 = (item - s_items[b]) * plan.chunk;
+    d_t1 = min(s_len[b], d_t0 + plan.chunk);
+  }
+  __syncthreads();  // the planner arrays in stage 1 are not read after this point
+
+  const int g = lane >> 5, hl = lane & 31;
+  const bool hvalid = hl < a.H;
+  const int P = a.P;
+  const char* __restrict__ pool = (const char*)a.pool;
+  const uint32_t lds_tiles = lds_addr_of(tiles);
+  uint32_t lane_off[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) lane_off[rb] = load_lane_off(lane, rb);
+  ReadOffsets ro;
+  {
+    const int sw = swz(hl);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ro.s[q] = 128 * hl + 16 * ((2 * q + g) ^ sw);
+    const int grp = lane >> 4, jl = lane & 15;
+    const int trow = 4 * g + (jl >> 2);
+    const int tchunk = 2 * (grp & 1) + ((jl >> 1) & 1);
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        ro.t[par][hf] = 128 * trow + 16 * ((4 * par + tchunk) ^ swz(trow + 8 * hf)) + 8 * (jl & 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) ro.p[kk] = p_off(hl, kk, g);
+  }
+  const float sl2 = a.scale_log2;
+  constexpr int LPW = LOADS_PER_TILE;  // one wave issues all 36 loads of a tile
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int item = __builtin_amdgcn_readlane(d_item, rd);
+    const int b = __builtin_amdgcn_readlane(d_b, rd);
+    const int t0 = __builtin_amdgcn_readlane(d_t0, rd);
+    const int t1 = __builtin_amdgcn_readlane(d_t1, rd);
+    const __attribute__((address_space(4))) int32_t* btb =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_table + (size_t)b * a.max_pages_per_seq);
+    const int ntiles = (t1 - t0 + TT - 1) / TT;
+    auto tile_ptr = [&](int tile, int& nvalid) {
+      const int tok0 = t0 + tile * TT;
+      nvalid = min(TT, t1 - tok0);
+      const int page = btb[tok0 / P];
+      return pool + ((size_t)page * P + (tok0 % P)) * (RW * 2);
+    };
+
+    u32x4 qf[KS];
+    {
+      const char* qb = (const char*)a.q_abs + (size_t)b * a.H * (RW * 2);
+      uint32_t qo = (uint32_t)((hvalid ? hl : 0) * (RW * 2) + 16 * g);
+      asm volatile("" : "+v"(qo));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = *(const u32x4*)(qb + qo + 32 * ks);
+        qf[ks] = hvalid ? v : u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (st < ntiles) {
+        int nv;
+        const char* tp = tile_ptr(st, nv);
+        issue_tile<1>(tp, nv, lds_tiles + st * TILE_BYTES, 0, lane, lane_off);
+      }
+    }
+
+    f32x16 acc[FB];
+#pragma unroll
+    for (int i = 0; i < FB; ++i) acc[i] = f32x16{};
+    float lsum = 0.f, m_ref = 0.f;
+    f32x16 sacc;
+
+    for (int it = 0; it < ntiles; ++it) {
+      // tile it landed (tile it+1's loads may remain)
+      if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      asm volatile("" ::: "memory");
+      const char* cur = tiles + (it & 1) * TILE_BYTES;
+      const int tok0 = t0 + it * TT;
+      {
+        constexpr int PF = 3;
+        u32x4 kf[PF];
+#pragma unroll
+        for (int ks = 0; ks < PF; ++ks) kf[ks] = *(const u32x4*)(cur + ro.s[ks & 3] + 4096 * (ks >> 2));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 c = kf[ks % PF];
+          if (ks + PF < KS) kf[ks % PF] = *(const u32x4*)(cur + ro.s[(ks + PF) & 3] + 4096 * ((ks + PF) >> 2));
+          if (ks == 0) score_first(sacc, c, qf[ks]);
+          else score_next(sacc, c, qf[ks]);
+        }
+        score_drain(sacc);
+      }
+      if (it == 0) m_ref = tile_max(sacc, t0, t1, g) * sl2;  // fixed for the whole item
+      if (tok0 + TT <= t1) tile_softmax<false>(sacc, tok0, t1, g, sl2, m_ref, pbuf, 0, lsum, ro);
+      else tile_softmax<true>(sacc, tok0, t1, g, sl2, m_ref, pbuf, 0, lsum, ro);
+      tile_step<1, false>(sacc, cur, qf, acc, cur, pbuf, 0, ro);
+      // every LDS read of this stage (and of the P^T buffer) has returned
+      // before the next tile's loads may overwrite it
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      if (it + 2 < ntiles) {
+        int nv;
+        const char* tp = tile_ptr(it + 2, nv);
+        issue_tile<1>(tp, nv, lds_tiles + (it & 1) * TILE_BYTES, 0, lane, lane_off);
+      }
+    }
+
+    lsum += __shfl_xor(lsum, 32);
+    const bool overflow = !(lsum < 0x1p100f);
+    if (hvalid && g == 0) {
+      a.part_ml[((size_t)item * a.H + hl) * 2 + 0] = overflow ? INFINITY : m_ref;
+      a.part_ml[((size_t)item * a.H + hl) * 2 + 1] = lsum;
+    }
+#pragma unroll
+    for (int fbl = 0; fbl < S::FBW; ++fbl) {
+      if (!hvalid) continue;
+      float* pa = a.part_acc + ((size_t)item * a.H + hl) * DC + 32 * fbl + 4 * g;
+      const f32x16& v = acc[fbl];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(f32x4*)(pa + 8 * q4) = f32x4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+    }
+    __syncthreads();
+  }
+}
+
+// ============================================================================
 // 8-bit cache (MLA_FLAG_FP8_CACHE: E4M3 codes, one float32 power-of-two scale
 // per row).  Same plan, item loop, ring of four stages and step order as
 // k_split; what changes is the tile and how its operands are read:
@@ -1240,10 +1408,10 @@ bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch) {
 // waves per split work-group: 32 heads each, and 16 / NW latent feature blocks
 static int split_waves(int H) { return H <= 32 ? 1 : (H <= 64 ? 2 : 4); }
 
-int decode_mfma_slots(int H, int cus) {
-  // the split kernel holds the whole LDS of a CU: one work-group per CU
-  (void)H;
-  return cus;
+int decode_mfma_slots(int H, int cus, bool fp8) {
+  // the split kernels hold a CU's whole LDS (one work-group per CU), except
+  // the few-heads bf16 kernel, two of which share a CU
+  return (!fp8 && split_waves(H) == 1) ? 2 * cus : cus;
 }
 
 int decode_mfma_grid(int slots, int max_items) {
@@ -1262,7 +1430,7 @@ hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s) {
     }
   } else {
     switch (split_waves(a.H)) {
-      case 1: hipLaunchKernelGGL(k_split<1>, g1, dim3(64), 0, s, a); break;
+      case 1: hipLaunchKernelGGL(k_split2s, g1, dim3(64), 0, s, a); break;
       case 2: hipLaunchKernelGGL(k_split<2>, g1, dim3(128), 0, s, a); break;
       default: hipLaunchKernelGGL(k_split<4>, g1, dim3(256), 0, s, a); break;
     }

@@ -80,7 +80,7 @@ struct DecodeLayout {
 bool decode_layout(const mla_dims_t* d, int batch, int max_seq_len, DecodeLayout& L) {
   const int cus = current_cus();
   if (cus <= 0) return false;
-  L.slots = decode_fast(d, batch) ? decode_mfma_slots(d->num_heads, cus) : cus;
+  L.slots = decode_fast(d, batch) ? decode_mfma_slots(d->num_heads, cus, fp8_cache(d)) : cus;
   const long long by_len = ((long long)batch * max_seq_len + kMaxChunk - 1) / kMaxChunk;
   const long long base = (long long)kMaxChunksPerSlot * L.slots;
   L.max_items = (int)((by_len > base ? by_len : base) + batch);

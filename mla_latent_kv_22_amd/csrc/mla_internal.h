@@ -92,7 +92,7 @@ hipError_t absorb_mfma(const AbsorbArgs& a, hipStream_t s);
 
 // MFMA decode kernels (bf16, latent width 512, rotary width 64)
 bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch);
-int decode_mfma_slots(int H, int cus);
+int decode_mfma_slots(int H, int cus, bool fp8);
 hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s);
 // MFMA prefill: d_n = d_v = 128, d_R = 64, bf16; workspace K_C and V as bf16 [H][total][128]
 bool prefill_mfma_supported(int d_n, int d_v, int d_r, int d_c, int P);
