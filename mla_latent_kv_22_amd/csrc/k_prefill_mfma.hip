@@ -120,33 +120,38 @@ __global__ void __launch_bounds__(256, 2) k_prefill_proj(PrefillArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const char* st = smem + (kc & 1) * XSTAGE;
-    const int ra = 32 * w + r32;  // A row: token
+    const int ra = 32 * w + r32;  // B column: token
 #pragma unroll
     for (int ks = 0; ks < XK / 16; ++ks) {
       const int c = 2 * ks + g;
       const u32x4 av = *(const u32x4*)(st + ra * 128 + 16 * xslot(ra, c));
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
-        const int rb = 32 * jt + r32;  // B column: output j (weight row)
+        const int rb = 32 * jt + r32;  // A row: output j (weight row)
         const u32x4 bv = *(const u32x4*)(st + XT * 128 + rb * 128 + 16 * xslot(rb, c));
-        acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), acc[jt], 0, 0, 0);
+        acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bv), as_bf16x8(av), acc[jt], 0, 0, 0);
       }
     }
     __syncthreads();  // the stage is free for the load two chunks on
   }
 
-  // D[token][j]: lane holds j = 32 jt + lane % 32, tokens 32 w + 8 (e/4) + 4 g + e % 4.
-  // Staged as bf16 [token][128], 16-byte slot (j / 8) ^ (token % 16), then
-  // written in whole 256-byte rows.
+  // The products are D^T: lane holds token 32 w + lane % 32 and outputs
+  // j = 32 jt + 8 (e/4) + 4 g + e % 4, four consecutive j per e/4, stored as
+  // one 8-byte bf16 group.  Staged as bf16 [token][128], 16-byte slot
+  // (j / 8) ^ (token % 16), then written in whole 256-byte rows.
   uint16_t* ot = (uint16_t*)smem;
+  {
+    const int tk = 32 * w + r32;
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
+    for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int tk = 32 * w + 8 * (e >> 2) + 4 * g + (e & 3);
-      const int j = 32 * jt + r32;
-      ot[tk * PD + 8 * ((j >> 3) ^ (tk & 15)) + (j & 7)] = f32_to_bf16(acc[jt][e]);
-    }
+      for (int eg = 0; eg < 4; ++eg) {
+        const int j0 = 32 * jt + 8 * eg + 4 * g;
+        const u32x2 v = {pack_bf16x2(acc[jt][4 * eg], acc[jt][4 * eg + 1]),
+                         pack_bf16x2(acc[jt][4 * eg + 2], acc[jt][4 * eg + 3])};
+        *(u32x2*)(ot + tk * PD + 8 * ((j0 >> 3) ^ (tk & 15)) + (j0 & 7)) = v;
+      }
+  }
   __syncthreads();
   uint16_t* dst = (uint16_t*)(which ? a.ws_v : a.ws_k) + ((size_t)h * N + n0) * PD;
 #pragma unroll
