@@ -22,6 +22,11 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
 // ---------------------------------------------------------------- cache write
 // Every wave owns a contiguous range of 64-wide k chunks.  A chunk of the 16
 // W rows and 16 * TB4 h rows is fetched with whole 128-byte lines per row (8
@@ -153,6 +158,128 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
     const uint32_t hi = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
     uint16_t* dst = (uint16_t*)a.pool + (size_t)slot[t] * R + rf;
     *(uint2*)dst = make_uint2(lo, hi);
+  }
+}
+
+// Cache write for many tokens (a prefill chunk): one work-group per (128
+// tokens, 192 cached features) with the whole hidden axis, so each h row is
+// fetched by the R / 192 work-groups of its token block only, and those run
+// on one XCD at the same time (its L2 serves the other fetches).  64-wide
+// k chunks of the 192 W rows and 128 h rows pass through two LDS stages by
+// direct-to-LDS loads (128-byte rows, 16-byte piece c at slot
+// c ^ ((row / 2) % 8)).  The products are D^T: wave (wf, wt) holds features
+// 96 wf .. +95 against tokens 64 wt .. +63, each lane four consecutive
+// features of one token per accumulator group, so the rotary pairs of the
+// k_R branch are rotated in registers and stored as one 8-byte group.
+constexpr int WB_T = 128, WB_F = 192, WB_K = 64;
+constexpr int WB_STAGE = (WB_F + WB_T) * WB_K * 2;  // 40 KiB
+constexpr int WB_LPW = (WB_F + WB_T) / 8 / 4;       // loads per wave per stage (10)
+
+__device__ __forceinline__ int wb_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__global__ void __launch_bounds__(256, 2) k_write_big(WriteCacheArgs a, int n_fb) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * WB_STAGE];
+  // work-group i runs on XCD i % 8: the n_fb feature blocks of a token block
+  // take consecutive slots of one XCD
+  const int id = blockIdx.x, xcd = id & 7, sl = id >> 3;
+  const int tb_blk = (sl / n_fb) * 8 + xcd, fblk = sl % n_fb;
+  const int n0 = tb_blk * WB_T, r0 = fblk * WB_F;
+  if (n0 >= a.n_tokens) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r32 = lane & 31;
+  const int wf = w >> 1, wt = w & 1;
+  const int N = a.n_tokens, D = a.D, R = a.d_c + a.d_r;
+  const char* __restrict__ Wb = (const char*)a.w_dkr + (size_t)r0 * D * 2;
+  const char* __restrict__ Hb = (const char*)a.h + (size_t)n0 * D * 2;
+  const uint32_t lds0 = lds_addr_of(smem);
+
+  // loads: instruction u (0..39) of a stage fills LDS bytes [1024 u, +1024):
+  // stage rows 8 u + lane / 8 (rows < 192: W row r0 + row; else h row
+  // n0 + row - 192, clamped to the last token), slot lane % 8.  Wave w
+  // issues u = w + 4 i.
+  uint32_t voff[WB_LPW];
+#pragma unroll
+  for (int i = 0; i < WB_LPW; ++i) {
+    const int u = w + 4 * i, r = 8 * u + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int row = r < WB_F ? r : min(r - WB_F, N - 1 - n0);
+    voff[i] = (uint32_t)(row * D * 2 + 16 * c);
+  }
+  auto issue = [&](int kc, int st) {
+    const uint32_t base = lds0 + st * WB_STAGE;
+#pragma unroll
+    for (int i = 0; i < WB_LPW; ++i) {
+      const int u = w + 4 * i;
+      dma16<0>((8 * u < WB_F ? Wb : Hb) + 128 * kc, voff[i], base + 1024 * u);
+    }
+  };
+
+  f32x16 acc[3][2];
+#pragma unroll
+  for (int fb = 0; fb < 3; ++fb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = f32x16{};
+  const int nk = D / WB_K;
+  issue(0, 0);
+  for (int kc = 0; kc < nk; ++kc) {
+    if (kc + 1 < nk) {
+      issue(kc + 1, (kc + 1) & 1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WB_LPW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* st = smem + (kc & 1) * WB_STAGE;
+#pragma unroll
+    for (int ks = 0; ks < WB_K / 16; ++ks) {
+      const int c = 2 * ks + g;
+      u32x4 bv[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int rb = WB_F + 64 * wt + 32 * tb + r32;  // B column: token
+        bv[tb] = *(const u32x4*)(st + rb * 128 + 16 * wb_slot(rb, c));
+      }
+#pragma unroll
+      for (int fb = 0; fb < 3; ++fb) {
+        const int ra = 96 * wf + 32 * fb + r32;  // A row: feature
+        const u32x4 av = *(const u32x4*)(st + ra * 128 + 16 * wb_slot(ra, c));
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv[tb]), acc[fb][tb], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the stage is free for the load two chunks on
+  }
+
+  // D^T[feature][token]: lane holds token 64 wt + 32 tb + lane % 32 and
+  // features 96 wf + 32 fb + 8 (e/4) + 4 g + e % 4
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int n = n0 + 64 * wt + 32 * tb + r32;
+    if (n >= N) continue;
+    const long long slot = a.dense ? (long long)n : a.slots[n];
+    if (slot < 0) continue;
+    const int pos = a.positions[n];
+    uint16_t* dst = (uint16_t*)a.pool + (size_t)slot * R;
+#pragma unroll
+    for (int fb = 0; fb < 3; ++fb)
+#pragma unroll
+      for (int eg = 0; eg < 4; ++eg) {
+        const int f0 = r0 + 96 * wf + 32 * fb + 8 * eg + 4 * g;
+        float o[4] = {acc[fb][tb][4 * eg], acc[fb][tb][4 * eg + 1], acc[fb][tb][4 * eg + 2], acc[fb][tb][4 * eg + 3]};
+        if (f0 >= a.d_c) {
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            float c, sn;
+            rope_cs_theta(pos, rope_inv_freq((f0 - a.d_c) / 2 + pr, a.d_r, a.rope_base), c, sn);
+            const float x0 = o[2 * pr], x1 = o[2 * pr + 1];
+            o[2 * pr] = x0 * c - x1 * sn;
+            o[2 * pr + 1] = x0 * sn + x1 * c;
+          }
+        }
+        *(uint2*)(dst + f0) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      }
   }
 }
 
@@ -294,7 +421,12 @@ hipError_t write_cache_mfma(const WriteCacheArgs& a, hipStream_t s) {
   // split the hidden axis, fetching their chunks in batches of 4 (two round
   // trips at D = 7168); many tokens: 4 token blocks per work-group reuse each W
   // fragment 4 times
-  if (a.n_tokens <= 1024) {
+  if (a.n_tokens >= 4096 && R % WB_F == 0 && a.D % WB_K == 0) {
+    // many tokens: whole-hidden-axis tiles (the grid covers 8 token blocks per
+    // XCD round; blocks past the last token return at once)
+    const int n_fb = R / WB_F, n_tb = (a.n_tokens + WB_T - 1) / WB_T;
+    hipLaunchKernelGGL(k_write_big, dim3(((n_tb + 7) / 8) * 8 * n_fb), dim3(256), 0, s, a, n_fb);
+  } else if (a.n_tokens <= 1024) {
     hipLaunchKernelGGL((k_write_mfma<1, 16, 4, 2>), dim3(R / 16, (a.n_tokens + 15) / 16), dim3(1024), 0, s, a);
   } else {
     hipLaunchKernelGGL((k_write_mfma<4, 4, 2, 2>), dim3(R / 16, (a.n_tokens + 63) / 64), dim3(256), 0, s, a);

@@ -66,8 +66,8 @@ def test_fp8_write_one_hot_is_bit_exact(flags):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("flags,seq_len", [(0, 300), (mla.FLAG_GENERIC, 300), (0, 700)],
-                         ids=["mfma_rows", "generic_rows", "mfma_rows_2100_tokens"])
+@pytest.mark.parametrize("flags,seq_len", [(0, 300), (mla.FLAG_GENERIC, 300), (0, 700), (0, 1667)],
+                         ids=["mfma_rows", "generic_rows", "mfma_rows_2100_tokens", "mfma_rows_5001_tokens"])
 def test_fp8_write_random_rows_within_half_step(flags, seq_len):
     need_gpu()
     _case(f"fp8 write random rows flags={flags} seq_len={seq_len}")
