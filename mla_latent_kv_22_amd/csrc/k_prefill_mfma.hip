@@ -238,41 +238,61 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
     }
   }
 
-  // tile loads: wave w issues loads u = w + 4 i (i < 5) of the 20:
-  // u < 8 K_C rows 4 u .. +3; u < 12 k_R rows 8 (u - 8) .. +7; else V rows 4 (u - 12) .. +3.
-  // Rows past the sequence end repeat its last key (masked in the scores).
+  // tile loads: wave w issues loads u = w + 4 i (i < 5) of the 20, so the
+  // kind of load depends on i alone: i < 2 K_C rows 4 u .. +3 (u = w + 4 i);
+  // i = 2 k_R rows 8 w .. +7; i > 2 V rows 4 (w + 4 (i - 3)) .. +3.  The lane
+  // offsets are fixed per wave; only the last tile of a sequence can be
+  // ragged, and there rows past the end repeat its last key (masked in the
+  // scores).
   const char* __restrict__ kc_base = (const char*)a.ws_k + ((size_t)h * N + ck0) * (PD * 2);
   const char* __restrict__ v_base = (const char*)a.ws_v + ((size_t)h * N + ck0) * (PD * 2);
   const int32_t* __restrict__ bt = a.block_table + (size_t)s * a.max_pages_per_seq;
   const uint32_t lds0 = lds_addr_of(smem);
+  int lrow[LPT], lcol[LPT];
+  uint32_t loff[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    if (i < 2) {
+      lrow[i] = 4 * (w + 4 * i) + (lane >> 4);
+      lcol[i] = 16 * ((lane & 15) ^ (lrow[i] & 15));
+    } else if (i == 2) {
+      lrow[i] = 8 * w + (lane >> 3);
+      lcol[i] = 16 * ((lane & 7) ^ ((lrow[i] >> 1) & 7));
+    } else {
+      lrow[i] = 4 * (w + 4 * (i - 3)) + (lane >> 4);
+      lcol[i] = 16 * ((lane & 15) ^ (4 * (lrow[i] & 3)));
+    }
+    loff[i] = (uint32_t)(lrow[i] * (i == 2 ? R * 2 : PD * 2) + lcol[i]);
+  }
   // the block-table entry of a tile is read one iteration before its loads
   // are issued, so the scalar load never stalls the wave (P % 32 == 0: a
-  // tile lies in one page)
+  // tile lies in one page; pages and in-page tiles advance by counting)
   // (through the constant address space: a scalar load, counted by lgkmcnt
   // and not by the vmcnt that tracks the tile loads)
   const __attribute__((address_space(4))) int32_t* bt_c = (const __attribute__((address_space(4))) int32_t*)bt;
-  auto page_of = [&](int kt) { return bt_c[min(kt, n_kt - 1) * AK / a.P]; };
-  auto issue = [&](int kt, int page) {
+  const int tpp = a.P / AK, pg_last = (n_kt - 1) / tpp;
+  const uint32_t page_bytes = (uint32_t)(a.P * R * 2), tile_bytes = (uint32_t)(AK * R * 2);
+  const char* __restrict__ kr_pool = (const char*)a.pool + a.d_c * 2;
+  auto issue = [&](int kt, int page, int in_page) {
     const int key0 = kt * AK;
     const int maxr = klen - 1 - key0;
-    const char* kr_base = (const char*)a.pool + ((size_t)page * a.P + key0 % a.P) * (size_t)R * 2 + a.d_c * 2;
+    const char* kr_base = kr_pool + (size_t)(uint32_t)page * page_bytes + (uint32_t)in_page * tile_bytes;
+    const char* kc_t = kc_base + (size_t)key0 * (PD * 2);
+    const char* v_t = v_base + (size_t)key0 * (PD * 2);
     const uint32_t st = lds0 + (kt & (NST - 1)) * ST_BYTES;
+    auto loads = [&](auto ragged) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int u = w + 4 * i;
-      if (u < 8) {
-        const int r = 4 * u + (lane >> 4), c = (lane & 15) ^ (r & 15);
-        dma16<0>(kc_base + (size_t)key0 * (PD * 2), (uint32_t)(min(r, maxr) * (PD * 2) + 16 * c),
-                 st + ST_KC + 1024 * u);
-      } else if (u < 12) {
-        const int r = 8 * (u - 8) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
-        dma16<0>(kr_base, (uint32_t)(min(r, maxr) * R * 2 + 16 * c), st + ST_KR + 1024 * (u - 8));
-      } else {
-        const int r = 4 * (u - 12) + (lane >> 4), c = (lane & 15) ^ (4 * (r & 3));
-        dma16<0>(v_base + (size_t)key0 * (PD * 2), (uint32_t)(min(r, maxr) * (PD * 2) + 16 * c),
-                 st + ST_V + 1024 * (u - 12));
+      for (int i = 0; i < LPT; ++i) {
+        uint32_t off = loff[i];
+        if constexpr (decltype(ragged)::value)
+          off = (uint32_t)(min(lrow[i], maxr) * (i == 2 ? R * 2 : PD * 2) + lcol[i]);
+        if (i < 2) dma16<0>(kc_t, off, st + ST_KC + 1024 * (w + 4 * i));
+        else if (i == 2) dma16<0>(kr_base, off, st + ST_KR + 1024 * w);
+        else dma16<0>(v_t, off, st + ST_V + 1024 * (w + 4 * (i - 3)));
       }
-    }
+    };
+    if (maxr >= AK - 1) loads(std::false_type{});
+    else loads(std::true_type{});
   };
 
   // V^T fragment offsets (A operand of O^T += V^T P^T): lane (d = lane % 32, g)
@@ -299,16 +319,23 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   // finite so that a fully masked score never meets inf - inf.
   float m = kMInit, l = 0.f;
 
-  int next_page = page_of(3);
+  // page and in-page tile of the next tile to load (tile 3 after the
+  // prologue), and its block-table entry
+  int ld_pg = 3 / tpp, ld_in = 3 % tpp;
+  int next_page = bt_c[min(ld_pg, pg_last)];
   auto sync = [&](int kt) {
-    const int ahead = min(2, n_kt - 1 - kt);
-    if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
+    // tile kt has landed once at most the later tiles' loads are in flight
+    if (kt + 2 < n_kt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
+    else if (kt + 1 < n_kt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();  // tile kt in LDS; tile kt-1's stage no longer read
     asm volatile("" ::: "memory");
-    if (kt + 3 < n_kt) issue(kt + 3, next_page);
-    next_page = page_of(kt + 4);
+    if (kt + 3 < n_kt) issue(kt + 3, next_page, ld_in);
+    if (++ld_in == tpp) {
+      ld_in = 0;
+      ++ld_pg;
+    }
+    next_page = bt_c[min(ld_pg, pg_last)];
   };
 
   // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASKED is
@@ -394,7 +421,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
 
 #pragma unroll
   for (int t = 0; t < 3; ++t)
-    if (t < n_kt) issue(t, page_of(t));
+    if (t < n_kt) issue(t, bt_c[t / tpp], t % tpp);
   // every wave takes part in all n_kt barriers and loads; it computes
   // tiles 0 .. kt_last, of which those from kt_mask on meet the diagonal (one
   // tile for a fresh sequence, at most two after a prefix that is not a
