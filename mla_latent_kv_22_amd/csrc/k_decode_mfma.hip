@@ -378,7 +378,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
   const int g = lane >> 5, hl = lane & 31;
   const int hq = w * 32 + hl;
   const bool hvalid = hq < a.H;
-  const int P = a.P;
+  const int P = a.P, tpp = P / TT;
+  const uint32_t page_bytes = (uint32_t)(P * RW * 2);
   const char* __restrict__ pool = (const char*)a.pool;
   const uint32_t lds_tiles = lds_addr_of(tiles);
   uint32_t lane_off[4];
@@ -414,11 +415,21 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
     const __attribute__((address_space(4))) int32_t* btb =
         (const __attribute__((address_space(4))) int32_t*)(a.block_table + (size_t)b * a.max_pages_per_seq);
     const int ntiles = (t1 - t0 + TT - 1) / TT;
+    // tiles are requested in order, so pages and in-page tiles are counted
+    // (a tile lies in one page: P % 32 == 0, t0 % 32 == 0), and the next
+    // tile's block-table entry is read one request ahead of its use
+    const int pg_end = (t1 - 1) / P;
+    int w_pg = t0 / P, w_in = (t0 % P) / TT;
+    int w_page = btb[w_pg];
     auto tile_ptr = [&](int tile, int& nvalid) {
-      const int tok0 = t0 + tile * TT;
-      nvalid = min(TT, t1 - tok0);
-      const int page = btb[tok0 / P];
-      return pool + ((size_t)page * P + (tok0 % P)) * (RW * 2);
+      nvalid = min(TT, t1 - (t0 + tile * TT));
+      const char* tp = pool + (size_t)(uint32_t)w_page * page_bytes + (uint32_t)w_in * (TT * RW * 2);
+      if (++w_in == tpp) {
+        w_in = 0;
+        ++w_pg;
+      }
+      w_page = btb[min(w_pg, pg_end)];
+      return tp;
     };
 
     // prologue: the absorbed query fragments (B operand of the score MFMA:
@@ -595,7 +606,8 @@ __global__ void __launch_bounds__(64, 1) k_split2s(DecodeArgs a) {
 
   const int g = lane >> 5, hl = lane & 31;
   const bool hvalid = hl < a.H;
-  const int P = a.P;
+  const int P = a.P, tpp = P / TT;
+  const uint32_t page_bytes = (uint32_t)(P * RW * 2);
   const char* __restrict__ pool = (const char*)a.pool;
   const uint32_t lds_tiles = lds_addr_of(tiles);
   uint32_t lane_off[4];
@@ -628,11 +640,21 @@ __global__ void __launch_bounds__(64, 1) k_split2s(DecodeArgs a) {
     const __attribute__((address_space(4))) int32_t* btb =
         (const __attribute__((address_space(4))) int32_t*)(a.block_table + (size_t)b * a.max_pages_per_seq);
     const int ntiles = (t1 - t0 + TT - 1) / TT;
+    // tiles are requested in order, so pages and in-page tiles are counted
+    // (a tile lies in one page: P % 32 == 0, t0 % 32 == 0), and the next
+    // tile's block-table entry is read one request ahead of its use
+    const int pg_end = (t1 - 1) / P;
+    int w_pg = t0 / P, w_in = (t0 % P) / TT;
+    int w_page = btb[w_pg];
     auto tile_ptr = [&](int tile, int& nvalid) {
-      const int tok0 = t0 + tile * TT;
-      nvalid = min(TT, t1 - tok0);
-      const int page = btb[tok0 / P];
-      return pool + ((size_t)page * P + (tok0 % P)) * (RW * 2);
+      nvalid = min(TT, t1 - (t0 + tile * TT));
+      const char* tp = pool + (size_t)(uint32_t)w_page * page_bytes + (uint32_t)w_in * (TT * RW * 2);
+      if (++w_in == tpp) {
+        w_in = 0;
+        ++w_pg;
+      }
+      w_page = btb[min(w_pg, pg_end)];
+      return tp;
     };
 
     u32x4 qf[KS];
@@ -979,7 +1001,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
   const int g = lane >> 5, hl = lane & 31;
   const int hq = w * 32 + hl;
   const bool hvalid = hq < a.H;
-  const int P = a.P;
+  const int P = a.P, tpp = P / TT;
   const size_t page8 = (size_t)P * (RW + 4);
   const char* __restrict__ pool = (const char*)a.pool;
   const uint32_t lds_tiles = lds_addr_of(tiles);
@@ -1011,12 +1033,22 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
     const __attribute__((address_space(4))) int32_t* btb =
         (const __attribute__((address_space(4))) int32_t*)(a.block_table + (size_t)b * a.max_pages_per_seq);
     const int ntiles = (t1 - t0 + TT - 1) / TT;
+    // tiles are requested in order: pages and in-page tiles are counted, and
+    // the next tile's block-table entry is read one request ahead of its use
+    const int pg_end = (t1 - 1) / P;
+    int w_pg = t0 / P, w_in = (t0 % P) / TT;
+    int w_page = btb[w_pg];
     auto tile_src = [&](int tile, int& nvalid, const char*& scales) {
-      const int tok0 = t0 + tile * TT;
-      nvalid = min(TT, t1 - tok0);
-      const char* pg = pool + (size_t)btb[tok0 / P] * page8;
-      scales = pg + (size_t)P * RW + 4 * (tok0 % P);
-      return pg + (size_t)(tok0 % P) * RW;
+      nvalid = min(TT, t1 - (t0 + tile * TT));
+      const char* pg = pool + (size_t)(uint32_t)w_page * page8;
+      scales = pg + (size_t)P * RW + 4 * TT * w_in;
+      const char* rows = pg + (size_t)(TT * RW) * w_in;
+      if (++w_in == tpp) {
+        w_in = 0;
+        ++w_pg;
+      }
+      w_page = btb[min(w_pg, pg_end)];
+      return rows;
     };
     auto stage = [&](int tile) { return tiles + (tile & 3) * TILE8_BYTES; };
     // E8M0 scale byte of the lane's row in a tile (the exponent field of the
