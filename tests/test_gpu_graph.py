@@ -1,6 +1,7 @@
-"""The decode step (cache write on a side stream, absorption, split + combine)
-captured in a HIP graph: every replay, with eager work and synchronisations
-between replays, gives the same bits as the eager step."""
+"""The decode step (cache write, absorption, split + combine; on one stream as
+the bench runs it, or with the cache write on a side stream) captured in a
+HIP graph: every replay, with eager work and synchronisations between
+replays, gives the same bits as the eager step."""
 import numpy as np
 import pytest
 import torch
@@ -11,13 +12,14 @@ from tests._util import need_gpu
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("two_streams", [False, True], ids=["one_stream", "side_stream_write"])
+def test_graph_replays_match_eager(two_streams):
     need_gpu()
-    print("[case] graph replay v2lite dims", flush=True)
+    print(f"[case] graph replay v2lite dims two_streams={two_streams}", flush=True)
     cfg = I.scaled(I.V2LITE, batch=6, seq_len=700, min_seq_len=1, paged=True)
     inp = I.make(cfg, 5)
     st = harness.DecodeStep(cfg, inp)
-    side = torch.cuda.Stream()
+    side = torch.cuda.Stream() if two_streams else None
     pool0 = st.pool.clone()
     st.step(pool=st.pool, side_stream=side)
     torch.cuda.synchronize()
