@@ -10,7 +10,14 @@ Prints one JSON line.  `value` is latent-cache GB/s of the step: the
 algorithmic bytes (sum of sequence lengths x 576 values x 2 bytes) divided by
 the step time; tokens/s (sequences decoded per second, per layer) rides along.
 
+Besides the headline line's step, the JSON carries: the decode call alone at
+every other decode workload (tiny fp32, V2-Lite, paged ragged), a measured
+streaming-read ceiling of the GPU, the prefill and 8-bit-cache legs, the
+float64 oracle timed on the host (cpu_baseline) and the run conditions.
+
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload v3_decode]
+       python bench.py --calibrate   (a 1 GiB device copy x 3, to scale the
+                                      FETCH_SIZE / WRITE_SIZE counters)
 """
 from __future__ import annotations
 
@@ -35,6 +42,138 @@ def _src_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def conditions():
+    """Run conditions: host CPU, cores, ROCm / torch versions, GPU name, the
+    code's identity (git SHA when the tree has one, else a hash of the
+    sources)."""
+    import platform
+    import subprocess
+    import torch
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        rocm = getattr(torch.version, "hip", None)
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except Exception:  # pragma: no cover
+        sha = None
+    h = hashlib.sha256()
+    for sub in ("include", os.path.join("mla_latent_kv_22_amd", "csrc")):
+        for dirpath, _, files in sorted(os.walk(os.path.join(ROOT, sub))):
+            for fn in sorted(files):
+                if fn.endswith((".h", ".hip")):
+                    with open(os.path.join(dirpath, fn), "rb") as f:
+                        h.update(fn.encode() + f.read())
+    return {"gpu": torch.cuda.get_device_name(0), "cpu_model": cpu, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "rocm": rocm, "torch": torch.__version__, "python": platform.python_version(), "git_sha": sha,
+            "source_sha256_16": h.hexdigest()[:16]}
+
+
+def stream_ceiling(gib=4, reps=5):
+    """Measured streaming-read ceiling: the best rate of a plain 16-byte read
+    stream (libmla_probe.so) over a buffer of `gib` GiB, well beyond the
+    256 MB Infinity Cache, over a few grid sizes."""
+    import ctypes
+    import numpy as np
+    import torch
+    L = ctypes.CDLL(os.path.join(ROOT, "mla_latent_kv_22_amd", "libmla_probe.so"))
+    L.mla_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p]
+    L.mla_probe_stream_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.random_(0, 255)
+    stream = torch.cuda.current_stream()
+    best, per = 0.0, {}
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.empty(blocks * 4, dtype=torch.int32, device="cuda")
+
+        def run():
+            assert L.mla_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream) == 0
+        run()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            run()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        per[blocks] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        best = max(best, per[blocks])
+    del buf
+    torch.cuda.empty_cache()
+    return {"gbs": best, "by_grid": per, "bytes": nbytes,
+            "kernel": "libmla_probe.so k_stream_read: 16-byte loads, 4 in flight per thread, 256 threads per group"}
+
+
+def decode_call_leg(cfg, copies, n, ceiling=None):
+    """The decode call alone (split + combine) at one workload: `copies` pool
+    copies alternate so that the cache is not warm in the Infinity Cache;
+    n calls, each timed with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_22_amd import harness, inputs as I, mla
+    print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
+    inp = I.make(cfg, 0)
+    st = harness.DecodeStep(cfg, inp)
+    st.step()
+    pools = [st.pool] + [st.pool.clone() for _ in range(copies - 1)]
+    stream = torch.cuda.current_stream()
+    for i in range(10):
+        st.attend(pool=pools[i % copies])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        st.attend(pool=pools[i % copies])
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    elem = 4 if cfg.dtype == "f32" else 2
+    algo = int(np.sum(inp["seq_lens"].astype(np.int64))) * cfg.row_width * elem
+    ms = float(np.mean(t))
+    gbs = algo / (ms * 1e-3) / 1e9
+    res = {"workload": f"{cfg.name}: B={cfg.batch} T={cfg.seq_len}{' (max, ragged U{%d..%d})' % (cfg.min_seq_len, cfg.seq_len) if cfg.min_seq_len else ''} "
+                       f"H={cfg.num_heads} d_c={cfg.d_c} d_R={cfg.d_r} {cfg.dtype} page={cfg.page_size}",
+           "fast_path": bool(mla.uses_fast_path(st.d, mla.OP_DECODE)),
+           "algorithmic_bytes": algo, "decode_us": round(ms * 1e3, 2),
+           "decode_us_p50_p95_p99": [round(float(np.percentile(t, p)) * 1e3, 2) for p in (50, 95, 99)],
+           "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1), "calls": n, "cache_copies_rotated": copies}
+    if ceiling:
+        res["frac_of_measured_ceiling"] = round(gbs / ceiling, 4)
+    del st, pools
+    torch.cuda.empty_cache()
+    return res
+
+
+def calibrate():
+    """A plain device copy of known size (1 GiB read + 1 GiB written, 3
+    times): the FETCH_SIZE and WRITE_SIZE counters of this run give the
+    factors from reported KiB to bytes."""
+    import torch
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {nbytes} bytes x 3", flush=True)
+
+
 def _traffic(n_steps_note=""):
     """HBM bytes per decode call from committed rocprofv3 counter runs, or None
     when the counters are absent or the kernel source changed since."""
@@ -51,7 +190,9 @@ def _traffic(n_steps_note=""):
 def cpu_baseline(cfg, inp, budget_s=20.0):
     """Time the float64 oracle on a bounded sample of the same workload: whole
     sequences over all heads (the oracle's cost is linear in both), as many as
-    fit in about budget_s seconds after timing the first one."""
+    fit in about budget_s seconds after timing the first one.  `cores` is the
+    BLAS thread count the oracle ran with (the box's CPU share sets it);
+    `affinity_cpus` is what the scheduler would allow."""
     import numpy as np
     from tests._util import oracle_decode
     try:
@@ -68,7 +209,7 @@ def cpu_baseline(cfg, inp, budget_s=20.0):
     dt = time.perf_counter() - t0
     sample_tokens = float(np.sum(inp["seq_lens"][:n].astype(np.int64)))
     return {"value": round(sample_tokens * cfg.row_width * 2 / dt / 1e9, 6), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"sequences 0..{n - 1} of {cfg.batch} ({int(sample_tokens)} cached tokens) x all {cfg.num_heads} "
                       f"heads, float64 NumPy, non-absorbed (per-head K and V materialised); rate = sample latent "
                       f"bytes / oracle seconds"}
@@ -216,6 +357,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache leg")
     ap.add_argument("--no-graph", action="store_true", help="launch the step's kernels eagerly")
+    ap.add_argument("--no-legs", action="store_true", help="skip the other decode workloads and the read ceiling")
+    ap.add_argument("--calibrate", action="store_true", help="only the counter-calibration copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); multi-GPU runs are not part of this "
@@ -226,6 +369,9 @@ def main():
     import torch
     from mla_latent_kv_22_amd import harness, inputs as I, mla
 
+    if args.calibrate:
+        calibrate()
+        return
     mla.lib()
     if args.workload == "v3_decode_fp8":
         # 8-bit cache leg only (profiling runs): one JSON line
@@ -335,6 +481,16 @@ def main():
                      "mfma_frac_of_bf16_peak": round(flops / (dec_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "wall_s_timed": round(wall, 3),
     }
+    if not args.no_legs:
+        print("[bench] streaming-read ceiling", file=sys.stderr, flush=True)
+        ceil = stream_ceiling()
+        res["measured_read_ceiling"] = ceil
+        res["roofline"]["measured_ceiling_gbs"] = ceil["gbs"]
+        res["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["gbs"], 4)
+        res["decode_workloads"] = [decode_call_leg(I.TINY, 1, 50, ceil["gbs"]),
+                                   decode_call_leg(I.V2LITE, 8, 100, ceil["gbs"]),
+                                   decode_call_leg(I.RAGGED, 1, 50, ceil["gbs"])]
+    res["conditions"] = conditions()
     if not args.no_prefill:
         res["prefill"] = prefill_leg()
     if not args.no_fp8:

@@ -28,11 +28,20 @@
  *     fp32 (bf16 operands, fp32 accumulation) in either case.
  *   - Argument errors are detected on the host before anything is launched
  *     and return a negative mla_status; nothing is written.  A failed kernel
- *     launch returns MLA_ERR_HIP.  Device-side preconditions (block-table
- *     entries < num_pages, positions >= 0) are the caller's duty and are not
- *     checked on the device, except that decode lengths are clamped to
- *     max_seq_len, which the host checks against the block-table capacity,
- *     so no read leaves the caller's pages.
+ *     launch returns MLA_ERR_HIP.
+ *   - Device-side values (block-table entries, slots, sequence lengths and
+ *     offsets) are read by the kernels.  Lengths are always clamped on the
+ *     device to the host-side bounds the call passes (max_seq_len,
+ *     max_q_len, max_kv_len, totals), which the host checks against the
+ *     block-table capacity, so a length never takes a read past a
+ *     sequence's block-table row.  Block-table entries must lie in
+ *     [0, num_pages) and slots in [-1, num_pages * P): a release build does
+ *     not check them.  A library built with MLA_DEBUG (libmla_debug.so,
+ *     same ABI) compares every entry and slot with num_pages before it forms
+ *     an address: an entry out of range sets a bit of the device error word
+ *     (MLA_DEVERR_*, read with mla_get_device_error) and is replaced by
+ *     page 0 (a slot is skipped), so no access leaves the pool; a clamped
+ *     length sets MLA_DEVERR_LENGTH.
  *   - Calls on one stream are ordered; calls that share an output or a
  *     workspace on different streams race.
  */
@@ -56,8 +65,16 @@ typedef enum {
   MLA_ERR_WORKSPACE = -4, /* workspace smaller than the *_workspace_size value */
   MLA_ERR_CAPACITY = -5,  /* max_seq_len exceeds max_pages_per_seq * page_size */
   MLA_ERR_HIP = -6,       /* a HIP launch or device query failed               */
-  MLA_ERR_ARG = -7        /* other invalid argument (negative count, bad flag) */
+  MLA_ERR_ARG = -7        /* other invalid argument (negative count, bad flag,
+                             softmax_scale <= 0, an empty pool for work)       */
 } mla_status;
+
+/* Bits of the device error word (set only by MLA_DEBUG builds). */
+enum {
+  MLA_DEVERR_PAGE = 1,   /* a block-table entry outside [0, num_pages)          */
+  MLA_DEVERR_SLOT = 2,   /* a slot_mapping entry outside [-1, num_pages * P)    */
+  MLA_DEVERR_LENGTH = 4  /* a device length or offset beyond its host bound    */
+};
 
 enum { MLA_F32 = 0, MLA_BF16 = 1 };
 
@@ -90,8 +107,8 @@ typedef struct {
   int32_t v_head;      /* d_v: per-head value width                             */
   int32_t page_size;   /* P: tokens per cache page                              */
   int32_t dtype;       /* MLA_F32 or MLA_BF16                                   */
-  float rope_base;     /* RoPE base (10000 in the pages' models)                */
-  float softmax_scale; /* sigma, multiplies every score                         */
+  float rope_base;     /* RoPE base (10000 in the pages' models), > 0           */
+  float softmax_scale; /* sigma > 0, multiplies every score                     */
   int32_t flags;       /* 0 or MLA_FLAG_* bits                                  */
 } mla_dims_t;
 
@@ -109,8 +126,8 @@ typedef struct {
  *   positions    [n_tokens]                    int32
  *   slot_mapping [n_tokens]                    int64  page * P + offset, -1 = skip
  *   pool         [num_pages, P, d_c + d_r]     dtype  updated in place
- * Slots must be distinct and < num_pages * P (unchecked on the device).
- * n_tokens == 0 is a no-op.
+ * Slots must be distinct and < num_pages * P (checked on the device only by
+ * MLA_DEBUG builds).  n_tokens == 0 is a no-op; otherwise num_pages >= 1.
  */
 int mla_write_cache(const mla_dims_t* dims, const void* h, const void* w_dkr,
                     const int32_t* positions, const int64_t* slot_mapping, int32_t n_tokens,
@@ -172,8 +189,8 @@ size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t 
  *                                               row_t is then the stored
  *                                               value E4M3(code) * scale
  *   block_table [batch, max_pages_per_seq]      int32
- *   seq_lens    [batch]                         int32 (device); lengths above
- *                                                max_seq_len are clamped to it
+ *   seq_lens    [batch]                         int32 (device); lengths are
+ *                                                clamped to [0, max_seq_len]
  *   w_uv        [H, d_v, d_c]                   dtype
  *   out         [batch, H, d_v]                 dtype
  *   lse         [batch, H]                      fp32, may be NULL
@@ -182,7 +199,11 @@ size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t 
  * max_pages_per_seq * P (MLA_ERR_CAPACITY) and it sizes the workspace.
  * Results do not depend on the page permutation (token-space split
  * boundaries, fixed merge order): two calls on permuted pools give identical
- * bits.
+ * bits.  num_pages >= 1.
+ * Range: the fast path accumulates unnormalised softmax numerators below
+ * 2^100 (larger ones are detected and the affected partial is recomputed
+ * exactly), so cached values must stay below 2^28 in magnitude for the fp32
+ * latent sums to stay finite.
  */
 int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int32_t num_pages,
                const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
@@ -209,6 +230,7 @@ size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t total_tokens);
  *   out         [total_tokens, H, d_v]          dtype
  *   lse         [total_tokens, H]               fp32, may be NULL
  * max_seq_len bounds every sequence length (capacity check and tiling).
+ * Device offsets are clamped as in mla_prefill_kv; num_pages >= 1.
  */
 int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t num_pages,
                 const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* cu_seqlens,
@@ -237,6 +259,13 @@ int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t
  * Other arguments, layouts and errors as mla_prefill; MLA_ERR_ARG also when
  * total_kv < total_q or max_kv_len < max_q_len.  mla_prefill is this call
  * with cu_seqlens_kv = cu_seqlens_q (no prefix).
+ * The kernels clamp the device offsets of sequence i before use:
+ *   q0 = clamp(cu_q[i], 0, total_q),   q_len  = clamp(cu_q[i+1] - q0, 0, min(max_q_len, total_q - q0)),
+ *   k0 = clamp(cu_kv[i], 0, total_kv), kv_len = clamp(cu_kv[i+1] - k0, 0, min(max_kv_len, total_kv - k0)),
+ *   q_len = min(q_len, kv_len),
+ * so inconsistent offsets give wrong rows but no access outside the
+ * caller's buffers (MLA_DEVERR_LENGTH in MLA_DEBUG builds); query rows that
+ * no clamped sequence covers are left unwritten.
  */
 int mla_prefill_kv(const mla_dims_t* dims, const void* q, const void* pool, int32_t num_pages,
                    const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* cu_seqlens_q,
@@ -259,9 +288,24 @@ const char* mla_status_string(int status);
 /*
  * Which kernels a call with these dims would use: 1 = MFMA fast path,
  * 0 = generic path, negative = invalid dims.  `op` is 0 write_cache,
- * 1 absorb_q, 2 decode, 3 prefill.
+ * 1 absorb_q, 2 decode, 3 prefill.  The answer depends on the dims alone:
+ * no batch size or length moves a call off the path reported here.
  */
 int mla_uses_fast_path(const mla_dims_t* dims, int32_t op);
+
+/*
+ * The device error word of the current device: waits for `stream`, stores
+ * the word (MLA_DEVERR_* bits, 0 if nothing was found) in *error_bits and
+ * clears it.  The word is shared by every call on the device since the last
+ * read, whatever its stream.  Only a library built with MLA_DEBUG ever sets
+ * a bit (see the conventions above); mla_debug_build tells which build this
+ * is.  Returns MLA_ERR_NULL for a NULL error_bits, MLA_ERR_HIP if the wait
+ * or the copy fails.
+ */
+int mla_get_device_error(int32_t* error_bits, hipStream_t stream);
+
+/* 1 for a library built with MLA_DEBUG (device-side index checks), else 0. */
+int mla_debug_build(void);
 
 #ifdef __cplusplus
 }

@@ -349,7 +349,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
 
   const int cap = a.len_cap;
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
-                                           a.ovh_tokens, s_len, s_items, red);
+                                           a.ovh_tokens, s_len, s_items, red, a.err, a.max_items);
   const int n_items = plan.n_items;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // work-group 0 publishes the plan for the combine pass:
@@ -420,7 +420,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
     // tile's block-table entry is read one request ahead of its use
     const int pg_end = (t1 - 1) / P;
     int w_pg = t0 / P, w_in = (t0 % P) / TT;
-    int w_page = btb[w_pg];
+    int w_page = checked_page(btb[w_pg], a.num_pages, a.err);
     auto tile_ptr = [&](int tile, int& nvalid) {
       nvalid = min(TT, t1 - (t0 + tile * TT));
       const char* tp = pool + (size_t)(uint32_t)w_page * page_bytes + (uint32_t)w_in * (TT * RW * 2);
@@ -428,7 +428,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
         w_in = 0;
         ++w_pg;
       }
-      w_page = btb[min(w_pg, pg_end)];
+      w_page = checked_page(btb[min(w_pg, pg_end)], a.num_pages, a.err);
       return tp;
     };
 
@@ -582,7 +582,7 @@ __global__ void __launch_bounds__(64, 1) k_split2s(DecodeArgs a) {
 
   const int cap = a.len_cap;
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
-                                           a.ovh_tokens, s_len, s_items, red);
+                                           a.ovh_tokens, s_len, s_items, red, a.err, a.max_items);
   const int n_items = plan.n_items;
   const int lane = threadIdx.x & 63;
   if (blockIdx.x == 0) {
@@ -645,7 +645,7 @@ __global__ void __launch_bounds__(64, 1) k_split2s(DecodeArgs a) {
     // tile's block-table entry is read one request ahead of its use
     const int pg_end = (t1 - 1) / P;
     int w_pg = t0 / P, w_in = (t0 % P) / TT;
-    int w_page = btb[w_pg];
+    int w_page = checked_page(btb[w_pg], a.num_pages, a.err);
     auto tile_ptr = [&](int tile, int& nvalid) {
       nvalid = min(TT, t1 - (t0 + tile * TT));
       const char* tp = pool + (size_t)(uint32_t)w_page * page_bytes + (uint32_t)w_in * (TT * RW * 2);
@@ -653,7 +653,7 @@ __global__ void __launch_bounds__(64, 1) k_split2s(DecodeArgs a) {
         w_in = 0;
         ++w_pg;
       }
-      w_page = btb[min(w_pg, pg_end)];
+      w_page = checked_page(btb[min(w_pg, pg_end)], a.num_pages, a.err);
       return tp;
     };
 
@@ -977,7 +977,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
 
   const int cap = a.len_cap;
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
-                                           a.ovh_tokens, s_len, s_items, red);
+                                           a.ovh_tokens, s_len, s_items, red, a.err, a.max_items);
   const int n_items = plan.n_items;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (blockIdx.x == 0) {
@@ -1037,7 +1037,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
     // the next tile's block-table entry is read one request ahead of its use
     const int pg_end = (t1 - 1) / P;
     int w_pg = t0 / P, w_in = (t0 % P) / TT;
-    int w_page = btb[w_pg];
+    int w_page = checked_page(btb[w_pg], a.num_pages, a.err);
     auto tile_src = [&](int tile, int& nvalid, const char*& scales) {
       nvalid = min(TT, t1 - (t0 + tile * TT));
       const char* pg = pool + (size_t)(uint32_t)w_page * page8;
@@ -1047,7 +1047,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
         w_in = 0;
         ++w_pg;
       }
-      w_page = btb[min(w_pg, pg_end)];
+      w_page = checked_page(btb[min(w_pg, pg_end)], a.num_pages, a.err);
       return rows;
     };
     auto stage = [&](int tile) { return tiles + (tile & 3) * TILE8_BYTES; };
@@ -1207,7 +1207,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
 __device__ __noinline__ void recompute_partial(const void* __restrict__ pool, const int32_t* __restrict__ bt,
                                                const uint16_t* __restrict__ qa, float* __restrict__ pa,
                                                float* __restrict__ pml, int P, float scale_log2, int t0, int t1,
-                                               float* scratch, int* red, int f8) {
+                                               float* scratch, int* red, int f8, int num_pages, int* err) {
   // blockDim.x in {256, 512}: thread tid keeps latent columns tid (+ blockDim.x)
   const int nth = blockDim.x;
   float* q = scratch;          // 576
@@ -1218,7 +1218,7 @@ __device__ __noinline__ void recompute_partial(const void* __restrict__ pool, co
   __syncthreads();
   // value f of token t's row
   auto val = [&](int t, int f) {
-    const long long slot = (long long)bt[t / P] * P + t % P;
+    const long long slot = (long long)checked_page(bt[t / P], num_pages, err) * P + t % P;
     return f8 ? e4m3_to_f32(fp8_row(pool, slot, P, RW)[f]) * fp8_scale(pool, slot, P, RW)
               : bf16_to_f32(((const uint16_t*)pool)[(size_t)slot * RW + f]);
   };
@@ -1322,12 +1322,11 @@ __global__ void __launch_bounds__(64 * CNW, 4) k_combine(DecodeArgs a) {
           const int bl = blo + 4 * k;
           const int i = (bl < nb) ? s_items[bl] + j0 + jj : 0;
           const bool ok = bl < nb && i < s_items[bl + 1];
-          const uint32_t ih = (uint32_t)(ok ? i : 0) * (uint32_t)a.H + (uint32_t)h;
-          const float2 ml = ok ? *(const float2*)((const char*)pml + 8u * ih) : make_float2(-INFINITY, 0.f);
+          const size_t ih = (size_t)(ok ? i : 0) * (size_t)a.H + (size_t)h;
+          const float2 ml = ok ? *(const float2*)(pml + 2 * ih) : make_float2(-INFINITY, 0.f);
           mi[k][jj] = ml.x;
           li[k][jj] = ml.y;
-          ai[k][jj] = ok ? *(const f32x4*)((const char*)pacc + (uint32_t)(DC * 4) * ih + 16u * cq)
-                         : f32x4{0.f, 0.f, 0.f, 0.f};
+          ai[k][jj] = ok ? *(const f32x4*)(pacc + DC * ih + 4 * cq) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
@@ -1361,7 +1360,8 @@ __global__ void __launch_bounds__(64 * CNW, 4) k_combine(DecodeArgs a) {
         const size_t ih = (size_t)i * a.H + h;
         recompute_partial(a.pool, a.block_table + (size_t)b * a.max_pages_per_seq,
                           (const uint16_t*)a.q_abs + ((size_t)b * a.H + h) * RW, a.part_acc + ih * DC,
-                          a.part_ml + ih * 2, a.P, a.scale_log2, t0, t1, (float*)lat_hi, red, a.fp8);
+                          a.part_ml + ih * 2, a.P, a.scale_log2, t0, t1, (float*)lat_hi, red, a.fp8, a.num_pages,
+                          a.err);
       }
     }
     __syncthreads();

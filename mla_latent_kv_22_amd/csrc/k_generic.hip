@@ -19,7 +19,7 @@ __global__ void __launch_bounds__(256) k_write_cache(WriteCacheArgs a) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)a.n_tokens * J) return;
   const int n = (int)(idx / J), j = (int)(idx % J);
-  const long long slot = a.dense ? (long long)n : a.slots[n];
+  const long long slot = a.dense ? (long long)n : checked_slot(a.slots[n], a.num_pages, a.P, a.err);
   if (slot < 0) return;
   const int R = a.d_c + a.d_r;
   const T* h = (const T*)a.h + (size_t)n * a.D;
@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(64) k_decode_split(DecodeArgs a) {
 
   const int cap = a.len_cap;
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk, a.ovh_tokens,
-                                           s_len, s_items, red);
+                                           s_len, s_items, red, a.err, a.max_items);
   const int item = blockIdx.x;
   if (item >= plan.n_items) return;
   const int h = blockIdx.y, lane = threadIdx.x;
@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(64) k_decode_split(DecodeArgs a) {
     float s = -INFINITY, rscale = 1.f;
     const RowT* row = nullptr;
     if (valid) {
-      const long long slot = (long long)bt[t / a.P] * a.P + (t % a.P);
+      const long long slot = (long long)checked_page(bt[t / a.P], a.num_pages, a.err) * a.P + (t % a.P);
       float dot = 0.f;
       if constexpr (F8) {
         row = fp8_row(a.pool, slot, a.P, R);
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(128) k_decode_combine(DecodeArgs a) {
   float* stat = lat + a.d_c;  // m*, 1/L
 
   const int cap = a.len_cap;
-  make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk, a.ovh_tokens, s_len, s_items, red);
+  make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk, a.ovh_tokens, s_len, s_items, red, a.err, a.max_items);
   const int b = blockIdx.x, h = blockIdx.y;
   const int i0 = s_items[b], i1 = s_items[b + 1];
   T* out = (T*)a.out + ((size_t)b * a.H + h) * a.d_v;
@@ -235,10 +235,11 @@ __global__ void __launch_bounds__(256) k_prefill_upproj(PrefillArgs a) {
   const long long nh = idx / J;
   const int h = (int)(nh % a.H), n = (int)(nh / a.H);  // n: key token (prefix and new)
   const int sq = seq_of(a.cu_kv, a.num_seqs, n);
-  const int t = n - a.cu_kv[sq];
+  // clamped so that the block-table read stays in row sq (max_kv_len <= capacity)
+  const int t = key_position(n, a.cu_kv[sq], a.max_kv_len, a.err);
   const int R = a.d_c + a.d_r;
-  const T* row = (const T*)a.pool +
-                 ((size_t)a.block_table[(size_t)sq * a.max_pages_per_seq + t / a.P] * a.P + t % a.P) * R;
+  const int page = checked_page(a.block_table[(size_t)sq * a.max_pages_per_seq + t / a.P], a.num_pages, a.err);
+  const T* row = (const T*)a.pool + ((size_t)page * a.P + t % a.P) * R;
   const T* w = (j < a.d_n) ? (const T*)a.w_uk + ((size_t)h * a.d_n + j) * a.d_c
                            : (const T*)a.w_uv + ((size_t)h * a.d_v + (j - a.d_n)) * a.d_c;
   float acc = 0.f;
@@ -255,9 +256,11 @@ __global__ void __launch_bounds__(128) k_prefill_attn(PrefillArgs a) {
   float* red = ps + 128;               // 4
   const int n = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int sq = seq_of(a.cu_q, a.num_seqs, n);
-  const int base = a.cu_kv[sq];  // first key token of the sequence in the workspace
-  const int prefix = max(0, (a.cu_kv[sq + 1] - base) - (a.cu_q[sq + 1] - a.cu_q[sq]));
-  const int i = prefix + n - a.cu_q[sq];  // position of this query in its sequence
+  const PrefillSeq sd = prefill_seq(a.cu_q, a.cu_kv, sq, a.total, a.total_kv, a.max_seq_len, a.max_kv_len, a.err);
+  if (n < sd.q0 || n >= sd.q0 + sd.q_len) return;  // a row no (clamped) sequence covers
+  const int base = sd.k0;  // first key token of the sequence in the workspace
+  const int prefix = sd.kv_len - sd.q_len;
+  const int i = prefix + n - sd.q0;  // position of this query in its sequence
   const int R = a.d_c + a.d_r;
   const T* qv = (const T*)a.q + ((size_t)n * a.H + h) * (a.d_n + a.d_r);
   for (int k = tid; k < a.d_n; k += 128) qs[k] = ld(qv, k);
@@ -279,7 +282,7 @@ __global__ void __launch_bounds__(128) k_prefill_attn(PrefillArgs a) {
     float s = -INFINITY;
     if (t <= i) {
       const float* kc = K + ((size_t)(base + t) * a.H + h) * a.d_n;
-      const T* row = (const T*)a.pool + ((size_t)bt[t / a.P] * a.P + t % a.P) * R;
+      const T* row = (const T*)a.pool + ((size_t)checked_page(bt[t / a.P], a.num_pages, a.err) * a.P + t % a.P) * R;
       float dot = 0.f;
       for (int k = 0; k < a.d_n; ++k) dot += qs[k] * kc[k];
       for (int r = 0; r < a.d_r; ++r) dot += qs[a.d_n + r] * ld(row, a.d_c + r);
@@ -327,10 +330,10 @@ __global__ void __launch_bounds__(128) k_prefill_attn(PrefillArgs a) {
 // nearest even; x / 2^e is exact), a -0 result stored as +0.
 __global__ void __launch_bounds__(256) k_quantize_rows(const uint16_t* __restrict__ rows,
                                                        const int64_t* __restrict__ slots, uint8_t* __restrict__ pool8,
-                                                       int n_tokens, int R, int P) {
+                                                       int n_tokens, int R, int P, int num_pages, int* err) {
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (n >= n_tokens) return;
-  const long long slot = slots[n];
+  const long long slot = checked_slot(slots[n], num_pages, P, err);
   if (slot < 0) return;
   const uint16_t* row = rows + (size_t)n * R;
   float amax = 0.f;
@@ -367,10 +370,10 @@ hipError_t write_cache_generic(const WriteCacheArgs& a, bool bf16, hipStream_t s
 }
 
 hipError_t quantize_rows_fp8(const uint16_t* rows, const int64_t* slots, void* pool8, int n_tokens, int R, int P,
-                             hipStream_t s) {
+                             int num_pages, int* err, hipStream_t s) {
   if (n_tokens == 0) return hipSuccess;
   hipLaunchKernelGGL(k_quantize_rows, dim3(blocks_for(n_tokens, 4)), dim3(256), 0, s, rows, slots, (uint8_t*)pool8,
-                     n_tokens, R, P);
+                     n_tokens, R, P, num_pages, err);
   return hipGetLastError();
 }
 

@@ -91,8 +91,9 @@ __global__ void __launch_bounds__(256, 2) k_prefill_proj(PrefillArgs a) {
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int n = min(n0 + r, N - 1);
     const int s = seq_of(a.cu_kv, a.num_seqs, n);
-    const int t = n - a.cu_kv[s];
-    const int page = a.block_table[(size_t)s * a.max_pages_per_seq + t / a.P];
+    // clamped so that the block-table read stays in row s (max_kv_len <= capacity)
+    const int t = key_position(n, a.cu_kv[s], a.max_kv_len, a.err);
+    const int page = checked_page(a.block_table[(size_t)s * a.max_pages_per_seq + t / a.P], a.num_pages, a.err);
     crow[i] = (const char*)a.pool + ((size_t)page * a.P + t % a.P) * (size_t)R * 2;
     cchunk[i] = 16u * c;
     woff[i] = (uint32_t)(r * a.d_c * 2 + 16 * c);
@@ -194,9 +195,11 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   // new tokens cu0 .. cu0 + len - 1 of q / out; the sequence's keys (a cached
   // prefix, then the new tokens) are key tokens ck0 .. ck0 + klen - 1 of the
   // workspace and positions 0 .. klen - 1 of the cache
-  const int cu0 = a.cu_q[s], len = a.cu_q[s + 1] - cu0;
-  const int ck0 = a.cu_kv[s], klen = a.cu_kv[s + 1] - ck0;
-  const int prefix = max(0, klen - len);
+  const PrefillSeq sd = prefill_seq(a.cu_q, a.cu_kv, s, a.total, a.total_kv, a.max_seq_len, a.max_kv_len,
+                                    (qr == 0 && h == 0) ? a.err : nullptr);
+  const int cu0 = sd.q0, len = sd.q_len;
+  const int ck0 = sd.k0, klen = sd.kv_len;
+  const int prefix = klen - len;
   const int q0 = qb * AQ;  // query block, in new-token indices
   if (q0 >= len) return;
   const int qend = min(len, q0 + AQ);
@@ -274,6 +277,7 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   const uint32_t page_bytes = (uint32_t)(a.P * R * 2), tile_bytes = (uint32_t)(AK * R * 2);
   const char* __restrict__ kr_pool = (const char*)a.pool + a.d_c * 2;
   auto issue = [&](int kt, int page, int in_page) {
+    page = checked_page(page, a.num_pages, a.err);
     const int key0 = kt * AK;
     const int maxr = klen - 1 - key0;
     const char* kr_base = kr_pool + (size_t)(uint32_t)page * page_bytes + (uint32_t)in_page * tile_bytes;

@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
         const int nc = min(n, a.n_tokens - 1);
         const long long sl = a.dense ? (long long)nc : a.slots[nc];
         pos[t] = a.positions[nc];
-        slot[t] = ((t % NWV) == w && n < a.n_tokens) ? sl : -1;
+        slot[t] = ((t % NWV) == w && n < a.n_tokens) ? checked_slot(sl, a.num_pages, a.P, a.err) : -1;
       }
     }
     // the slices are private to the wave and LDS operations of one wave
@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(256, 2) k_write_big(WriteCacheArgs a, int n_fb
   for (int tb = 0; tb < 2; ++tb) {
     const int n = n0 + 64 * wt + 32 * tb + r32;
     if (n >= N) continue;
-    const long long slot = a.dense ? (long long)n : a.slots[n];
+    const long long slot = a.dense ? (long long)n : checked_slot(a.slots[n], a.num_pages, a.P, a.err);
     if (slot < 0) continue;
     const int pos = a.positions[n];
     uint16_t* dst = (uint16_t*)a.pool + (size_t)slot * R;

@@ -27,7 +27,10 @@ int check_dims(const mla_dims_t* d) {
       d->page_size < 1)
     return MLA_ERR_DIMS;
   if ((d->d_c & 1) || (d->d_r & 1)) return MLA_ERR_DIMS;
-  if (!(d->rope_base > 0.f) || !isfinite(d->rope_base) || !isfinite(d->softmax_scale)) return MLA_ERR_ARG;
+  // the kernels take the scaled maximum score as the softmax reference, which
+  // needs a positive scale
+  if (!(d->rope_base > 0.f) || !isfinite(d->rope_base) || !(d->softmax_scale > 0.f) || !isfinite(d->softmax_scale))
+    return MLA_ERR_ARG;
   if (fp8_cache(d)) {
     if (d->dtype != MLA_BF16) return MLA_ERR_DTYPE;
     // the float32 scales after the rows of a page stay 4-byte aligned
@@ -50,6 +53,22 @@ int current_cus() {
     return -1;
   if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+// The device error word (MLA_DEVERR_* bits), one per device; set only by
+// kernels of an MLA_DEBUG build.  Host code uses its per-device address.
+__device__ int g_device_error;
+
+int* device_error_word() {
+  static std::atomic<int*> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  int* p = cache[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(g_device_error)) != hipSuccess || !addr) return nullptr;
+  cache[dev].store((int*)addr, std::memory_order_release);
+  return (int*)addr;
 }
 
 bool bf16_fast(const mla_dims_t* d) { return d->dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC); }
@@ -100,6 +119,62 @@ size_t prefill_ws_bytes(const mla_dims_t* d, int total) {
 
 int launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Host-side checks shared by both decode entry points; MLA_OK means go on.
+int decode_args_ok(const mla_dims_t* dims, const void* q_abs, const void* pool, int32_t num_pages,
+                   const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                   int32_t max_seq_len, const void* w_uv, void* out) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || max_seq_len < 0 || num_pages < 0 || max_pages_per_seq < 0) return MLA_ERR_ARG;
+  if (batch > kMaxDecodeBatch) return MLA_ERR_DIMS;
+  if (batch == 0) return 1;  // nothing to do
+  if (!q_abs || !pool || !block_table || !seq_lens || !w_uv || !out) return MLA_ERR_NULL;
+  if (num_pages < 1) return MLA_ERR_ARG;
+  if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * dims->page_size) return MLA_ERR_CAPACITY;
+  return MLA_OK;
+}
+
+// Launch the decode with partial buffers laid out in `ws` as L says.
+int decode_launch(const mla_dims_t* dims, const void* q_abs, const void* pool, int32_t num_pages,
+                  const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                  int32_t max_seq_len, const void* w_uv, void* out, float* lse, char* ws, const DecodeLayout& L,
+                  hipStream_t stream) {
+  int* err = device_error_word();
+  if (!err) return MLA_ERR_HIP;
+  DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.q_abs = q_abs;
+  a.pool = pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.w_uv = w_uv;
+  a.out = out;
+  a.lse = lse;
+  a.part_acc = (float*)ws;
+  a.part_ml = (float*)(ws + L.acc_bytes);
+  a.plan = (int*)(ws + L.acc_bytes + L.ml_bytes);
+  a.batch = batch;
+  a.H = dims->num_heads;
+  a.d_c = dims->d_c;
+  a.d_r = dims->d_r;
+  a.d_v = dims->v_head;
+  a.P = dims->page_size;
+  a.max_pages_per_seq = max_pages_per_seq;
+  a.len_cap = max_seq_len;
+  a.slots = L.slots;
+  a.max_items = L.max_items;
+  a.min_chunk = 256;
+  // partial (m, l, acc) written and read back, in cache-row equivalents
+  a.ovh_tokens = (int)((2.0 * dims->num_heads * (dims->d_c + 2) * 4.0) /
+                       ((double)(dims->d_c + dims->d_r) * cache_elem_bytes(dims)));
+  a.scale_log2 = dims->softmax_scale * kLog2e;
+  a.fp8 = fp8_cache(dims) ? 1 : 0;
+  a.num_pages = num_pages;
+  a.err = err;
+  if (decode_fast(dims, batch)) return launched(decode_mfma(a, stream));
+  return launched(decode_generic(a, dims->dtype == MLA_BF16, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,7 +215,7 @@ int mla_uses_fast_path(const mla_dims_t* dims, int32_t op) {
   switch (op) {
     case 0: return write_fast(dims) ? 1 : 0;
     case 1: return absorb_fast(dims) ? 1 : 0;
-    case 2: return decode_fast(dims, 1) ? 1 : 0;
+    case 2: return decode_fast(dims, kMaxDecodeBatch) ? 1 : 0;  // every accepted batch takes the same path
     case 3: return (prefill_fast(dims) && !fp8_cache(dims)) ? 1 : 0;
     default: return MLA_ERR_ARG;
   }
@@ -154,18 +229,21 @@ int mla_write_cache_ws(const mla_dims_t* dims, const void* h, const void* w_dkr,
   if (n_tokens < 0 || num_pages < 0) return MLA_ERR_ARG;
   if (n_tokens == 0) return MLA_OK;
   if (!h || !w_dkr || !positions || !slot_mapping || !pool) return MLA_ERR_NULL;
+  if (num_pages < 1) return MLA_ERR_ARG;
   const size_t need = mla_write_cache_workspace_size(dims, n_tokens);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  int* err = device_error_word();
+  if (!err) return MLA_ERR_HIP;
   const bool f8 = fp8_cache(dims);
   // 8-bit cache: the bf16 rows go to the workspace (row n at row n), then
   // each is quantized into its slot
   WriteCacheArgs a{h, w_dkr, positions, slot_mapping, f8 ? workspace : pool, n_tokens, dims->hidden, dims->d_c,
-                   dims->d_r, dims->page_size, dims->rope_base, f8 ? 1 : 0};
+                   dims->d_r, dims->page_size, dims->rope_base, f8 ? 1 : 0, num_pages, err};
   hipError_t e = write_fast(dims) ? write_cache_mfma(a, stream)
                                   : write_cache_generic(a, dims->dtype == MLA_BF16, stream);
   if (e != hipSuccess || !f8) return launched(e);
   return launched(quantize_rows_fp8((const uint16_t*)workspace, slot_mapping, pool, n_tokens, dims->d_c + dims->d_r,
-                                    dims->page_size, stream));
+                                    dims->page_size, num_pages, err, stream));
 }
 
 int mla_write_cache(const mla_dims_t* dims, const void* h, const void* w_dkr, const int32_t* positions,
@@ -198,47 +276,15 @@ int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int3
                const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
                int32_t max_seq_len, const void* w_uv, void* out, float* lse, void* workspace,
                size_t workspace_bytes, hipStream_t stream) {
-  int st = check_dims(dims);
-  if (st != MLA_OK) return st;
-  if (batch < 0 || max_seq_len < 0 || num_pages < 0 || max_pages_per_seq < 0) return MLA_ERR_ARG;
-  if (batch > kMaxDecodeBatch) return MLA_ERR_DIMS;
-  if (batch == 0) return MLA_OK;
-  if (!q_abs || !pool || !block_table || !seq_lens || !w_uv || !out || !workspace) return MLA_ERR_NULL;
-  if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * dims->page_size) return MLA_ERR_CAPACITY;
+  const int st = decode_args_ok(dims, q_abs, pool, num_pages, block_table, max_pages_per_seq, seq_lens, batch,
+                                max_seq_len, w_uv, out);
+  if (st != MLA_OK) return st == 1 ? MLA_OK : st;
+  if (!workspace) return MLA_ERR_NULL;
   DecodeLayout L;
   if (!decode_layout(dims, batch, max_seq_len, L)) return MLA_ERR_HIP;
   if (workspace_bytes < L.total()) return MLA_ERR_WORKSPACE;
-  DecodeArgs a;
-  memset(&a, 0, sizeof a);
-  a.q_abs = q_abs;
-  a.pool = pool;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.w_uv = w_uv;
-  a.out = out;
-  a.lse = lse;
-  a.part_acc = (float*)workspace;
-  a.part_ml = (float*)((char*)workspace + L.acc_bytes);
-  a.plan = (int*)((char*)workspace + L.acc_bytes + L.ml_bytes);
-  a.batch = batch;
-  a.H = dims->num_heads;
-  a.d_c = dims->d_c;
-  a.d_r = dims->d_r;
-  a.d_v = dims->v_head;
-  a.P = dims->page_size;
-  a.max_pages_per_seq = max_pages_per_seq;
-  a.len_cap = max_seq_len;
-  a.slots = L.slots;
-  a.max_items = L.max_items;
-  a.min_chunk = 256;
-  // partial (m, l, acc) written and read back, in cache-row equivalents
-  a.ovh_tokens = (int)((2.0 * dims->num_heads * (dims->d_c + 2) * 4.0) /
-                       ((double)(dims->d_c + dims->d_r) * cache_elem_bytes(dims)));
-  a.scale_log2 = dims->softmax_scale * kLog2e;
-  a.fp8 = fp8_cache(dims) ? 1 : 0;
-  // the MFMA path addresses partials with 32-bit offsets
-  if (decode_fast(dims, batch) && L.acc_bytes < ((size_t)1 << 32)) return launched(decode_mfma(a, stream));
-  return launched(decode_generic(a, dims->dtype == MLA_BF16, stream));
+  return decode_launch(dims, q_abs, pool, num_pages, block_table, max_pages_per_seq, seq_lens, batch, max_seq_len,
+                       w_uv, out, lse, (char*)workspace, L, stream);
 }
 
 size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t total_tokens) {
@@ -262,8 +308,11 @@ int mla_prefill_kv(const mla_dims_t* dims, const void* q, const void* pool, int3
   if (num_seqs == 0 || total_q == 0) return MLA_OK;
   if (!q || !pool || !block_table || !cu_seqlens_q || !cu_seqlens_kv || !w_uk || !w_uv || !out || !workspace)
     return MLA_ERR_NULL;
+  if (num_pages < 1) return MLA_ERR_ARG;
   if ((int64_t)max_kv_len > (int64_t)max_pages_per_seq * dims->page_size) return MLA_ERR_CAPACITY;
   if (workspace_bytes < prefill_ws_bytes(dims, total_kv)) return MLA_ERR_WORKSPACE;
+  int* err = device_error_word();
+  if (!err) return MLA_ERR_HIP;
   size_t kb = (size_t)total_kv * dims->num_heads * dims->qk_nope * sizeof(float);
   kb = (kb + 255) & ~(size_t)255;
   PrefillArgs a;
@@ -292,6 +341,9 @@ int mla_prefill_kv(const mla_dims_t* dims, const void* q, const void* pool, int3
   a.max_pages_per_seq = max_pages_per_seq;
   a.rope_base = dims->rope_base;
   a.scale = dims->softmax_scale;
+  a.max_kv_len = max_kv_len;
+  a.num_pages = num_pages;
+  a.err = err;
   if (prefill_fast(dims)) return launched(prefill_mfma(a, stream));
   return launched(prefill_generic(a, dims->dtype == MLA_BF16, stream));
 }
@@ -305,5 +357,20 @@ int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t
                         total_tokens, total_tokens, max_seq_len, max_seq_len, w_uk, w_uv, out, lse, workspace,
                         workspace_bytes, stream);
 }
+
+int mla_get_device_error(int32_t* error_bits, hipStream_t stream) {
+  if (!error_bits) return MLA_ERR_NULL;
+  *error_bits = 0;
+  int* err = device_error_word();
+  if (!err) return MLA_ERR_HIP;
+  int v = 0;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MLA_ERR_HIP;
+  if (hipMemcpy(&v, err, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
+  if (v != 0 && hipMemset(err, 0, sizeof v) != hipSuccess) return MLA_ERR_HIP;
+  *error_bits = v;
+  return MLA_OK;
+}
+
+int mla_debug_build(void) { return kChecked ? 1 : 0; }
 
 }  // extern "C"

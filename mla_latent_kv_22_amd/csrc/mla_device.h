@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mla_checks.h"
+
 namespace mla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -132,12 +134,14 @@ struct DecodePlan {
   int n_items;
 };
 
-__device__ __forceinline__ int clamp_len(int len, int cap) { return len < 0 ? 0 : (len > cap ? cap : len); }
+__device__ __forceinline__ int clamp_len(int len, int cap, int* err) { return clamp_report(len, 0, cap, err); }
 
 // Candidate chunk sizes: the total token count spread over k * slots items
 // for k = 1, 2, 4, rounded up to 32 and clamped to [min_chunk, max_chunk].  The chosen one
 // minimises (rounds of `slots` items) * chunk + the partial-result overhead
-// (ovh_tokens token-equivalents per item, spread over the slots).
+// (ovh_tokens token-equivalents per item, spread over the slots), among the
+// candidates whose item count fits the partial buffers (max_items; the host
+// sizes them so that k = 1 always fits).
 // The first wave computes the plan with wave reductions (no barrier inside);
 // one barrier then publishes it.  s_len, s_items: LDS, >= batch + 1 ints;
 // red: LDS, >= 16 ints.  All threads call.
@@ -148,12 +152,12 @@ __device__ __forceinline__ long long wave_sum_ll(long long v) {
 
 __device__ inline DecodePlan make_decode_plan(const int32_t* __restrict__ seq_lens, int batch, int cap,
                                               int slots, int min_chunk, int max_chunk, int ovh_tokens, int* s_len,
-                                              int* s_items, int* red) {
+                                              int* s_items, int* red, int* err, int max_items) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     long long part = 0;
     for (int b = lane; b < batch; b += 64) {
-      const int L = clamp_len(seq_lens[b], cap);
+      const int L = clamp_len(seq_lens[b], cap, blockIdx.x == 0 ? err : nullptr);
       s_len[b] = L;
       part += L;
     }
@@ -168,6 +172,7 @@ __device__ inline DecodePlan make_decode_plan(const int32_t* __restrict__ seq_le
       long long it = 0;
       for (int b = lane; b < batch; b += 64) it += (s_len[b] + ch - 1) / ch;  // this lane's own entries
       it = wave_sum_ll(it);
+      if (k > 1 && it > max_items) continue;
       const long long rounds = (it + slots - 1) / slots;
       const long long cost = rounds * ch + (it * ovh_tokens) / slots;
       if (best_cost < 0 || cost < best_cost) {

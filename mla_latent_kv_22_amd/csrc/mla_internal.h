@@ -26,6 +26,8 @@ struct WriteCacheArgs {
   int n_tokens, D, d_c, d_r, P;
   float rope_base;
   int dense;  // 1: row n goes to row n of `pool` (a [n_tokens][R] staging buffer), slots unused
+  int num_pages;
+  int* err;   // device error word (set by MLA_DEBUG builds only)
 };
 
 struct AbsorbArgs {
@@ -55,6 +57,8 @@ struct DecodeArgs {
   int min_chunk, ovh_tokens;
   float scale_log2; // softmax_scale * log2(e)
   int fp8;          // 1: 8-bit pool (E4M3 rows + float32 row scales per page)
+  int num_pages;
+  int* err;         // device error word (set by MLA_DEBUG builds only)
 };
 
 struct PrefillArgs {
@@ -71,12 +75,15 @@ struct PrefillArgs {
   void* ws_v;  // up-projected V:   fp32 [total_kv, H, d_v] (generic) or bf16 [H, total_kv, d_v] (MFMA)
   int num_seqs, total, total_kv, max_seq_len, H, d_n, d_r, d_c, d_v, P, max_pages_per_seq;
   float rope_base, scale;
+  int max_kv_len;  // bound of every sequence's key count (max_seq_len bounds its new tokens)
+  int num_pages;
+  int* err;        // device error word (set by MLA_DEBUG builds only)
 };
 
 // 8-bit cache: quantize the bf16 rows of a [n_tokens][R] staging buffer into
 // their slots of an 8-bit pool
 hipError_t quantize_rows_fp8(const uint16_t* rows, const int64_t* slots, void* pool8, int n_tokens, int R, int P,
-                             hipStream_t s);
+                             int num_pages, int* err, hipStream_t s);
 
 // generic kernels (any shape, fp32 or bf16 storage)
 hipError_t write_cache_generic(const WriteCacheArgs& a, bool bf16, hipStream_t s);

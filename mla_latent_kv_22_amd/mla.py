@@ -8,6 +8,7 @@ does, and raises if it is missing.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -16,6 +17,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla.so")
+# the same ABI built with MLA_DEBUG: device-side index checks and the error word
+DEBUG_LIB_PATH = os.path.join(_HERE, "libmla_debug.so")
 
 F32, BF16 = 0, 1
 FLAG_GENERIC = 1
@@ -24,7 +27,9 @@ OP_WRITE_CACHE, OP_ABSORB_Q, OP_DECODE, OP_PREFILL = 0, 1, 2, 3
 
 _SYMBOLS = ("mla_write_cache", "mla_write_cache_ws", "mla_write_cache_workspace_size", "mla_absorb_q",
             "mla_decode_workspace_size", "mla_decode", "mla_prefill_workspace_size", "mla_prefill",
-            "mla_prefill_kv", "mla_cache_bytes", "mla_page_bytes", "mla_status_string", "mla_uses_fast_path")
+            "mla_prefill_kv", "mla_cache_bytes", "mla_page_bytes", "mla_status_string", "mla_uses_fast_path",
+            "mla_get_device_error", "mla_debug_build")
+DEVERR_PAGE, DEVERR_SLOT, DEVERR_LENGTH = 1, 2, 4
 
 
 class Dims(ctypes.Structure):
@@ -40,16 +45,29 @@ class MLAError(RuntimeError):
         self.status = status
 
 
-_lib = None
+_libs = {}
+_use_debug = False
+
+
+@contextlib.contextmanager
+def debug_library():
+    """Route the calls of this module through libmla_debug.so inside the block."""
+    global _use_debug
+    old, _use_debug = _use_debug, True
+    try:
+        yield lib()
+    finally:
+        _use_debug = old
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded library (raises if it has not been built)."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mla_latent_kv_22_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
+    """The loaded library (raises if it has not been built): libmla.so, or
+    libmla_debug.so inside ``debug_library()``."""
+    path = DEBUG_LIB_PATH if _use_debug else LIB_PATH
+    if path not in _libs:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m mla_latent_kv_22_amd.build`")
+        L = ctypes.CDLL(path)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         dp = ctypes.POINTER(Dims)
         L.mla_write_cache.argtypes = [dp, vp, vp, vp, vp, i32, vp, i32, vp]
@@ -72,11 +90,13 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_uses_fast_path.argtypes = [dp, i32]
+        L.mla_get_device_error.argtypes = [ctypes.POINTER(ctypes.c_int32), vp]
+        L.mla_debug_build.argtypes = []
         for f in ("mla_write_cache", "mla_write_cache_ws", "mla_absorb_q", "mla_decode", "mla_prefill",
-                  "mla_prefill_kv", "mla_uses_fast_path"):
+                  "mla_prefill_kv", "mla_uses_fast_path", "mla_get_device_error", "mla_debug_build"):
             getattr(L, f).restype = ctypes.c_int
-        _lib = L
-    return _lib
+        _libs[path] = L
+    return _libs[path]
 
 
 def status_string(status: int) -> str:
@@ -209,3 +229,15 @@ def cache_bytes(d: Dims, tokens: int, layers: int) -> int:
 
 def uses_fast_path(d: Dims, op: int) -> int:
     return int(lib().mla_uses_fast_path(ctypes.byref(d), int(op)))
+
+
+def get_device_error(stream=None) -> int:
+    """mla_get_device_error: waits for the stream, returns and clears the
+    device error word (MLA_DEVERR_* bits)."""
+    v = ctypes.c_int32(0)
+    _check(lib().mla_get_device_error(ctypes.byref(v), _stream(stream)), "mla_get_device_error")
+    return int(v.value)
+
+
+def debug_build() -> bool:
+    return bool(lib().mla_debug_build())

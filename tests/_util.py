@@ -9,6 +9,17 @@ import oracle as O
 
 # max relative error per output tensor: ||g - o||_inf / ||o||_inf
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# max absolute error of the natural-log LSE (values of order ln T + score)
+LSE_TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def spike_lse_tol(dtype, lse_ref) -> float:
+    """LSE bound where one score dominates and is huge (the spike tests): the
+    bf16 absorbed query carries a relative rounding of up to 2^-9 per element,
+    which moves a score whose terms all share one sign by up to 2^-9 of its
+    value, and the LSE follows that score."""
+    big = float(np.max(np.abs(np.asarray(lse_ref)[np.isfinite(lse_ref)]), initial=0.0))
+    return LSE_TOL[dtype] + (2.0 ** -9 * big if dtype == "bf16" else 0.0)
 
 
 def rel_err(g, o) -> float:
@@ -22,15 +33,16 @@ def rel_err(g, o) -> float:
 
 
 def lse_err(g, o) -> float:
-    """LSE compared on its own scale (values of order log T): absolute error
-    divided by max(1, max |o|)."""
+    """Largest absolute LSE error; entries that are -inf on both sides (empty
+    sequences) count as equal, a -inf on one side only as infinitely wrong."""
     g = np.asarray(g, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
-    both_inf = np.isneginf(g) & np.isneginf(o)
     if np.any(np.isneginf(g) != np.isneginf(o)) or np.isnan(g).any():
         return float("inf")
-    d = np.where(both_inf, 0.0, np.abs(g - o))
-    return float(np.max(d) / max(1.0, float(np.max(np.abs(np.where(both_inf, 0.0, o))))))
+    fin = ~np.isneginf(o)
+    if not np.any(fin):
+        return 0.0
+    return float(np.max(np.abs(g[fin] - o[fin])))
 
 
 def full_path(cfg) -> bool:

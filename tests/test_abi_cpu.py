@@ -54,6 +54,31 @@ def test_cache_bytes_formula():
     assert mla.cache_bytes(_dims(d_c=3), 1, 1) == 0
 
 
+def test_debug_library_same_abi():
+    """libmla_debug.so (MLA_DEBUG: device-side index checks) exports the same
+    symbols and says which build it is; the release library never reports a
+    device error."""
+    assert not mla.debug_build()
+    rel = mla.lib()
+    with mla.debug_library() as dbg:
+        assert dbg is not rel
+        assert mla.debug_build()
+        for n in _declared():
+            assert hasattr(dbg, n), n
+    assert mla.lib() is rel
+    assert rel.mla_get_device_error(None, None) == -1
+
+
+def test_empty_pool_rejected():
+    L = mla.lib()
+    d = _dims()
+    assert L.mla_write_cache(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, None) == -7
+    assert L.mla_decode(ctypes.byref(d), FAKE, FAKE, 0, FAKE, 4, FAKE, 2, 64, FAKE, FAKE, None, FAKE, 1 << 30,
+                        None) == -7
+    assert L.mla_prefill(ctypes.byref(d), FAKE, FAKE, 0, FAKE, 4, FAKE, 2, 64, 32, FAKE, FAKE, FAKE, None, FAKE,
+                         1 << 30, None) == -7
+
+
 def test_fast_path_selection():
     assert mla.uses_fast_path(_dims(), mla.OP_DECODE) == 1
     assert mla.uses_fast_path(_dims(num_heads=16), mla.OP_DECODE) == 1
@@ -72,7 +97,8 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=5), -3), (dict(d_c=3), -2), (dict(d_r=0), -2), (dict(num_heads=0), -2), (dict(flags=4), -7),
-    (dict(rope_base=-1.0), -7), (dict(softmax_scale=float("inf")), -7), (dict(page_size=0), -2)])
+    (dict(rope_base=-1.0), -7), (dict(softmax_scale=float("inf")), -7), (dict(page_size=0), -2),
+    (dict(softmax_scale=0.0), -7), (dict(softmax_scale=-0.07), -7), (dict(softmax_scale=float("nan")), -7)])
 def test_bad_dims_rejected(kw, code):
     d = _dims()
     for k, v in kw.items():

@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 from mla_latent_kv_22_amd import harness, inputs as I, mla
-from tests._util import TOL, lse_err, need_gpu, oracle_decode, rel_err, seq_rows
+from tests._util import LSE_TOL, TOL, lse_err, need_gpu, oracle_decode, rel_err, seq_rows, spike_lse_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -116,7 +116,7 @@ def _run_step(cfg, inp, flags=0):
     return st
 
 
-def _check(cfg, inp, st, seqs, heads=None):
+def _check(cfg, inp, st, seqs, heads=None, spike=False):
     o_ref, l_ref = oracle_decode(cfg, inp, seqs, heads)
     out = O.from_storage(harness.to_host_bits(st.out), cfg.dtype)[seqs]
     lse = st.lse.cpu().numpy().astype(np.float64)[seqs]
@@ -125,7 +125,7 @@ def _check(cfg, inp, st, seqs, heads=None):
     e_o, e_l = rel_err(out, o_ref), lse_err(lse, l_ref)
     print(f"  out rel err {e_o:.3e}  lse err {e_l:.3e}", flush=True)
     assert e_o < TOL[cfg.dtype]
-    assert e_l < TOL[cfg.dtype]
+    assert e_l < (spike_lse_tol(cfg.dtype, l_ref) if spike else LSE_TOL[cfg.dtype])
 
 
 def test_decode_tiny_f32_full_path():
@@ -231,20 +231,21 @@ def test_position_branch_matters_on_gpu():
 @pytest.mark.slow
 def test_decode_v3_full_size():
     """B=64, T=8192, H=128 in the launch configuration the benchmark times;
-    the oracle checks two sequences over all heads and two more over 16 heads."""
+    the oracle checks every sequence over every head."""
     need_gpu()
     _case("decode v3 full size")
     cfg = I.V3
     inp = I.make(cfg, 0)
     st = _run_step(cfg, inp)
-    _check(cfg, inp, st, [0, 41])
-    _check(cfg, inp, st, [17, 63], heads=list(range(0, 128, 8)))
+    assert mla.uses_fast_path(st.d, mla.OP_DECODE) == 1
+    for b0 in range(0, cfg.batch, 16):
+        _check(cfg, inp, st, list(range(b0, b0 + 16)))
 
 
 @pytest.mark.slow
 def test_decode_ragged_paged_full_size():
     """B=128, lengths U{512..32768}, random page permutation: the longest, the
-    shortest and two seeded sequences, 12 heads each."""
+    shortest and two seeded sequences, every head."""
     need_gpu()
     _case("decode ragged paged full size")
     cfg = I.RAGGED
@@ -252,7 +253,7 @@ def test_decode_ragged_paged_full_size():
     st = _run_step(cfg, inp)
     lens = inp["seq_lens"]
     seqs = [int(np.argmax(lens)), int(np.argmin(lens))] + [int(x) for x in np.random.default_rng(1).choice(128, 2)]
-    _check(cfg, inp, st, seqs, heads=[0, 1, 31, 32, 63, 64, 65, 95, 96, 100, 126, 127])
+    _check(cfg, inp, st, seqs)
 
 
 @pytest.mark.parametrize("flags,amp", [(0, 40.0), (mla.FLAG_GENERIC, 40.0), (0, 13.0), (0, 17.0)],
@@ -278,4 +279,4 @@ def test_decode_score_spike_far_above_first_tile(flags, amp):
     rows[inp["block_table"][1, t_spike // P], t_spike % P] = I.f32_to_bf16_bits(spike)
     inp["rows"] = rows
     st = _run_step(cfg, inp, flags)
-    _check(cfg, inp, st, [0, 1, 2])
+    _check(cfg, inp, st, [0, 1, 2], spike=True)

@@ -9,7 +9,7 @@ import torch
 
 import oracle as O
 from mla_latent_kv_22_amd import harness, inputs as I, mla
-from tests._util import TOL, lse_err, need_gpu, rel_err
+from tests._util import LSE_TOL, TOL, lse_err, need_gpu, rel_err, spike_lse_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -142,8 +142,10 @@ def test_fp8_decode_parity(cfg, flags, lens):
     _case(f"fp8 decode {cfg.name} H={cfg.num_heads} flags={flags} lens={lens}")
     d, out, lse, o_ref, l_ref = _decode_case(cfg, flags, 21, lens)
     e_o, e_l = rel_err(out, o_ref), lse_err(lse, l_ref)
-    print(f"  fast={mla.uses_fast_path(d, mla.OP_DECODE)} out rel err {e_o:.3e}  lse err {e_l:.3e}", flush=True)
-    assert e_o < TOL["bf16"] and e_l < TOL["bf16"]
+    fast = mla.uses_fast_path(d, mla.OP_DECODE)
+    print(f"  fast={fast} out rel err {e_o:.3e}  lse err {e_l:.3e}", flush=True)
+    assert fast == (0 if flags & mla.FLAG_GENERIC else 1)
+    assert e_o < TOL["bf16"] and e_l < LSE_TOL["bf16"]
 
 
 def _e4m3_code(v):
@@ -188,7 +190,7 @@ def test_fp8_score_spike_far_above_first_tile(flags, mag, scale):
                             cfg.softmax_scale, cfg.rope_base)
     e_o, e_l = rel_err(out, o_ref), lse_err(lse, l_ref)
     print(f"  out rel err {e_o:.3e}  lse err {e_l:.3e}", flush=True)
-    assert e_o < TOL["bf16"] and e_l < TOL["bf16"]
+    assert e_o < TOL["bf16"] and e_l < spike_lse_tol("bf16", l_ref)
 
 
 def test_fp8_page_permutation_bit_invariance_and_determinism():
@@ -247,4 +249,4 @@ def test_fp8_decode_v3_full_size():
         hs = list(range(cfg.num_heads)) if heads is None else heads
         e_o, e_l = rel_err(out[b, hs], o_ref[hs]), lse_err(lse[b, hs], l_ref[hs])
         print(f"  seq {b}: out rel err {e_o:.3e}  lse err {e_l:.3e}", flush=True)
-        assert e_o < TOL["bf16"] and e_l < TOL["bf16"]
+        assert e_o < TOL["bf16"] and e_l < LSE_TOL["bf16"]

@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 from mla_latent_kv_22_amd import harness, inputs as I
-from tests._util import TOL, lse_err, need_gpu, rel_err, seq_rows
+from tests._util import LSE_TOL, TOL, lse_err, need_gpu, rel_err, seq_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def _check(cfg, inp, pf, seq, queries=None, heads=None):
     sel = np.ix_(qi, hi)
     e_o, e_l = rel_err(out[sel], o_ref[sel]), lse_err(lse[sel], l_ref[sel])
     print(f"  seq {seq}: out rel err {e_o:.3e}  lse err {e_l:.3e}", flush=True)
-    assert e_o < TOL[cfg.dtype] and e_l < TOL[cfg.dtype]
+    assert e_o < TOL[cfg.dtype] and e_l < LSE_TOL[cfg.dtype]
 
 
 @pytest.mark.parametrize("cfg", [
@@ -119,7 +119,7 @@ def test_prefill_onto_prefix(cfg):
         e_f = rel_err(o, o_full)
         print(f"  seq {s}: prefix {P} new {L}: out rel err {e_o:.3e} lse err {e_l:.3e}, vs fresh prefill {e_f:.3e}",
               flush=True)
-        assert e_o < TOL[cfg.dtype] and e_l < TOL[cfg.dtype]
+        assert e_o < TOL[cfg.dtype] and e_l < LSE_TOL[cfg.dtype]
         # tiles are aligned to key positions and each query meets the same
         # tiles in the same order, so the rows agree with the fresh prefill
         assert e_f < TOL[cfg.dtype]
@@ -149,4 +149,4 @@ def test_prefill_onto_prefix_full_size_sampled():
         lg = lse[a:a + L].cpu().numpy().astype(np.float64)
         e_o, e_l = rel_err(o[picks], o_ref[picks]), lse_err(lg[picks], l_ref[picks])
         print(f"  seq {s}: prefix {P}: out rel err {e_o:.3e} lse err {e_l:.3e}", flush=True)
-        assert e_o < TOL[cfg.dtype] and e_l < TOL[cfg.dtype]
+        assert e_o < TOL[cfg.dtype] and e_l < LSE_TOL[cfg.dtype]

@@ -54,8 +54,13 @@ def test_cache_bytes_v3():
     per_head = O.gqa_cache_bytes_per_token(e["layers"], r["heads"], r["head_dim"], e["elem_bytes"])
     assert round(per_head * e8["tokens"] / 2**30, 2) == e8["printed_per_head_gib"]
     assert round(per_head / per_tok, 1) == e8["printed_ratio"]
-    # the head count does not enter the MLA figure
-    assert O.mla_cache_bytes_per_token(61, 512, 64, 2) == O.mla_cache_bytes_per_token(61, 512, 64, 2)
+    # the head count does not enter the MLA figure: per token it equals the
+    # uniform-GQA formula with the 2.25 KV-head groups LLMScale prints
+    # (at the 128-wide heads of that comparison), whatever the query heads
+    groups = _golden()["scale_v2_groups"]["printed_groups"]
+    assert O.gqa_cache_bytes_per_token(e["layers"], groups, 128, e["elem_bytes"]) == per_tok
+    for heads in (16, 128):
+        assert O.gqa_cache_bytes_per_token(e["layers"], heads, 128, e["elem_bytes"]) / per_tok == heads / groups
 
 
 def test_gqa_equivalent_groups():
@@ -706,6 +711,47 @@ def _mut_prefill_prefix_position(q, rows, w_uk, w_uv, d_c, sigma, base, queries=
     return o, lse
 
 
+def _wuk_as_transposed(w_uk):
+    """W_UK [H, d_n, d_c] read with the layout [H, d_c, d_n] (a row-major
+    buffer taken in the wrong order), given back as [H, d_n, d_c]."""
+    H, d_n, d_c = w_uk.shape
+    return np.ascontiguousarray(w_uk).reshape(H, d_c, d_n).transpose(0, 2, 1)
+
+
+def _mut_wuk_transposed(orig, pos):
+    """An oracle function that reads its W_UK argument (position pos) with
+    the transposed layout.  Applied to decode, prefill, absorption and the
+    logits alike, the oracle stays self-consistent, so only pins with their
+    own indexing of W_UK can catch it."""
+    def f(*args, **kw):
+        args = list(args)
+        args[pos] = _wuk_as_transposed(np.asarray(args[pos]))
+        return orig(*args, **kw)
+    return f
+
+
+# position of the W_UK argument of each oracle function
+_WUK_ARG = {"decode_one": 2, "prefill_one": 2, "absorb_query": 1, "nonabsorbed_logits": 2}
+
+
+def _mut_prefill_no_mask(q, rows, w_uk, w_uv, d_c, sigma, base, queries=None, heads=None, prefix=0):
+    """prefill with the causal mask dropped: every query sees every row."""
+    T, H, _ = q.shape
+    d_n = w_uk.shape[1]
+    o = np.full((T, H, w_uv.shape[1]), np.nan)
+    lse = np.full((T, H), np.nan)
+    for h in (range(H) if heads is None else heads):
+        K = rows[:, :d_c] @ w_uk[h].T
+        V = rows[:, :d_c] @ w_uv[h].T
+        for i in (range(T) if queries is None else queries):
+            s = sigma * (K @ q[i, h, :d_n] + rows[:, d_c:] @ O.rope(q[i, h, d_n:], prefix + i, base))
+            m = s.max()
+            w = np.exp(s - m)
+            o[i, h] = (w @ V) / w.sum()
+            lse[i, h] = m + math.log(w.sum())
+    return o, lse
+
+
 def _mut_attend_log2(scores, values):
     m = float(np.max(scores))
     w = np.exp(scores - m)
@@ -744,7 +790,8 @@ def _mut_unpack_scales_first(pages, P, R):
 
 @pytest.mark.parametrize("mutation", ["rope_sign", "rope_pairing", "drop_kr", "sigma_content_only",
                                       "causal_off_by_one", "lse_log2", "prefix_position",
-                                      "fp8_ties_away", "fp8_scale_exponent", "fp8_scales_first"])
+                                      "fp8_ties_away", "fp8_scale_exponent", "fp8_scales_first",
+                                      "wuk_transposed", "causal_mask_dropped"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     import oracle.mla_oracle as M
 
@@ -771,6 +818,11 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
         patch("row_scale_exponent", _mut_scale_exponent_plus_one)
     elif mutation == "fp8_scales_first":
         patch("unpack_fp8_pages", _mut_unpack_scales_first)
+    elif mutation == "wuk_transposed":
+        for name, pos in _WUK_ARG.items():
+            patch(name, _mut_wuk_transposed(getattr(M, name), pos))
+    elif mutation == "causal_mask_dropped":
+        patch("prefill_one", _mut_prefill_no_mask)
     pins = [test_rope_closed_forms, lambda: test_brute_force_decode(0), lambda: test_brute_force_prefill(0),
             test_absorbed_equals_sdpa_mqa, test_causal_prefill_equals_sdpa_causal,
             test_absorbed_and_nonabsorbed_logits_agree, test_single_token_context,
