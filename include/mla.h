@@ -210,6 +210,31 @@ int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int3
                int32_t batch, int32_t max_seq_len, const void* w_uv, void* out, float* lse,
                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments, results and errors as mla_decode, without the
+ * workspace.  The split pass keeps its partial results in a device array
+ * inside the library, MLA_NOALLOC_SCRATCH_BYTES per device, which each device
+ * holds from the library's load until the process ends.  The call allocates
+ * nothing and calls no allocating routine.
+ * Size limit: the plan needs up to max(S, ceil(batch * max_seq_len / 8192)) +
+ * batch work items of num_heads * (d_c + 2) * 4 bytes each, where S is the
+ * number of split work-groups the device holds at once (its CU count, or
+ * twice that for a bf16 cache with num_heads <= 32); a call whose items do
+ * not fit returns MLA_ERR_WORKSPACE and launches nothing.  At num_heads 128,
+ * d_c 512 on a 256-CU MI355X that is about 510 items, for example 64
+ * sequences of up to 57k tokens or 192 of up to 8k.
+ * Every call on one device shares its array and leaves its last contents
+ * there: calls on one device that overlap (other streams, other threads)
+ * race.  Nothing in the array needs clearing between calls.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int mla_decode_noalloc(const mla_dims_t* dims, const void* q_abs, const void* pool, int32_t num_pages,
+                       const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                       int32_t batch, int32_t max_seq_len, const void* w_uv, void* out, float* lse,
+                       hipStream_t stream);
+
 /* Bytes of workspace mla_prefill needs for `total_tokens` query tokens, and
  * mla_prefill_kv for `total_tokens` key tokens (pass its total_kv). */
 size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t total_tokens);

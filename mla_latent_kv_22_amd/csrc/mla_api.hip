@@ -175,6 +175,49 @@ int decode_launch(const mla_dims_t* dims, const void* q_abs, const void* pool, i
   return launched(decode_generic(a, dims->dtype == MLA_BF16, stream));
 }
 
+// ---------------------------------------------------------------- no-alloc decode
+// mla_decode_noalloc keeps the partial results of the split pass in this
+// file-scope device array (each device holds its own copy until the process
+// ends) instead of a caller's workspace.  In host code `scratch` only stands
+// for the symbol: kernels, copies and fills get the per-device address that
+// hipGetSymbolAddress returns, never the name itself.
+constexpr size_t kNoAllocScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device and kept.
+char* scratch_address() {
+  static std::atomic<char*> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  char* p = cache[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  char* ptr = nullptr;
+  if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  cache[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
+// Layout of the partial buffers in `bytes` of scratch: as many items as fit.
+// Returns MLA_ERR_WORKSPACE when even the smallest plan (one chunk per slot,
+// see make_decode_plan) does not fit.
+int decode_layout_in(const mla_dims_t* d, int batch, int max_seq_len, size_t bytes, DecodeLayout& L) {
+  if (!decode_layout(d, batch, max_seq_len, L)) return MLA_ERR_HIP;
+  const size_t per_item = (size_t)d->num_heads * ((size_t)d->d_c + 2) * sizeof(float);
+  const size_t fixed = L.plan_bytes + 512;  // plan, and the 256-byte roundings of the two arrays
+  if (bytes <= fixed) return MLA_ERR_WORKSPACE;
+  const long long cap = (long long)((bytes - fixed) / per_item);
+  const long long by_len = ((long long)batch * max_seq_len + kMaxChunk - 1) / kMaxChunk;
+  const long long need = (by_len > L.slots ? by_len : L.slots) + batch;
+  if (need > cap) return MLA_ERR_WORKSPACE;
+  if (cap < L.max_items) {
+    L.max_items = (int)cap;
+    L.acc_bytes = ((size_t)L.max_items * d->num_heads * d->d_c * sizeof(float) + 255) & ~(size_t)255;
+    L.ml_bytes = ((size_t)L.max_items * d->num_heads * 2 * sizeof(float) + 255) & ~(size_t)255;
+  }
+  return L.total() <= bytes ? MLA_OK : MLA_ERR_WORKSPACE;
+}
+
 }  // namespace
 
 extern "C" {
@@ -285,6 +328,22 @@ int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int3
   if (workspace_bytes < L.total()) return MLA_ERR_WORKSPACE;
   return decode_launch(dims, q_abs, pool, num_pages, block_table, max_pages_per_seq, seq_lens, batch, max_seq_len,
                        w_uv, out, lse, (char*)workspace, L, stream);
+}
+
+int mla_decode_noalloc(const mla_dims_t* dims, const void* q_abs, const void* pool, int32_t num_pages,
+                       const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                       int32_t batch, int32_t max_seq_len, const void* w_uv, void* out, float* lse,
+                       hipStream_t stream) {
+  const int st = decode_args_ok(dims, q_abs, pool, num_pages, block_table, max_pages_per_seq, seq_lens, batch,
+                                max_seq_len, w_uv, out);
+  if (st != MLA_OK) return st == 1 ? MLA_OK : st;
+  DecodeLayout L;
+  const int lt = decode_layout_in(dims, batch, max_seq_len, kNoAllocScratchBytes, L);
+  if (lt != MLA_OK) return lt;
+  char* ws = scratch_address();
+  if (!ws) return MLA_ERR_HIP;
+  return decode_launch(dims, q_abs, pool, num_pages, block_table, max_pages_per_seq, seq_lens, batch, max_seq_len,
+                       w_uv, out, lse, ws, L, stream);
 }
 
 size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t total_tokens) {

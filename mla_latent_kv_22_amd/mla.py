@@ -28,7 +28,7 @@ OP_WRITE_CACHE, OP_ABSORB_Q, OP_DECODE, OP_PREFILL = 0, 1, 2, 3
 _SYMBOLS = ("mla_write_cache", "mla_write_cache_ws", "mla_write_cache_workspace_size", "mla_absorb_q",
             "mla_decode_workspace_size", "mla_decode", "mla_prefill_workspace_size", "mla_prefill",
             "mla_prefill_kv", "mla_cache_bytes", "mla_page_bytes", "mla_status_string", "mla_uses_fast_path",
-            "mla_get_device_error", "mla_debug_build")
+            "mla_get_device_error", "mla_debug_build", "mla_decode_noalloc")
 DEVERR_PAGE, DEVERR_SLOT, DEVERR_LENGTH = 1, 2, 4
 
 
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_workspace_size.argtypes = [dp, i32, i32]
         L.mla_decode_workspace_size.restype = sz
         L.mla_decode.argtypes = [dp, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.mla_decode_noalloc.argtypes = [dp, vp, vp, i32, vp, i32, vp, i32, i32, vp, vp, vp, vp]
         L.mla_prefill_workspace_size.argtypes = [dp, i32]
         L.mla_prefill_workspace_size.restype = sz
         L.mla_prefill.argtypes = [dp, vp, vp, i32, vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -92,7 +93,8 @@ def lib() -> ctypes.CDLL:
         L.mla_uses_fast_path.argtypes = [dp, i32]
         L.mla_get_device_error.argtypes = [ctypes.POINTER(ctypes.c_int32), vp]
         L.mla_debug_build.argtypes = []
-        for f in ("mla_write_cache", "mla_write_cache_ws", "mla_absorb_q", "mla_decode", "mla_prefill",
+        for f in ("mla_write_cache", "mla_write_cache_ws", "mla_absorb_q", "mla_decode", "mla_decode_noalloc",
+                  "mla_prefill",
                   "mla_prefill_kv", "mla_uses_fast_path", "mla_get_device_error", "mla_debug_build"):
             getattr(L, f).restype = ctypes.c_int
         _libs[path] = L
@@ -189,6 +191,19 @@ def decode(d: Dims, q_abs, pool, block_table, seq_lens, max_seq_len: int, w_uv, 
                             _ptr(out, "out", dt), _ptr(lse, "lse", torch.float32),
                             _ptr(workspace, "workspace", torch.uint8),
                             0 if workspace is None else workspace.numel(), _stream(stream)), "mla_decode")
+
+
+def decode_noalloc(d: Dims, q_abs, pool, block_table, seq_lens, max_seq_len: int, w_uv, out, lse,
+                   stream=None) -> None:
+    """mla_decode_noalloc: mla_decode with the partial results in the
+    library's own per-device scratch array (no workspace)."""
+    dt = _torch_dtype(d)
+    _check(lib().mla_decode_noalloc(ctypes.byref(d), _ptr(q_abs, "q_abs", dt), _ptr(pool, "pool", _pool_dtype(d)),
+                                    int(pool.shape[0]), _ptr(block_table, "block_table", torch.int32),
+                                    int(block_table.shape[1]), _ptr(seq_lens, "seq_lens", torch.int32),
+                                    int(seq_lens.shape[0]), int(max_seq_len), _ptr(w_uv, "w_uv", dt),
+                                    _ptr(out, "out", dt), _ptr(lse, "lse", torch.float32), _stream(stream)),
+           "mla_decode_noalloc")
 
 
 def prefill_workspace_size(d: Dims, total_tokens: int) -> int:
