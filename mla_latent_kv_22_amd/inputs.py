@@ -192,6 +192,31 @@ def make(cfg: Config, seed: int = 0, with_rows: bool = True,
                 q=q, q_positions=q_positions, cu_seqlens=cu)
 
 
+# query rank of the query compression; no workload names one, so the V3
+# shapes take DeepSeek-V3's (1536) and the tiny fp32 shape a small one
+Q_RANK = {"tiny_f32": 48}
+Q_RANK_DEFAULT = 1536
+
+
+def projection_inputs(cfg: Config, n_tokens: int, seed: int, d_cq: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Inputs of the query compression and the output projection, drawn from
+    their own stream (fixed order): W_DQ [d_cq, D], W_UQ [H, d_n + d_R, d_cq],
+    W_O [D, H d_v] ~ N(0, std^2) with the workload's weight std; hidden states
+    h [n_tokens, D] ~ N(0, 1); positions U{0 .. seq_len - 1}; attention
+    outputs o [n_tokens, H, d_v] ~ N(0, 1/64) (the order of a softmax average
+    of W_UV-projected N(0, 1) rows)."""
+    rng = np.random.default_rng(seed)
+    d_cq = d_cq or Q_RANK.get(cfg.name, Q_RANK_DEFAULT)
+    D, H = cfg.hidden, cfg.num_heads
+    w_dq = _normal(rng, (d_cq, D), cfg.weight_std, cfg.dtype)
+    w_uq = _normal(rng, (H, cfg.qk_head, d_cq), cfg.weight_std, cfg.dtype)
+    w_o = _normal(rng, (D, H * cfg.v_head), cfg.weight_std, cfg.dtype)
+    h = _normal(rng, (n_tokens, D), 1.0, cfg.dtype)
+    positions = rng.integers(0, cfg.seq_len, size=n_tokens).astype(np.int32)
+    o = _normal(rng, (n_tokens, H, cfg.v_head), 0.125, cfg.dtype)
+    return dict(d_cq=d_cq, w_dq=w_dq, w_uq=w_uq, w_o=w_o, h=h, positions=positions, o=o)
+
+
 def fp8_pages(num_pages: int, P: int, R: int, rng: np.random.Generator) -> np.ndarray:
     """Random 8-bit cache pages [num_pages, P * (R + 4)] for decode inputs:
     per page, P rows of R E4M3 codes (random sign, exponent field 4..7 so the

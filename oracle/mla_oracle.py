@@ -38,6 +38,9 @@ Readings where the pages leave a step open (all pinned by tests/test_oracle_*):
     allows 8-bit storage of the cached vector; [arch] 3 mentions its scales):
     E4M3 codes of the bf16 row over one power-of-two scale per row, nearest
     code with ties to even; see the section "8-bit cache rows" below.
+  * Query compression and output projection ([blog] "MLA nasil calisir?",
+    [arch] 1): c_Q = W_DQ h, per head [q_C | q_R] = W_UQ,h c_Q, and
+    y = W_O [o_1 | ... | o_H]; see the section at the end of this file.
   * Prefill onto a cached prefix (the pages ask for prefill to be measured
     under real serving shapes, [arch] 4; they do not spell out chunking): the
     new tokens of a sequence follow ``prefix`` tokens already in the cache;
@@ -451,3 +454,54 @@ def merge_partials(parts) -> Tuple[np.ndarray, float]:
     l_star = float(sum(w * p[1] for w, p in zip(wts, parts)))
     acc = sum(w * p[2] for w, p in zip(wts, parts))
     return acc / l_star, m_star + math.log(l_star)
+
+
+# --------------------------------------------------------------------------
+# query low-rank compression and the output projection ([blog] "MLA nasil
+# calisir?", last paragraph: the queries go through the same kind of
+# compression; [arch] 1: the decompression matrices are folded into the
+# query and the output matrices)
+#
+# Readings (the pages name the steps, not their shapes or a normalisation):
+#   * c_Q,n = W_DQ h_n, a d_cq-wide query latent, not normalised;
+#   * per head, [q_C | q_R] = W_UQ,h c_Q,n with W_UQ [H, d_n + d_R, d_cq];
+#     q_R is rotated at the token's position exactly as before;
+#   * y_n = W_O [o_n,1 | ... | o_n,H] with W_O [D, H d_v]: head h's output
+#     meets columns h d_v .. h d_v + d_v - 1 of W_O.
+# The folded ("absorbed") weights below are the same function in another
+# order; the plain order above is the definition.
+# --------------------------------------------------------------------------
+
+
+def compress_query(h: np.ndarray, w_dq: np.ndarray) -> np.ndarray:
+    """c_Q = W_DQ h: h [N, D], w_dq [d_cq, D] -> [N, d_cq]."""
+    return h @ w_dq.T
+
+
+def query_from_latent(c_q: np.ndarray, w_uq: np.ndarray) -> np.ndarray:
+    """Per-head pre-RoPE query [q_C | q_R] = W_UQ,h c_Q: c_q [N, d_cq],
+    w_uq [H, d_n + d_R, d_cq] -> [N, H, d_n + d_R]."""
+    return np.einsum("nc,hjc->nhj", c_q, w_uq)
+
+
+def output_projection(o: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """y = W_O [o_1 | ... | o_H]: o [N, H, d_v] (heads in order), w_o
+    [D, H d_v] -> [N, D]."""
+    return o.reshape(o.shape[0], -1) @ w_o.T
+
+
+def folded_query_weights(w_uq: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """W_UK folded into W_UQ: per head [W_UK,h^T W_UQ,h[:d_n] ; W_UQ,h[d_n:]],
+    [H, d_c + d_R, d_cq], so that the absorbed query (before RoPE of its last
+    d_R values) is this matrix times c_Q."""
+    d_n = w_uk.shape[1]
+    content = np.einsum("hjc,hjk->hck", w_uk, w_uq[:, :d_n])
+    return np.concatenate([content, w_uq[:, d_n:]], axis=1)
+
+
+def folded_output_weights(w_o: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """W_UV folded into W_O: per head W_O,h W_UV,h, [H, D, d_c], so that
+    y = sum_h W_OV,h lat_h for the softmax-weighted latent sums lat_h."""
+    H, d_v, _ = w_uv.shape
+    D = w_o.shape[0]
+    return np.einsum("dhv,hvc->hdc", w_o.reshape(D, H, d_v), w_uv)

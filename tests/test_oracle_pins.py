@@ -621,6 +621,86 @@ def test_fp8_pool_decode_equals_decode_of_its_values():
 
 
 # ---------------------------------------------------------------------------
+# query compression and output projection ([blog] "MLA nasil calisir?";
+# [arch] 1 and 6: folding the decompression matrices into the query and the
+# output matrices changes the order, not the function)
+# ---------------------------------------------------------------------------
+
+def _qo_case(seed, H=3, T=17, D=14, d_c=8, d_r=4, d_n=5, d_v=6, d_cq=7):
+    rng = np.random.default_rng(seed)
+    return dict(
+        rows=rng.standard_normal((T, d_c + d_r)), h=rng.standard_normal((1, D)),
+        w_dq=rng.standard_normal((d_cq, D)) * 0.4, w_uq=rng.standard_normal((H, d_n + d_r, d_cq)) * 0.4,
+        w_uk=rng.standard_normal((H, d_n, d_c)) * 0.4, w_uv=rng.standard_normal((H, d_v, d_c)) * 0.4,
+        w_o=rng.standard_normal((D, H * d_v)) * 0.4, d_c=d_c, d_r=d_r, d_n=d_n, sigma=0.3, base=10000.0, pos=T - 1)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_folded_query_weights_give_the_same_logits(seed):
+    c = _qo_case(seed)
+    c_q = O.compress_query(c["h"], c["w_dq"])
+    q = O.query_from_latent(c_q, c["w_uq"])[0]
+    plain = O.nonabsorbed_logits(q, c["rows"], c["w_uk"], c["pos"], c["d_c"], c["sigma"], c["base"])
+    w_qk = O.folded_query_weights(c["w_uq"], c["w_uk"])
+    qa = np.einsum("hjc,c->hj", w_qk, c_q[0])
+    qa[:, c["d_c"]:] = O.rope(qa[:, c["d_c"]:], c["pos"], c["base"])
+    folded = c["sigma"] * (qa @ c["rows"].T)
+    assert _rel(folded, plain) < 1e-12
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_folded_output_weights_give_the_same_output(seed):
+    c = _qo_case(seed)
+    q = O.query_from_latent(O.compress_query(c["h"], c["w_dq"]), c["w_uq"])[0]
+    o, _ = O.decode_one(q, c["rows"], c["w_uk"], c["w_uv"], c["pos"], c["d_c"], c["sigma"], c["base"])
+    y = O.output_projection(o[None], c["w_o"])[0]
+    # folded: the softmax-weighted latent sums of each head through W_O,h W_UV,h
+    s = O.nonabsorbed_logits(q, c["rows"], c["w_uk"], c["pos"], c["d_c"], c["sigma"], c["base"])
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    lat = (p / p.sum(axis=1, keepdims=True)) @ c["rows"][:, : c["d_c"]]
+    y_folded = np.einsum("hdc,hc->d", O.folded_output_weights(c["w_o"], c["w_uv"]), lat)
+    assert _rel(y_folded, y) < 1e-12
+
+
+def test_brute_force_query_and_output_projection():
+    c = _qo_case(3, H=2, T=4, D=5, d_c=3, d_r=2, d_n=2, d_v=2, d_cq=3)
+    h, w_dq, w_uq, w_o = c["h"][0].tolist(), c["w_dq"].tolist(), c["w_uq"].tolist(), c["w_o"].tolist()
+    cq = [sum(w_dq[i][j] * h[j] for j in range(len(h))) for i in range(len(w_dq))]
+    q_bf = [[sum(w_uq[hh][j][i] * cq[i] for i in range(len(cq))) for j in range(len(w_uq[0]))]
+            for hh in range(len(w_uq))]
+    q = O.query_from_latent(O.compress_query(c["h"], c["w_dq"]), c["w_uq"])[0]
+    assert _rel(q, q_bf) < 1e-12
+    rng = np.random.default_rng(4)
+    o = rng.standard_normal((2, 2, 2))  # [N, H, d_v]
+    y = O.output_projection(o, c["w_o"])
+    for n in range(2):
+        for d in range(len(w_o)):
+            ref = sum(w_o[d][hh * 2 + v] * o[n, hh, v] for hh in range(2) for v in range(2))
+            assert abs(y[n, d] - ref) < 1e-12
+
+
+def test_projected_decode_equals_sdpa_then_output_matmul():
+    """From h to y: the compressed query, MLA decode and the output projection
+    equal torch's SDPA over one shared key [c | k_R] and value c (float64),
+    followed by W_UV,h per head and W_O, written out with torch matmuls."""
+    c = _qo_case(5, H=4, T=29, D=16, d_c=8, d_r=4, d_n=6, d_v=5, d_cq=9)
+    q = O.query_from_latent(O.compress_query(c["h"], c["w_dq"]), c["w_uq"])[0]
+    o, _ = O.decode_one(q, c["rows"], c["w_uk"], c["w_uv"], c["pos"], c["d_c"], c["sigma"], c["base"])
+    y = O.output_projection(o[None], c["w_o"])[0]
+    d_n, d_c, H = c["d_n"], c["d_c"], q.shape[0]
+    cq_t = torch.nn.functional.linear(torch.tensor(c["h"]), torch.tensor(c["w_dq"]))[0]
+    q_t = torch.stack([torch.tensor(c["w_uq"][i]) @ cq_t for i in range(H)])
+    qa = torch.stack([torch.cat([torch.tensor(c["w_uk"][i]).T @ q_t[i, :d_n],
+                                 torch.tensor(O.rope(q_t[i, d_n:].numpy(), c["pos"], c["base"]))]) for i in range(H)])
+    K = torch.tensor(c["rows"])[None, None].expand(1, H, -1, -1)
+    V = torch.tensor(c["rows"][:, :d_c])[None, None].expand(1, H, -1, -1)
+    lat = torch.nn.functional.scaled_dot_product_attention(qa[None, :, None, :], K, V, scale=c["sigma"])[0, :, 0]
+    heads = [torch.tensor(c["w_uv"][i]) @ lat[i] for i in range(H)]
+    y_ref = torch.tensor(c["w_o"]) @ torch.cat(heads)
+    assert _rel(y, y_ref.numpy()) < 1e-12
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: a copy of the oracle with one plausible slip must fail a pin
 # ---------------------------------------------------------------------------
 
@@ -752,6 +832,17 @@ def _mut_prefill_no_mask(q, rows, w_uk, w_uv, d_c, sigma, base, queries=None, he
     return o, lse
 
 
+def _mut_output_value_major(o, w_o):
+    """output projection that flattens the head outputs value-major."""
+    return np.transpose(o, (0, 2, 1)).reshape(o.shape[0], -1) @ w_o.T
+
+
+def _mut_query_from_latent_transposed(c_q, w_uq):
+    """W_UQ [H, d_n + d_R, d_cq] read with the layout [H, d_cq, d_n + d_R]."""
+    H, J, C = w_uq.shape
+    return np.einsum("nc,hcj->nhj", c_q, np.ascontiguousarray(w_uq).reshape(H, C, J))
+
+
 def _mut_attend_log2(scores, values):
     m = float(np.max(scores))
     w = np.exp(scores - m)
@@ -791,7 +882,8 @@ def _mut_unpack_scales_first(pages, P, R):
 @pytest.mark.parametrize("mutation", ["rope_sign", "rope_pairing", "drop_kr", "sigma_content_only",
                                       "causal_off_by_one", "lse_log2", "prefix_position",
                                       "fp8_ties_away", "fp8_scale_exponent", "fp8_scales_first",
-                                      "wuk_transposed", "causal_mask_dropped"])
+                                      "wuk_transposed", "causal_mask_dropped", "output_value_major",
+                                      "wuq_transposed"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     import oracle.mla_oracle as M
 
@@ -823,6 +915,10 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
             patch(name, _mut_wuk_transposed(getattr(M, name), pos))
     elif mutation == "causal_mask_dropped":
         patch("prefill_one", _mut_prefill_no_mask)
+    elif mutation == "output_value_major":
+        patch("output_projection", _mut_output_value_major)
+    elif mutation == "wuq_transposed":
+        patch("query_from_latent", _mut_query_from_latent_transposed)
     pins = [test_rope_closed_forms, lambda: test_brute_force_decode(0), lambda: test_brute_force_prefill(0),
             test_absorbed_equals_sdpa_mqa, test_causal_prefill_equals_sdpa_causal,
             test_absorbed_and_nonabsorbed_logits_agree, test_single_token_context,
@@ -830,7 +926,10 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
             test_prefix_prefill_is_the_tail_of_a_full_prefill, test_prefix_prefill_of_one_token_is_decode,
             test_e4m3_quantize_matches_torch_cast, test_e4m3_quantize_inverts_decode,
             lambda: test_row_scale_exponent_bounds(0.37), test_quantize_row_error_bound_and_scale,
-            test_fp8_pages_layout_and_roundtrip, test_fp8_write_one_hot_rows_and_skip]
+            test_fp8_pages_layout_and_roundtrip, test_fp8_write_one_hot_rows_and_skip,
+            lambda: test_folded_query_weights_give_the_same_logits(0),
+            lambda: test_folded_output_weights_give_the_same_output(0),
+            test_brute_force_query_and_output_projection, test_projected_decode_equals_sdpa_then_output_matmul]
     caught = 0
     for p in pins:
         try:
