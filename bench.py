@@ -160,6 +160,61 @@ def decode_call_leg(cfg, copies, n, ceiling=None):
     return res
 
 
+def projection_leg(n=64, calls=30):
+    """Query compression (mla_project_q: W_DQ, W_UQ, then the absorption with
+    W_UK) and output projection (mla_project_out: W_O) at the V3 shapes for
+    one decode batch of n tokens.  Both stream their weights once per call;
+    weight copies rotate so that they are not served from the 256 MB Infinity
+    Cache."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_22_amd import harness, inputs as I, mla
+    cfg = I.V3
+    print("[bench] projection leg", file=sys.stderr, flush=True)
+    inp = I.make(cfg, 0, with_rows=False)
+    pj = I.projection_inputs(cfg, n, 3)
+    d = harness.dims_for(cfg)
+    dev = lambda x, dt="bf16": harness.to_device(x, dt)  # noqa: E731
+    wq = [(dev(pj["w_dq"]), dev(pj["w_uq"]), dev(inp["w_uk"])) for _ in range(3)]
+    wo = [dev(pj["w_o"]) for _ in range(2)]
+    h, pos, o = dev(pj["h"]), dev(pj["positions"], "i32"), dev(pj["o"])
+    q_abs = torch.empty((n, cfg.num_heads, cfg.row_width), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((n, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    wsq = torch.empty(mla.project_q_workspace_size(d, pj["d_cq"], n), dtype=torch.uint8, device="cuda")
+    wso_n = mla.project_out_workspace_size(d, n)
+    wso = torch.empty(max(wso_n, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for i in range(5):
+            fn(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+    tq = timed(lambda i: mla.project_q(d, h, *wq[i % 3][:2], wq[i % 3][2], pos, q_abs, wsq))
+    to = timed(lambda i: mla.project_out(d, o, wo[i % 2], y, wso if wso_n else None))
+    bq = 2 * (pj["w_dq"].size + pj["w_uq"].size + inp["w_uk"].size)
+    bo = 2 * pj["w_o"].size
+
+    def leg(t, b, what):
+        us = float(np.mean(t))
+        return {"what": what, "weight_bytes": int(b), "us": round(us, 2),
+                "us_p50_p95_p99": [round(float(np.percentile(t, p)), 2) for p in (50, 95, 99)],
+                "weight_gbs": round(b / (us * 1e-6) / 1e9, 1), "frac_of_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del wq, wo
+    torch.cuda.empty_cache()
+    return {"workload": f"V3 shapes, {n} tokens: D={cfg.hidden}, d_cq={pj['d_cq']}, H={cfg.num_heads}, "
+                        f"d_n+d_R={cfg.qk_head}, d_v={cfg.v_head}, bf16",
+            "project_q": leg(tq, bq, "c_Q = W_DQ h, q = W_UQ c_Q, absorbed with W_UK"),
+            "project_out": leg(to, bo, "y = W_O [o_1 | ... | o_H]")}
+
+
 def calibrate():
     """A plain device copy of known size (1 GiB read + 1 GiB written, 3
     times): the FETCH_SIZE and WRITE_SIZE counters of this run give the
@@ -490,6 +545,7 @@ def main():
         res["decode_workloads"] = [decode_call_leg(I.TINY, 1, 50, ceil["gbs"]),
                                    decode_call_leg(I.V2LITE, 8, 100, ceil["gbs"]),
                                    decode_call_leg(I.RAGGED, 1, 50, ceil["gbs"])]
+        res["projections"] = projection_leg()
     res["conditions"] = conditions()
     if not args.no_prefill:
         res["prefill"] = prefill_leg()

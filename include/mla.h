@@ -299,6 +299,49 @@ int mla_prefill_kv(const mla_dims_t* dims, const void* q, const void* pool, int3
                    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Query low-rank compression and the output projection (yapayzekasozluk.tr
+ * "MLA nasil calisir?", last paragraph: the queries get the same kind of
+ * compression as K and V; openarchlab section 1: the decompression matrices
+ * are folded into the query and the output matrices).
+ *
+ * mla_project_q: from the hidden states to the absorbed queries that
+ * mla_decode reads, for n_tokens tokens:
+ *   c_Q[n]       = W_DQ h[n]                                  (d_cq wide)
+ *   q[n][h]      = W_UQ,h c_Q[n] = [q_C | q_R]                (d_n + d_r)
+ *   q_abs[n][h]  = [W_UK,h^T q_C | RoPE(q_R, positions[n])]   (as mla_absorb_q)
+ * c_Q and q are rounded to dtype (bf16: nearest even) in the workspace before
+ * the next product.  The products run in this order (W_UK applied to q_C,
+ * not folded into W_UQ beforehand): the same function as the folded matrix
+ * W_UK,h^T W_UQ,h, with 192 d_cq + 64 K weights per head instead of
+ * 576 d_cq at the DeepSeek-V3 shapes.
+ *   h       [n_tokens, D]                 dtype
+ *   w_dq    [d_cq, D]                     dtype
+ *   w_uq    [H, d_n + d_r, d_cq]          dtype
+ *   w_uk    [H, d_n, d_c]                 dtype
+ *   q_abs   [n_tokens, H, d_c + d_r]      dtype  output
+ *   workspace >= mla_project_q_workspace_size(dims, d_cq, n_tokens) bytes
+ * d_cq >= 1.  n_tokens == 0 is a no-op.
+ *
+ * mla_project_out: the attention output through W_O, y[n] = W_O [o[n][0] |
+ * ... | o[n][H-1]], head h at columns h d_v .. h d_v + d_v - 1 of W_O.  With
+ * mla_decode's W_UV this is y = sum_h (W_O,h W_UV,h) lat_h, the folded output
+ * matrix applied in two steps (d_v (D + d_c) weights per head instead of
+ * D d_c).
+ *   o       [n_tokens, H, d_v]            dtype  (mla_decode's out)
+ *   w_o     [D, H d_v]                    dtype
+ *   y       [n_tokens, D]                 dtype  output
+ *   workspace >= mla_project_out_workspace_size(dims, n_tokens) bytes (may
+ *             be 0: then NULL is accepted)
+ */
+size_t mla_project_q_workspace_size(const mla_dims_t* dims, int32_t d_cq, int32_t n_tokens);
+int mla_project_q(const mla_dims_t* dims, int32_t d_cq, const void* h, const void* w_dq, const void* w_uq,
+                  const void* w_uk, const int32_t* positions, int32_t n_tokens, void* q_abs, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+size_t mla_project_out_workspace_size(const mla_dims_t* dims, int32_t n_tokens);
+int mla_project_out(const mla_dims_t* dims, const void* o, const void* w_o, int32_t n_tokens, void* y,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Ideal cache bytes of `tokens` tokens over `layers` layers:
  * layers x tokens x (d_c + d_r) x element bytes (openarchlab section 3;
  * LLMScale "Multi-head latent attention (MLA)": the head count drops out).

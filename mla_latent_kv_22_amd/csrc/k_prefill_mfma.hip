@@ -39,18 +39,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
-// Direct-to-LDS load from a 64-bit per-lane address (rows gathered through
-// the block table can lie anywhere in a pool larger than 4 GiB).
-__device__ __forceinline__ void dma16_v(const void* p, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(p), "s"(lds_addr)
-      : "memory", "m0");
-}
-
 __device__ __forceinline__ int seq_of(const int32_t* __restrict__ cu, int num_seqs, int n) {
   int lo = 0, hi = num_seqs - 1;
   while (lo < hi) {

@@ -220,6 +220,36 @@ int decode_layout_in(const mla_dims_t* d, int batch, int max_seq_len, size_t byt
 
 }  // namespace
 
+// ---------------------------------------------------------------- query compression, output projection
+namespace {
+
+struct ProjQLayout {
+  size_t cq, q, part;
+  size_t total() const { return cq + q + part; }
+};
+
+bool proj_mfma(const mla_dims_t* d, int N, int M, int K) {
+  return d->dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC) && gemm_mfma_supported(N, M, K);
+}
+
+size_t proj_part_bytes(const mla_dims_t* d, int N, int M, int K, int cus) {
+  return proj_mfma(d, N, M, K) ? gemm_workspace_bytes(N, M, K, cus) : 0;
+}
+
+int proj_q_layout(const mla_dims_t* d, int d_cq, int n, ProjQLayout& L) {
+  const int cus = current_cus();
+  if (cus <= 0) return MLA_ERR_HIP;
+  const size_t e = (size_t)elem_bytes(d->dtype);
+  const int qw = d->num_heads * (d->qk_nope + d->d_r);
+  L.cq = ((size_t)n * d_cq * e + 255) & ~(size_t)255;
+  L.q = ((size_t)n * qw * e + 255) & ~(size_t)255;
+  const size_t p1 = proj_part_bytes(d, n, d_cq, d->hidden, cus), p2 = proj_part_bytes(d, n, qw, d_cq, cus);
+  L.part = p1 > p2 ? p1 : p2;
+  return MLA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* mla_status_string(int status) {
@@ -415,6 +445,63 @@ int mla_prefill(const mla_dims_t* dims, const void* q, const void* pool, int32_t
   return mla_prefill_kv(dims, q, pool, num_pages, block_table, max_pages_per_seq, cu_seqlens, cu_seqlens, num_seqs,
                         total_tokens, total_tokens, max_seq_len, max_seq_len, w_uk, w_uv, out, lse, workspace,
                         workspace_bytes, stream);
+}
+
+
+size_t mla_project_q_workspace_size(const mla_dims_t* dims, int32_t d_cq, int32_t n_tokens) {
+  if (check_dims(dims) != MLA_OK || fp8_cache(dims) || d_cq < 1 || n_tokens < 0) return 0;
+  ProjQLayout L;
+  if (proj_q_layout(dims, d_cq, n_tokens, L) != MLA_OK) return 0;
+  return L.total();
+}
+
+int mla_project_q(const mla_dims_t* dims, int32_t d_cq, const void* h, const void* w_dq, const void* w_uq,
+                  const void* w_uk, const int32_t* positions, int32_t n_tokens, void* q_abs, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (d_cq < 1 || n_tokens < 0) return MLA_ERR_ARG;
+  if (n_tokens == 0) return MLA_OK;
+  if (!h || !w_dq || !w_uq || !w_uk || !positions || !q_abs || !workspace) return MLA_ERR_NULL;
+  ProjQLayout L;
+  if ((st = proj_q_layout(dims, d_cq, n_tokens, L)) != MLA_OK) return st;
+  if (workspace_bytes < L.total()) return MLA_ERR_WORKSPACE;
+  const int cus = current_cus();
+  const bool bf = dims->dtype == MLA_BF16;
+  const int D = dims->hidden, qw = dims->num_heads * (dims->qk_nope + dims->d_r);
+  char* ws = (char*)workspace;
+  void* cq = ws;
+  void* q = ws + L.cq;
+  float* part = (float*)(ws + L.cq + L.q);
+  hipError_t e = gemm_bt(h, w_dq, cq, n_tokens, d_cq, D, bf, proj_mfma(dims, n_tokens, d_cq, D), part, cus, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  e = gemm_bt(cq, w_uq, q, n_tokens, qw, d_cq, bf, proj_mfma(dims, n_tokens, qw, d_cq), part, cus, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  return mla_absorb_q(dims, q, w_uk, positions, n_tokens, q_abs, stream);
+}
+
+size_t mla_project_out_workspace_size(const mla_dims_t* dims, int32_t n_tokens) {
+  if (check_dims(dims) != MLA_OK || n_tokens < 0) return 0;
+  const int cus = current_cus();
+  if (cus <= 0) return 0;
+  return proj_part_bytes(dims, n_tokens, dims->hidden, dims->num_heads * dims->v_head, cus);
+}
+
+int mla_project_out(const mla_dims_t* dims, const void* o, const void* w_o, int32_t n_tokens, void* y,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0) return MLA_ERR_ARG;
+  if (n_tokens == 0) return MLA_OK;
+  if (!o || !w_o || !y) return MLA_ERR_NULL;
+  const int cus = current_cus();
+  if (cus <= 0) return MLA_ERR_HIP;
+  const int D = dims->hidden, K = dims->num_heads * dims->v_head;
+  const size_t need = proj_part_bytes(dims, n_tokens, D, K, cus);
+  if (need > 0 && !workspace) return MLA_ERR_NULL;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  return launched(gemm_bt(o, w_o, y, n_tokens, D, K, dims->dtype == MLA_BF16, proj_mfma(dims, n_tokens, D, K),
+                          (float*)workspace, cus, stream));
 }
 
 int mla_get_device_error(int32_t* error_bits, hipStream_t stream) {

@@ -82,6 +82,18 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
       : "memory", "m0");
 }
 
+// Direct-to-LDS load from a 64-bit per-lane address (rows gathered through
+// a block table can lie anywhere in a pool larger than 4 GiB).
+__device__ __forceinline__ void dma16_v(const void* p, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(p), "s"(lds_addr)
+      : "memory", "m0");
+}
+
 // ---------------------------------------------------------------- RoPE
 // Rotation of pair i of a d-wide vector at position pos: angle pos * theta_i,
 // theta_i = base^(-2i/d).

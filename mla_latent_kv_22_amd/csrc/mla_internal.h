@@ -101,6 +101,15 @@ hipError_t absorb_mfma(const AbsorbArgs& a, hipStream_t s);
 bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch);
 int decode_mfma_slots(int H, int cus, bool fp8);
 hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s);
+// Y[N, M] = X[N, K] W[M, K]^T (query compression, output projection): MFMA
+// for bf16 with M % 64 == 0 and K % 64 == 0 (K split over work-groups when
+// the tiles do not fill the GPU; part: gemm_workspace_bytes of fp32 partials),
+// else plain kernels (fp32 or bf16 storage, fp32 arithmetic).
+bool gemm_mfma_supported(int N, int M, int K);
+int gemm_splits(int N, int M, int K, int cus);
+size_t gemm_workspace_bytes(int N, int M, int K, int cus);
+hipError_t gemm_bt(const void* X, const void* W, void* Y, int N, int M, int K, bool bf16, bool mfma, float* part,
+                   int cus, hipStream_t s);
 // MFMA prefill: d_n = d_v = 128, d_R = 64, bf16; workspace K_C and V as bf16 [H][total][128]
 bool prefill_mfma_supported(int d_n, int d_v, int d_r, int d_c, int P);
 hipError_t prefill_mfma(const PrefillArgs& a, hipStream_t s);

@@ -28,7 +28,8 @@ OP_WRITE_CACHE, OP_ABSORB_Q, OP_DECODE, OP_PREFILL = 0, 1, 2, 3
 _SYMBOLS = ("mla_write_cache", "mla_write_cache_ws", "mla_write_cache_workspace_size", "mla_absorb_q",
             "mla_decode_workspace_size", "mla_decode", "mla_prefill_workspace_size", "mla_prefill",
             "mla_prefill_kv", "mla_cache_bytes", "mla_page_bytes", "mla_status_string", "mla_uses_fast_path",
-            "mla_get_device_error", "mla_debug_build", "mla_decode_noalloc")
+            "mla_get_device_error", "mla_debug_build", "mla_decode_noalloc", "mla_project_q_workspace_size",
+            "mla_project_q", "mla_project_out_workspace_size", "mla_project_out")
 DEVERR_PAGE, DEVERR_SLOT, DEVERR_LENGTH = 1, 2, 4
 
 
@@ -92,10 +93,17 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_uses_fast_path.argtypes = [dp, i32]
         L.mla_get_device_error.argtypes = [ctypes.POINTER(ctypes.c_int32), vp]
+        L.mla_project_q_workspace_size.argtypes = [dp, i32, i32]
+        L.mla_project_q_workspace_size.restype = sz
+        L.mla_project_q.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+        L.mla_project_out_workspace_size.argtypes = [dp, i32]
+        L.mla_project_out_workspace_size.restype = sz
+        L.mla_project_out.argtypes = [dp, vp, vp, i32, vp, vp, sz, vp]
         L.mla_debug_build.argtypes = []
         for f in ("mla_write_cache", "mla_write_cache_ws", "mla_absorb_q", "mla_decode", "mla_decode_noalloc",
                   "mla_prefill",
-                  "mla_prefill_kv", "mla_uses_fast_path", "mla_get_device_error", "mla_debug_build"):
+                  "mla_prefill_kv", "mla_uses_fast_path", "mla_get_device_error", "mla_debug_build",
+                  "mla_project_q", "mla_project_out"):
             getattr(L, f).restype = ctypes.c_int
         _libs[path] = L
     return _libs[path]
@@ -256,3 +264,29 @@ def get_device_error(stream=None) -> int:
 
 def debug_build() -> bool:
     return bool(lib().mla_debug_build())
+
+
+def project_q_workspace_size(d: Dims, d_cq: int, n_tokens: int) -> int:
+    return int(lib().mla_project_q_workspace_size(ctypes.byref(d), int(d_cq), int(n_tokens)))
+
+
+def project_q(d: Dims, h, w_dq, w_uq, w_uk, positions, q_abs, workspace, stream=None) -> None:
+    """mla_project_q: c_Q = W_DQ h, q = W_UQ c_Q, then the absorbed queries."""
+    dt = _torch_dtype(d)
+    _check(lib().mla_project_q(ctypes.byref(d), int(w_dq.shape[0]), _ptr(h, "h", dt), _ptr(w_dq, "w_dq", dt),
+                               _ptr(w_uq, "w_uq", dt), _ptr(w_uk, "w_uk", dt),
+                               _ptr(positions, "positions", torch.int32), int(h.shape[0]), _ptr(q_abs, "q_abs", dt),
+                               _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)),
+           "mla_project_q")
+
+
+def project_out_workspace_size(d: Dims, n_tokens: int) -> int:
+    return int(lib().mla_project_out_workspace_size(ctypes.byref(d), int(n_tokens)))
+
+
+def project_out(d: Dims, o, w_o, y, workspace=None, stream=None) -> None:
+    """mla_project_out: y = W_O [o_1 | ... | o_H]."""
+    dt = _torch_dtype(d)
+    _check(lib().mla_project_out(ctypes.byref(d), _ptr(o, "o", dt), _ptr(w_o, "w_o", dt), int(o.shape[0]),
+                                 _ptr(y, "y", dt), _ptr(workspace, "workspace", torch.uint8),
+                                 0 if workspace is None else workspace.numel(), _stream(stream)), "mla_project_out")
