@@ -496,8 +496,7 @@ def main():
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in evs])
 
-    t_write = timed(lambda i: mla.write_cache(st.d, st.h, st.w_dkr, st.positions, st.slots, pools[i % 2]),
-                    args.steps)
+    t_write = timed(lambda i: st.write(pool=pools[i % 2]), args.steps)
     t_absorb = timed(lambda i: st.absorb(), args.steps)
     t_decode = timed(lambda i: st.attend(pool=pools[i % 2]), args.steps)
     dec_ms = float(np.mean(t_decode))

@@ -58,9 +58,13 @@ class DecodeStep:
         self.lse = torch.empty((B, H), dtype=torch.float32, device=device)
         ws = mla.decode_workspace_size(self.d, B, self.max_seq_len)
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        # the cache write's workspace: 8-bit row staging and the split-K partials
+        wws = mla.write_cache_workspace_size(self.d, int(inp["h"].shape[0]))
+        self.write_ws = torch.empty(max(wws, 1), dtype=torch.uint8, device=device)
 
-    def write(self, stream=None):
-        mla.write_cache(self.d, self.h, self.w_dkr, self.positions, self.slots, self.pool, stream)
+    def write(self, stream=None, pool=None):
+        mla.write_cache(self.d, self.h, self.w_dkr, self.positions, self.slots, self.pool if pool is None else pool,
+                        stream, workspace=self.write_ws)
 
     def absorb(self, stream=None):
         mla.absorb_q(self.d, self.q, self.w_uk, self.q_positions, self.q_abs, stream)
@@ -77,11 +81,11 @@ class DecodeStep:
         main = stream if stream is not None else torch.cuda.current_stream()
         if side_stream is not None:
             side_stream.wait_stream(main)
-            mla.write_cache(self.d, self.h, self.w_dkr, self.positions, self.slots, pool, side_stream)
+            self.write(side_stream, pool)
             self.absorb(main)
             main.wait_stream(side_stream)
         else:
-            mla.write_cache(self.d, self.h, self.w_dkr, self.positions, self.slots, pool, main)
+            self.write(main, pool)
             self.absorb(main)
         self.attend(main, pool)
 

@@ -22,10 +22,11 @@ def _case(label):
 @pytest.mark.parametrize("cfg,flags", [
     (I.TINY, 0),
     (I.scaled(I.V3, hidden=512, batch=3, seq_len=150, paged=True), 0),
+    (I.scaled(I.V3, seq_len=128, paged=True), 0),  # the decode step's write: 64 tokens, D = 7168
     (I.scaled(I.V3, hidden=512, batch=3, seq_len=150, paged=True), mla.FLAG_GENERIC),
     (I.scaled(I.PREFILL, hidden=512, batch=3, seq_len=700), 0),   # > 1024 tokens: wide token blocks
     (I.scaled(I.PREFILL, hidden=512, batch=3, seq_len=1667), 0),  # >= 4096 tokens: whole-hidden-axis tiles
-], ids=["tiny_f32", "v3dims_bf16_mfma", "v3dims_bf16_generic", "prefill_rows_mfma", "prefill_rows_5001_tokens"])
+], ids=["tiny_f32", "v3dims_bf16_mfma", "v3_64_tokens_mfma", "v3dims_bf16_generic", "prefill_rows_mfma", "prefill_rows_5001_tokens"])
 def test_write_cache_parity_and_untouched_slots(cfg, flags):
     need_gpu()
     _case(f"write_cache {cfg.name} flags={flags}")
