@@ -236,7 +236,10 @@ int mla_decode_noalloc(const mla_dims_t* dims, const void* q_abs, const void* po
                        hipStream_t stream);
 
 /* Bytes of workspace mla_prefill needs for `total_tokens` query tokens, and
- * mla_prefill_kv for `total_tokens` key tokens (pass its total_kv). */
+ * mla_prefill_kv for `total_tokens` key tokens (pass its total_kv): the
+ * up-projected K_C and V of every key token, H * (d_n + d_v) values per token
+ * (plus at most 255 bytes of alignment), stored as bf16 on the MFMA path
+ * (mla_uses_fast_path(dims, 3) == 1) and as fp32 otherwise. */
 size_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t total_tokens);
 
 /*

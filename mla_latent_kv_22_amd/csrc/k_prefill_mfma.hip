@@ -316,18 +316,25 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn_mfma(PrefillArgs a, int
   int ld_pg = 3 / tpp, ld_in = 3 % tpp;
   int next_page = bt_c[min(ld_pg, pg_last)];
   auto sync = [&](int kt) {
-    // tile kt has landed once at most the later tiles' loads are in flight
-    if (kt + 2 < n_kt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
-    else if (kt + 1 < n_kt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __builtin_amdgcn_s_barrier();  // tile kt in LDS; tile kt-1's stage no longer read
-    asm volatile("" ::: "memory");
-    if (kt + 3 < n_kt) issue(kt + 3, next_page, ld_in);
+    // tile kt+3's page (read one sync earlier), then the next entry's scalar
+    // load, in flight over the wait and the barrier below
+    const int page3 = next_page, in3 = ld_in;
     if (++ld_in == tpp) {
       ld_in = 0;
       ++ld_pg;
     }
     next_page = bt_c[min(ld_pg, pg_last)];
+    // tile kt has landed once at most the later tiles' loads are in flight
+    if (kt + 2 < n_kt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
+    else if (kt + 1 < n_kt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();  // tile kt in LDS; tile kt-1's stage no longer read
+    // the scalar load is done by now; waiting for it here lets the tile's
+    // first score MFMA wait for its own K fragment only (a scalar load in
+    // flight forces every LDS wait to count down to zero)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    if (kt + 3 < n_kt) issue(kt + 3, page3, in3);
   };
 
   // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASKED is

@@ -111,10 +111,18 @@ bool decode_layout(const mla_dims_t* d, int batch, int max_seq_len, DecodeLayout
   return true;
 }
 
+// Prefill workspace: up-projected K_C then V for every key token, in the
+// element the path stores (bf16 on the MFMA path, fp32 on the plain one); the
+// K_C part is rounded up to 256 bytes.
+size_t prefill_elem_bytes(const mla_dims_t* d) { return prefill_fast(d) ? 2 : sizeof(float); }
+
+size_t prefill_k_bytes(const mla_dims_t* d, int total) {
+  const size_t k = (size_t)total * d->num_heads * d->qk_nope * prefill_elem_bytes(d);
+  return (k + 255) & ~(size_t)255;
+}
+
 size_t prefill_ws_bytes(const mla_dims_t* d, int total) {
-  size_t k = (size_t)total * d->num_heads * d->qk_nope * sizeof(float);
-  k = (k + 255) & ~(size_t)255;
-  return k + (size_t)total * d->num_heads * d->v_head * sizeof(float);
+  return prefill_k_bytes(d, total) + (size_t)total * d->num_heads * d->v_head * prefill_elem_bytes(d);
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
@@ -402,8 +410,7 @@ int mla_prefill_kv(const mla_dims_t* dims, const void* q, const void* pool, int3
   if (workspace_bytes < prefill_ws_bytes(dims, total_kv)) return MLA_ERR_WORKSPACE;
   int* err = device_error_word();
   if (!err) return MLA_ERR_HIP;
-  size_t kb = (size_t)total_kv * dims->num_heads * dims->qk_nope * sizeof(float);
-  kb = (kb + 255) & ~(size_t)255;
+  const size_t kb = prefill_k_bytes(dims, total_kv);
   PrefillArgs a;
   memset(&a, 0, sizeof a);
   a.q = q;

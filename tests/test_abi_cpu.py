@@ -157,6 +157,21 @@ def test_null_and_count_errors():
                          1 << 30, None) == -2
 
 
+def test_prefill_workspace_size_formula():
+    """K_C and V of every key token, H (d_n + d_v) values each: bf16 on the
+    MFMA path, fp32 on the plain kernels; the K_C part rounded up to 256 bytes."""
+    H, dn, dv = 128, 128, 128
+    bf = _dims()
+    assert mla.uses_fast_path(bf, mla.OP_PREFILL) == 1
+    assert mla.prefill_workspace_size(bf, 512) == 512 * H * (dn + dv) * 2
+    assert mla.prefill_workspace_size(bf, 1) == ((H * dn * 2 + 255) // 256) * 256 + H * dv * 2
+    gen = _dims(flags=mla.FLAG_GENERIC)
+    assert mla.uses_fast_path(gen, mla.OP_PREFILL) == 0
+    assert mla.prefill_workspace_size(gen, 512) == 512 * H * (dn + dv) * 4
+    assert mla.prefill_workspace_size(_dims(dtype="f32"), 3) == ((3 * H * dn * 4 + 255) // 256) * 256 + 3 * H * dv * 4
+    assert mla.prefill_workspace_size(bf, 0) == 0
+
+
 def test_binding_rejects_host_tensors():
     import torch
     d = _dims(hidden=8, num_heads=1, d_c=4, d_r=2, qk_nope=2, v_head=2, dtype="f32")
