@@ -172,6 +172,27 @@ def test_prefill_workspace_size_formula():
     assert mla.prefill_workspace_size(bf, 0) == 0
 
 
+def test_project_calls_check_arguments_before_the_device():
+    """mla_project_q / mla_project_out: empty calls are no-ops, bad sizes and
+    NULL pointers are rejected before any device work (no GPU here)."""
+    L = mla.lib()
+    d = _dims()
+    bad = _dims(d_c=3)
+    pq = lambda dims, d_cq, h, n, ws: L.mla_project_q(  # noqa: E731
+        ctypes.byref(dims), d_cq, h, FAKE, FAKE, FAKE, FAKE, n, FAKE, ws, 1 << 30, None)
+    assert pq(d, 1536, FAKE, 0, FAKE) == 0         # no tokens: nothing to do
+    assert pq(d, 0, FAKE, 4, FAKE) == -7           # d_cq < 1
+    assert pq(d, 1536, FAKE, -1, FAKE) == -7       # negative token count
+    assert pq(d, 1536, None, 4, FAKE) == -1        # h
+    assert pq(d, 1536, FAKE, 4, None) == -1        # workspace
+    assert pq(bad, 1536, FAKE, 4, FAKE) == -2      # invalid dims first
+    po = lambda dims, o, n: L.mla_project_out(ctypes.byref(dims), o, FAKE, n, FAKE, FAKE, 1 << 30, None)  # noqa: E731
+    assert po(d, FAKE, 0) == 0
+    assert po(d, FAKE, -3) == -7
+    assert po(d, None, 4) == -1
+    assert po(bad, FAKE, 4) == -2
+
+
 def test_binding_rejects_host_tensors():
     import torch
     d = _dims(hidden=8, num_heads=1, d_c=4, d_r=2, qk_nope=2, v_head=2, dtype="f32")

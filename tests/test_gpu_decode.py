@@ -181,6 +181,32 @@ def test_decode_ragged_edges(lens, heads):
         assert np.all(np.isneginf(st.lse.cpu().numpy()[b]))
 
 
+@pytest.mark.parametrize("heads", [16, 128])
+def test_decode_max_batch(heads):
+    """The largest batch the decode accepts (4096 sequences, the planner's LDS
+    arrays full), lengths U{0..96} with empty sequences among them: a seeded
+    sample of sequences against the oracle over every head, every empty one
+    exactly zero with lse = -inf."""
+    need_gpu()
+    _case(f"decode max batch H={heads}")
+    B = 4096
+    lens = np.random.default_rng(21).integers(0, 96, size=B, endpoint=True).astype(np.int32)
+    lens[[0, 1, B - 1]] = [0, 96, 0]
+    cfg = I.scaled(I.RAGGED, hidden=512, num_heads=heads, batch=B, seq_len=96, min_seq_len=1)
+    inp = I.make(cfg, 12, lengths=lens)
+    st = _run_step(cfg, inp)
+    assert mla.uses_fast_path(st.d, mla.OP_DECODE) == 1
+    nz = np.flatnonzero(lens > 0)
+    sample = sorted({1, int(nz[-1])} | {int(b) for b in np.random.default_rng(22).choice(nz, 46, replace=False)})
+    _check(cfg, inp, st, sample)
+    z = np.flatnonzero(lens == 0)
+    assert len(z) > 2
+    out = harness.to_host_bits(st.out)
+    lse = st.lse.cpu().numpy()
+    assert np.all(out[z].astype(np.uint16) == 0)
+    assert np.all(np.isneginf(lse[z]))
+
+
 @pytest.mark.parametrize("flags", [0, mla.FLAG_GENERIC], ids=["mfma", "generic"])
 def test_page_permutation_bit_invariance_and_determinism(flags):
     need_gpu()
