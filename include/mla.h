@@ -169,6 +169,21 @@ size_t mla_page_bytes(const mla_dims_t* dims);
 int mla_absorb_q(const mla_dims_t* dims, const void* q, const void* w_uk,
                  const int32_t* positions, int32_t n_tokens, void* q_abs, hipStream_t stream);
 
+/*
+ * The decode step's cache write and query absorption in one call: the
+ * result is that of mla_write_cache(dims, h, w_dkr, positions, slot_mapping,
+ * n_write, pool, num_pages) followed by mla_absorb_q(dims, q, w_uk,
+ * q_positions, n_q, q_abs), bit for bit, with the same arguments, layouts and
+ * errors (the two are independent: the absorption does not read the pool).
+ * With bf16 operands on the MFMA paths, n_write and n_q in [1, 64], d_n = 128
+ * and d_c = 512, both run in one launch, so the absorption uses the CUs the
+ * cache write leaves idle; otherwise the two calls run in sequence.  An 8-bit
+ * cache returns MLA_ERR_WORKSPACE (its write needs mla_write_cache_ws).
+ */
+int mla_write_absorb(const mla_dims_t* dims, const void* h, const void* w_dkr, const int32_t* positions,
+                     const int64_t* slot_mapping, int32_t n_write, void* pool, int32_t num_pages, const void* q,
+                     const void* w_uk, const int32_t* q_positions, int32_t n_q, void* q_abs, hipStream_t stream);
+
 /* Bytes of workspace mla_decode needs for `batch` sequences of at most
  * max_seq_len tokens (0 on invalid arguments or when no device is present). */
 size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t max_seq_len);

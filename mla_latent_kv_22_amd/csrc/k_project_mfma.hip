@@ -36,15 +36,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // piece p of row r at slot p ^ (r % 8) (conflict-free fragment reads).
 // KB chunks are loaded into registers at a time (all of a wave's chunks in
 // one round trip when KB covers them) and pass through NSL LDS slices.
+template <int TB4, int NWV, int NSL>
+struct WriteLds {
+  uint16_t stage[NWV][NSL][(16 + 16 * TB4) * 64];  // W rows, then h rows
+  f32x4 part[NWV][TB4][64];
+};
+
+// One work-group's tile (features 16 bx .. +15, tokens 16 TB4 by ..) of the cache write.
 template <int TB4, int NWV, int KB, int NSL>
-__global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
+__device__ __forceinline__ void write_tile(const WriteCacheArgs& a, int bx, int by, WriteLds<TB4, NWV, NSL>& lds) {
   constexpr int ROWS = 16 + 16 * TB4;  // W rows, then h rows
-  __shared__ __attribute__((aligned(16))) uint16_t stage[NWV][NSL][ROWS * 64];
-  __shared__ f32x4 part[NWV][TB4][64];
+  auto& stage = lds.stage;
+  auto& part = lds.part;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int R = a.d_c + a.d_r;
-  const int r0 = blockIdx.x * 16;
-  const int n0 = blockIdx.y * 16 * TB4;
+  const int r0 = bx * 16;
+  const int n0 = by * 16 * TB4;
   const uint16_t* __restrict__ W = (const uint16_t*)a.w_dkr;
   const uint16_t* __restrict__ H = (const uint16_t*)a.h;
   const int D = a.D, nchunk = D / 64;
@@ -159,6 +166,12 @@ __global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
     uint16_t* dst = (uint16_t*)a.pool + (size_t)slot[t] * R + rf;
     *(uint2*)dst = make_uint2(lo, hi);
   }
+}
+
+template <int TB4, int NWV, int KB, int NSL>
+__global__ void __launch_bounds__(64 * NWV) k_write_mfma(WriteCacheArgs a) {
+  __shared__ __attribute__((aligned(16))) WriteLds<TB4, NWV, NSL> lds;
+  write_tile<TB4, NWV, KB, NSL>(a, blockIdx.x, blockIdx.y, lds);
 }
 
 // Cache write for many tokens (a prefill chunk): one work-group per (128
@@ -410,7 +423,159 @@ __global__ void __launch_bounds__(256) k_absorb_mfma(AbsorbArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- write + absorption, one launch
+// The decode step's cache write (k_write_mfma<1, 16, 4, 2> tiles, 144
+// work-groups at 64 tokens) leaves most CUs idle for its whole duration, and
+// the absorption does not depend on it.  k_write_absorb runs both in one
+// grid of 1024-thread work-groups: the first ones are cache-write tiles, the
+// rest each take whole heads of the absorption (d_n = 128, d_c = 512, at
+// most 64 tokens).  For a head, sub-group s (threads 256 s .. +255, four
+// waves) computes latent columns 128 s .. +127 exactly as one k_absorb_mfma
+// work-group does (same operands, same k order, so the results are
+// bit-identical); the q_C block is staged once for the four, and each
+// sub-group's W_UK column block is overwritten by its output tile once every
+// wave has finished reading it.
+constexpr int WA_WBLK = 32768;                 // one W_UK column block: 128 rows x 256 bytes
+constexpr int WA_LDS = 4 * WA_WBLK + AB_T * 256;  // + the q_C block: 147456 bytes
+// cache-write tiles of 16 features x 16 WA_TB4 tokens, WA_NSL LDS slices per wave
+constexpr int WA_TB4 = 1, WA_NSL = 2;
+static_assert(sizeof(WriteLds<WA_TB4, 16, WA_NSL>) <= (size_t)WA_LDS, "write tile fits the fused kernel's LDS");
+
+__device__ __forceinline__ void absorb_head16(const AbsorbArgs& a, int h, char* smem) {
+  constexpr int DN = 128, NP = AB_DR / 2;
+  const int tid = threadIdx.x, ts = tid & 255, lane = tid & 63;
+  const int wv16 = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave within the work-group (uniform)
+  const int sg = wv16 >> 2, ws = wv16 & 3;                     // sub-group, wave within it
+  const int H = a.H, dc = a.d_c, dq = a.d_n + a.d_r, R = a.d_c + a.d_r;
+  const int cb = sg;
+  char* wtile = smem + cb * WA_WBLK;  // W_UK column block, later the output tile
+  char* qtile = smem + 4 * WA_WBLK;   // 64 x 256 B, piece p at slot p ^ (row % 8)
+  const uint16_t* __restrict__ wuk = (const uint16_t*)a.w_uk + (size_t)h * DN * dc + cb * AB_C;
+  const uint16_t* __restrict__ Q = (const uint16_t*)a.q;
+  uint16_t* __restrict__ out = (uint16_t*)a.q_abs;
+  // loads, in this order: the rotary inputs (sub-group 0), then the W_UK
+  // block and the q_C block straight into LDS (vmcnt retires in issue order,
+  // so the rotation waits only for its own loads).  Direct-to-LDS load i of a
+  // sub-group fills rows 4 i .. 4 i + 3 of its W block (lane l: row
+  // 4 i + l / 16, slot l % 16, whose source chunk is slot ^ 2 (row % 4)); load
+  // w16 of the work-group fills q_C rows 4 w16 .. +3 (slot l % 16, source
+  // piece slot ^ (row % 8); rows past the last token repeat it: their outputs
+  // are not stored).
+  constexpr int RK = AB_T * NP / 1024;  // rotary units per thread (2): every thread takes part
+  uint32_t pr[RK];
+  int ps[RK];
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
+    const int u = 1024 * k + tid;
+    const int nn = min(u / NP, a.n_tokens - 1), i = u % NP;
+    pr[k] = *(const uint32_t*)(Q + ((size_t)nn * H + h) * dq + DN + 2 * i);
+    ps[k] = a.positions[nn];
+  }
+  const uint32_t lds_w = lds_addr_of(wtile), lds_q = lds_addr_of(qtile);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = 4 * k + ws;  // this wave's load k of the sub-group's 32
+    const int j = 4 * i + (lane >> 4), slot = lane & 15;
+    dma16_v(wuk + (size_t)j * dc + 8 * (slot ^ (2 * (j & 3))), lds_w + 1024 * i);
+  }
+  {
+    const int t = 4 * wv16 + (lane >> 4), slot = lane & 15;
+    dma16_v(Q + ((size_t)min(t, a.n_tokens - 1) * H + h) * dq + 8 * (slot ^ (t & 7)), lds_q + 1024 * wv16);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));  // the rotary inputs (the 9 loads into LDS may remain)
+  {
+    static_assert(1024 % NP == 0, "pair index fixed per thread");
+    const double th = rope_inv_freq(tid % NP, AB_DR, a.rope_base);
+#pragma unroll
+    for (int k = 0; k < RK; ++k) {
+      const int u = 1024 * k + tid;
+      const int nn = u / NP, i = u % NP;
+      if (nn >= a.n_tokens) continue;
+      float c, sn;
+      rope_cs_theta(ps[k], th, c, sn);
+      const float x0 = __uint_as_float(pr[k] << 16), x1 = __uint_as_float(pr[k] & 0xffff0000u);
+      const uint32_t o = (uint32_t)f32_to_bf16(x0 * c - x1 * sn) | ((uint32_t)f32_to_bf16(x0 * sn + x1 * c) << 16);
+      *(uint32_t*)(out + ((size_t)nn * H + h) * R + dc + 2 * i) = o;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();  // W_UK blocks and the q_C block are in LDS
+  asm volatile("" ::: "memory");
+
+  const int g = lane >> 5, r = lane & 31;
+  const int grp = lane >> 4, jl = lane & 15;
+  const int tcol = 32 * ws + 16 * (grp & 1) + 4 * (jl & 3);
+  f32x16 acc[AB_T / 32];
+#pragma unroll
+  for (int tb = 0; tb < AB_T / 32; ++tb) {
+    const int trow = 32 * tb + r;
+    acc[tb] = f32x16{};
+#pragma unroll 2
+    for (int ks = 0; ks < DN / 16; ++ks) {
+      const int pc = 2 * ks + g;
+      const u32x4 av = *(const u32x4*)(qtile + trow * 256 + 16 * (pc ^ (trow & 7)));
+      const int k0 = 16 * ks + 8 * g;
+      const int j1 = k0 + (jl >> 2), j2 = j1 + 4;
+      const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(wtile + j1 * 256 + 16 * ((tcol >> 3) ^ (2 * (j1 & 3))) + 2 * (tcol & 7)));
+      const s16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(wtile + j2 * 256 + 16 * ((tcol >> 3) ^ (2 * (j2 & 3))) + 2 * (tcol & 7)));
+      const s16x8 bv = s16x8{b1[0], b1[1], b1[2], b1[3], b2[0], b2[1], b2[2], b2[3]};
+      acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), __builtin_bit_cast(bf16x8, bv), acc[tb], 0, 0,
+                                                        0);
+    }
+  }
+  __syncthreads();  // every wave has read its W_UK block: it becomes the output tile
+  char* otile = wtile;  // 64 x 256 B, piece p at slot p ^ (row % 8)
+  const int col = 32 * ws + r;
+#pragma unroll
+  for (int tb = 0; tb < AB_T / 32; ++tb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int t = 32 * tb + 8 * (j >> 2) + 4 * g + (j & 3);
+      *(uint16_t*)(otile + t * 256 + 16 * ((col >> 3) ^ (t & 7)) + 2 * (col & 7)) = f32_to_bf16(acc[tb][j]);
+    }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < AB_T * 16 / 256; ++k) {
+    const int u = k * 256 + ts, t = u >> 4, pc = u & 15;
+    if (t < a.n_tokens)
+      *(u32x4*)(out + ((size_t)t * H + h) * R + cb * AB_C + 8 * pc) = *(const u32x4*)(otile + t * 256 + 16 * (pc ^ (t & 7)));
+  }
+}
+
+// Work-group x < n_wblocks: cache-write tile (x % (R / 16), x / (R / 16));
+// otherwise heads x - n_wblocks, x - n_wblocks + n_ablocks, ... of the absorption.
+__global__ void __launch_bounds__(1024, 1) k_write_absorb(WriteCacheArgs wa, AbsorbArgs aa, int n_wblocks, int n_ablocks) {
+  __shared__ __attribute__((aligned(16))) char smem[WA_LDS];
+  const int x = blockIdx.x;
+  if (x < n_wblocks) {
+    const int fb = (wa.d_c + wa.d_r) / 16;
+    write_tile<WA_TB4, 16, 4, WA_NSL>(wa, x % fb, x / fb, *(WriteLds<WA_TB4, 16, WA_NSL>*)smem);
+    return;
+  }
+  for (int h = x - n_wblocks; h < aa.H; h += n_ablocks) {
+    absorb_head16(aa, h, smem);
+    __syncthreads();  // the next head reuses the LDS
+  }
+}
+
 }  // namespace
+
+bool write_absorb_fused_supported(int n_write, int n_q, int D, int d_c, int d_r, int H, int d_n) {
+  return n_write >= 1 && n_write <= 64 && n_q >= 1 && n_q <= AB_T && write_mfma_supported(D, d_c, d_r) &&
+         absorb_mfma_supported(H, d_n, d_c, d_r) && d_n == 128 && d_c == 4 * AB_C;
+}
+
+hipError_t write_absorb_mfma(const WriteCacheArgs& wa, const AbsorbArgs& aa, int cus, hipStream_t s) {
+  const int R = wa.d_c + wa.d_r;
+  const int n_wblocks = (R / 16) * ((wa.n_tokens + 16 * WA_TB4 - 1) / (16 * WA_TB4));
+  int n_ablocks = cus - n_wblocks;
+  if (n_ablocks > aa.H) n_ablocks = aa.H;
+  if (n_ablocks < (aa.H + 1) / 2) n_ablocks = (aa.H + 1) / 2;  // at most two heads per work-group
+  hipLaunchKernelGGL(k_write_absorb, dim3(n_wblocks + n_ablocks), dim3(1024), 0, s, wa, aa, n_wblocks, n_ablocks);
+  return hipGetLastError();
+}
 
 bool write_mfma_supported(int D, int d_c, int d_r) { return D % 64 == 0 && d_c % 16 == 0 && d_r % 16 == 0; }
 

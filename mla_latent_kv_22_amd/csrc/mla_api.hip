@@ -346,6 +346,35 @@ int mla_absorb_q(const mla_dims_t* dims, const void* q, const void* w_uk, const 
   return launched(absorb_generic(a, dims->dtype == MLA_BF16, stream));
 }
 
+int mla_write_absorb(const mla_dims_t* dims, const void* h, const void* w_dkr, const int32_t* positions,
+                     const int64_t* slot_mapping, int32_t n_write, void* pool, int32_t num_pages, const void* q,
+                     const void* w_uk, const int32_t* q_positions, int32_t n_q, void* q_abs, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_write < 0 || n_q < 0 || num_pages < 0) return MLA_ERR_ARG;
+  if (fp8_cache(dims) && n_write > 0) return MLA_ERR_WORKSPACE;  // the 8-bit write stages rows in a workspace
+  const bool fused = write_fast(dims) && absorb_fast(dims) &&
+                     write_absorb_fused_supported(n_write, n_q, dims->hidden, dims->d_c, dims->d_r,
+                                                  dims->num_heads, dims->qk_nope);
+  if (!fused) {
+    // the two calls in sequence (their own checks and paths)
+    st = mla_write_cache(dims, h, w_dkr, positions, slot_mapping, n_write, pool, num_pages, stream);
+    if (st != MLA_OK) return st;
+    return mla_absorb_q(dims, q, w_uk, q_positions, n_q, q_abs, stream);
+  }
+  if (!h || !w_dkr || !positions || !slot_mapping || !pool || !q || !w_uk || !q_positions || !q_abs)
+    return MLA_ERR_NULL;
+  if (num_pages < 1) return MLA_ERR_ARG;
+  int* err = device_error_word();
+  const int cus = current_cus();
+  if (!err || cus <= 0) return MLA_ERR_HIP;
+  WriteCacheArgs wa{h, w_dkr, positions, slot_mapping, pool, n_write, dims->hidden, dims->d_c,
+                    dims->d_r, dims->page_size, dims->rope_base, 0, num_pages, err};
+  AbsorbArgs aa{q, w_uk, q_positions, q_abs, n_q, dims->num_heads, dims->qk_nope, dims->d_c, dims->d_r,
+                dims->rope_base};
+  return launched(write_absorb_mfma(wa, aa, cus, stream));
+}
+
 size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t max_seq_len) {
   if (check_dims(dims) != MLA_OK || batch < 0 || batch > kMaxDecodeBatch || max_seq_len < 0) return 0;
   DecodeLayout L;

@@ -96,6 +96,11 @@ bool write_mfma_supported(int D, int d_c, int d_r);
 hipError_t write_cache_mfma(const WriteCacheArgs& a, hipStream_t s);
 bool absorb_mfma_supported(int H, int d_n, int d_c, int d_r);
 hipError_t absorb_mfma(const AbsorbArgs& a, hipStream_t s);
+// the decode step's cache write and absorption in one launch (at most 64
+// tokens each, d_n = 128, d_c = 512): bit-identical to write_cache_mfma then
+// absorb_mfma
+bool write_absorb_fused_supported(int n_write, int n_q, int D, int d_c, int d_r, int H, int d_n);
+hipError_t write_absorb_mfma(const WriteCacheArgs& wa, const AbsorbArgs& aa, int cus, hipStream_t s);
 
 // MFMA decode kernels (bf16, latent width 512, rotary width 64)
 bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch);

@@ -66,6 +66,11 @@ class DecodeStep:
         mla.write_cache(self.d, self.h, self.w_dkr, self.positions, self.slots, self.pool if pool is None else pool,
                         stream, workspace=self.write_ws)
 
+    def write_absorb(self, stream=None, pool=None):
+        """The cache write and the absorption in one call (mla_write_absorb)."""
+        mla.write_absorb(self.d, self.h, self.w_dkr, self.positions, self.slots, self.pool if pool is None else pool,
+                         self.q, self.w_uk, self.q_positions, self.q_abs, stream)
+
     def absorb(self, stream=None):
         mla.absorb_q(self.d, self.q, self.w_uk, self.q_positions, self.q_abs, stream)
 

@@ -193,6 +193,21 @@ def test_project_calls_check_arguments_before_the_device():
     assert po(bad, FAKE, 4) == -2
 
 
+def test_write_absorb_checks_arguments_before_the_device():
+    L = mla.lib()
+    d = _dims()
+    wa = lambda dims, h, nw, q, nq: L.mla_write_absorb(  # noqa: E731
+        ctypes.byref(dims), h, FAKE, FAKE, FAKE, nw, FAKE, 4, q, FAKE, FAKE, nq, FAKE, None)
+    assert wa(d, FAKE, 0, FAKE, 0) == 0                       # nothing to do
+    assert wa(d, FAKE, -1, FAKE, 4) == -7
+    assert wa(d, FAKE, 4, FAKE, -2) == -7
+    assert wa(d, None, 4, FAKE, 4) == -1                      # fused path: every pointer checked first
+    assert wa(d, FAKE, 4, None, 4) == -1
+    assert wa(_dims(d_c=3), FAKE, 4, FAKE, 4) == -2
+    assert wa(_dims(flags=mla.FLAG_FP8_CACHE), FAKE, 4, FAKE, 4) == -4  # the 8-bit write needs a workspace
+    assert wa(_dims(dtype="f32"), None, 4, FAKE, 4) == -1     # sequential path: mla_write_cache's check
+
+
 def test_binding_rejects_host_tensors():
     import torch
     d = _dims(hidden=8, num_heads=1, d_c=4, d_r=2, qk_nope=2, v_head=2, dtype="f32")
