@@ -1,9 +1,9 @@
 """Benchmark of one MLA decode step on one MI355X.
 
 A step is the whole decode hot path on one batch: write the newest latent row
-of every sequence (mla_write_cache), absorb W_UK into the queries
-(mla_absorb_q), then split-T decode + LSE-merge combine with W_UV
-(mla_decode).  Default workload: DeepSeek-V3 attention shapes, B=64 sequences
+of every sequence and absorb W_UK into the queries (mla_write_absorb, the
+result of mla_write_cache then mla_absorb_q in one launch), then split-T
+decode + LSE-merge combine with W_UV (mla_decode).  Default workload: DeepSeek-V3 attention shapes, B=64 sequences
 of T=8192 cached tokens, H=128 heads, d_c=512, d_R=64, bf16, page size 64.
 
 Prints one JSON line.  `value` is latent-cache GB/s of the step: the
@@ -102,8 +102,7 @@ def stream_ceiling(gib=4, reps=5):
 
         def run():
             assert L.mla_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream) == 0
-        run()
-        torch.cuda.synchronize()
+        prewarm(lambda i: run(), 0.1)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in evs:
             a.record(stream)
@@ -119,6 +118,21 @@ def stream_ceiling(gib=4, reps=5):
             "kernel": "libmla_probe.so k_stream_read: 16-byte loads, 4 in flight per thread, 256 threads per group"}
 
 
+def prewarm(fn, seconds=0.2):
+    """Untimed calls fn(0), fn(1), ... for `seconds`: after an idle spell the
+    clock ramps up over the first tens of milliseconds of sustained load, and
+    calls measured there ran 10-20% slower."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def decode_call_leg(cfg, copies, n, ceiling=None):
     """The decode call alone (split + combine) at one workload: `copies` pool
     copies alternate so that the cache is not warm in the Infinity Cache;
@@ -132,9 +146,7 @@ def decode_call_leg(cfg, copies, n, ceiling=None):
     st.step()
     pools = [st.pool] + [st.pool.clone() for _ in range(copies - 1)]
     stream = torch.cuda.current_stream()
-    for i in range(10):
-        st.attend(pool=pools[i % copies])
-    torch.cuda.synchronize()
+    prewarm(lambda i: st.attend(pool=pools[i % copies]))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for i, (a, b) in enumerate(evs):
         a.record(stream)
@@ -186,9 +198,7 @@ def projection_leg(n=64, calls=30):
     stream = torch.cuda.current_stream()
 
     def timed(fn):
-        for i in range(5):
-            fn(i)
-        torch.cuda.synchronize()
+        prewarm(fn)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
         for i, (a, b) in enumerate(evs):
             a.record(stream)
@@ -283,9 +293,9 @@ def prefill_flops(cfg, lens):
 
 def prefill_leg(steps=5, warmup=10):
     """Cache write of every token + causal prefill at the v3_prefill workload.
-    Each timed block follows `warmup` untimed calls of the same operation, so
-    that the clocks have settled under the sustained load (the first calls
-    after idle run up to 20% slower)."""
+    Each timed block follows 0.2 s and then `warmup` untimed calls of the same
+    operation, so that the clocks have settled under the sustained load (the
+    first calls after idle run up to 20% slower)."""
     import numpy as np
     import torch
     from mla_latent_kv_22_amd import harness, inputs as I
@@ -308,6 +318,7 @@ def prefill_leg(steps=5, warmup=10):
         return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     def settle(fn):
+        prewarm(lambda i: fn())
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -374,8 +385,7 @@ def fp8_leg(steps=20):
         mla.write_cache(st.d, st.h, st.w_dkr, st.positions, st.slots, pools[i % 2], workspace=ws)
 
     def timed(fn, n):
-        for i in range(3):
-            fn(i)
+        prewarm(fn, 0.1)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for i in range(n):
@@ -412,6 +422,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache leg")
     ap.add_argument("--no-graph", action="store_true", help="launch the step's kernels eagerly")
+    ap.add_argument("--prewarm-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup steps (the clock ramps up under load)")
     ap.add_argument("--no-legs", action="store_true", help="skip the other decode workloads and the read ceiling")
     ap.add_argument("--calibrate", action="store_true", help="only the counter-calibration copy")
     args = ap.parse_args()
@@ -448,17 +460,18 @@ def main():
     stream = torch.cuda.current_stream()
     algo_bytes = int(np.sum(inp["seq_lens"].astype(np.int64))) * cfg.row_width * 2
 
-    # the three calls run back to back on one stream: a side stream for the
-    # cache write (concurrent with the absorption) measured 17 us slower per
-    # step in a graph, the cost of joining the two streams before the decode
+    # one stream: mla_write_absorb (the cache write and the absorption in one
+    # launch), then the decode.  A side stream for a separate cache write
+    # (concurrent with the absorption) measured 17 us slower per step in a
+    # graph, the cost of joining the two streams before the decode.
     def step(i):
         st.step(pool=pools[i % 2])
 
-    for i in range(args.warmup):
+    for i in range(2):
         step(i)
     torch.cuda.synchronize()
     if not args.no_graph:
-        # one HIP graph per cache copy: the step's four launches replay without
+        # one HIP graph per cache copy: the step's three launches replay without
         # host launch gaps (the kernels allocate nothing and take no host sync)
         graphs = []
         for k in range(2):
@@ -470,9 +483,12 @@ def main():
 
         def step(i):  # noqa: F811
             graphs[i % 2].replay()
-        for i in range(2):
-            step(i)
-        torch.cuda.synchronize()
+    # the timed step runs untimed for --prewarm-s seconds (the clock ramps up
+    # under load), then W warmup steps
+    prewarm(step, args.prewarm_s)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
     print("[bench] warm", file=sys.stderr, flush=True)
 
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -496,9 +512,12 @@ def main():
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in evs])
 
+    # the decode first, while the clock is where the step loop left it; the
+    # short projection calls after it
+    t_decode = timed(lambda i: st.attend(pool=pools[i % 2]), args.steps)
     t_write = timed(lambda i: st.write(pool=pools[i % 2]), args.steps)
     t_absorb = timed(lambda i: st.absorb(), args.steps)
-    t_decode = timed(lambda i: st.attend(pool=pools[i % 2]), args.steps)
+    t_wa = timed(lambda i: st.write_absorb(pool=pools[i % 2]), args.steps)
     dec_ms = float(np.mean(t_decode))
 
     flops = 2.0 * cfg.num_heads * (cfg.row_width + cfg.d_c) * float(np.sum(inp["seq_lens"]))
@@ -510,6 +529,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_s": args.prewarm_s,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -519,13 +539,15 @@ def main():
         "config": {"workload": f"{cfg.name}: B={cfg.batch} T={cfg.seq_len}{' (max, ragged)' if cfg.min_seq_len else ''} "
                                f"H={cfg.num_heads} d_c={cfg.d_c} d_R={cfg.d_r} d_v={cfg.v_head} bf16 page={cfg.page_size}",
                    "batch": cfg.batch, "context": cfg.seq_len, "heads": cfg.num_heads,
-                   "step": "write_cache(B rows), absorb_q, decode(split + combine), one stream",
+                   "step": "write_absorb (cache write of B rows + absorb_q, one launch), decode(split + combine), "
+                           "one stream",
                    "launch": "eager" if args.no_graph else "hip graph per step",
                    "cache_copies_rotated": 2},
         "pct_hbm_peak": round(100.0 * algo_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(cfg.batch / (ms_step * 1e-3), 1),
         "algorithmic_bytes_per_step": algo_bytes,
-        "phases_ms": {"write_cache": round(float(np.mean(t_write)), 5), "absorb_q": round(float(np.mean(t_absorb)), 5),
+        "phases_ms": {"write_absorb": round(float(np.mean(t_wa)), 5),
+                      "write_cache": round(float(np.mean(t_write)), 5), "absorb_q": round(float(np.mean(t_absorb)), 5),
                       "decode": round(dec_ms, 5),
                       "decode_p50_p95_p99": [round(float(np.percentile(t_decode, p)), 5) for p in (50, 95, 99)]},
         "roofline": {"kernel": "mla_decode (split-T pass + combine, one stream)", "bound": "hbm",

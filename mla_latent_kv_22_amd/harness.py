@@ -78,10 +78,11 @@ class DecodeStep:
         mla.decode(self.d, self.q_abs, self.pool if pool is None else pool, self.block_table, self.seq_lens,
                    self.max_seq_len, self.w_uv, self.out, self.lse, self.workspace, stream)
 
-    def step(self, stream=None, pool=None, side_stream=None):
-        """write_cache, absorb_q, decode.  With side_stream, the cache write
-        (which only touches the new rows) runs there concurrently with the
-        absorption, and decode waits for both."""
+    def step(self, stream=None, pool=None, side_stream=None, fused=True):
+        """Cache write, absorption, decode.  By default the first two are one
+        mla_write_absorb call; fused=False makes them two calls.  With
+        side_stream, the cache write (which only touches the new rows) runs
+        there concurrently with the absorption, and decode waits for both."""
         pool = self.pool if pool is None else pool
         main = stream if stream is not None else torch.cuda.current_stream()
         if side_stream is not None:
@@ -89,6 +90,8 @@ class DecodeStep:
             self.write(side_stream, pool)
             self.absorb(main)
             main.wait_stream(side_stream)
+        elif fused and not self.d.flags & mla.FLAG_FP8_CACHE:  # the 8-bit write needs its workspace
+            self.write_absorb(main, pool)
         else:
             self.write(main, pool)
             self.absorb(main)
