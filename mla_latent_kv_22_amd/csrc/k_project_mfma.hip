@@ -438,7 +438,7 @@ __global__ void __launch_bounds__(256) k_absorb_mfma(AbsorbArgs a) {
 constexpr int WA_WBLK = 32768;                 // one W_UK column block: 128 rows x 256 bytes
 constexpr int WA_LDS = 4 * WA_WBLK + AB_T * 256;  // + the q_C block: 147456 bytes
 // cache-write tiles of 16 features x 16 WA_TB4 tokens, WA_NSL LDS slices per wave
-constexpr int WA_TB4 = 1, WA_NSL = 2;
+constexpr int WA_TB4 = 2, WA_NSL = 1, WA_KB = 3;
 static_assert(sizeof(WriteLds<WA_TB4, 16, WA_NSL>) <= (size_t)WA_LDS, "write tile fits the fused kernel's LDS");
 
 __device__ __forceinline__ void absorb_head16(const AbsorbArgs& a, int h, char* smem) {
@@ -551,7 +551,7 @@ __global__ void __launch_bounds__(1024, 1) k_write_absorb(WriteCacheArgs wa, Abs
   const int x = blockIdx.x;
   if (x < n_wblocks) {
     const int fb = (wa.d_c + wa.d_r) / 16;
-    write_tile<WA_TB4, 16, 4, WA_NSL>(wa, x % fb, x / fb, *(WriteLds<WA_TB4, 16, WA_NSL>*)smem);
+    write_tile<WA_TB4, 16, WA_KB, WA_NSL>(wa, x % fb, x / fb, *(WriteLds<WA_TB4, 16, WA_NSL>*)smem);
     return;
   }
   for (int h = x - n_wblocks; h < aa.H; h += n_ablocks) {
