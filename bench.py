@@ -421,7 +421,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache leg")
-    ap.add_argument("--no-graph", action="store_true", help="launch the step's kernels eagerly")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as a HIP graph (one per cache copy) instead of launching it eagerly")
+    ap.add_argument("--no-graph", action="store_true", help="eager launches (the default)")
     ap.add_argument("--prewarm-s", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup steps (the clock ramps up under load)")
     ap.add_argument("--no-legs", action="store_true", help="skip the other decode workloads and the read ceiling")
@@ -463,14 +465,17 @@ def main():
     # one stream: mla_write_absorb (the cache write and the absorption in one
     # launch), then the decode.  A side stream for a separate cache write
     # (concurrent with the absorption) measured 17 us slower per step in a
-    # graph, the cost of joining the two streams before the decode.
+    # graph, the cost of joining the two streams before the decode.  Eager
+    # launches by default: the host stays ahead of the GPU, so the kernels of
+    # consecutive steps run back to back, while graph replays left about 8 us
+    # idle between one replay and the next (kernel trace).
     def step(i):
         st.step(pool=pools[i % 2])
 
     for i in range(2):
         step(i)
     torch.cuda.synchronize()
-    if not args.no_graph:
+    if args.graph and not args.no_graph:
         # one HIP graph per cache copy: the step's three launches replay without
         # host launch gaps (the kernels allocate nothing and take no host sync)
         graphs = []
@@ -541,7 +546,7 @@ def main():
                    "batch": cfg.batch, "context": cfg.seq_len, "heads": cfg.num_heads,
                    "step": "write_absorb (cache write of B rows + absorb_q, one launch), decode(split + combine), "
                            "one stream",
-                   "launch": "eager" if args.no_graph else "hip graph per step",
+                   "launch": "hip graph per step" if args.graph and not args.no_graph else "eager, one stream",
                    "cache_copies_rotated": 2},
         "pct_hbm_peak": round(100.0 * algo_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(cfg.batch / (ms_step * 1e-3), 1),
