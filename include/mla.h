@@ -169,20 +169,41 @@ size_t mla_page_bytes(const mla_dims_t* dims);
 int mla_absorb_q(const mla_dims_t* dims, const void* q, const void* w_uk,
                  const int32_t* positions, int32_t n_tokens, void* q_abs, hipStream_t stream);
 
+/* Bytes of workspace mla_write_absorb needs for n_write rows (0 on invalid
+ * arguments): 256 bytes of counters, then the split-K partials of the fused
+ * launch (2 MiB at D = 7168, d_c + d_r = 576) or, for an 8-bit cache, the
+ * bf16 staging of the rows. */
+size_t mla_write_absorb_workspace_size(const mla_dims_t* dims, int32_t n_write);
+
 /*
- * The decode step's cache write and query absorption in one call: the
- * result is that of mla_write_cache(dims, h, w_dkr, positions, slot_mapping,
- * n_write, pool, num_pages) followed by mla_absorb_q(dims, q, w_uk,
- * q_positions, n_q, q_abs), bit for bit, with the same arguments, layouts and
- * errors (the two are independent: the absorption does not read the pool).
- * With bf16 operands on the MFMA paths, n_write and n_q in [1, 64], d_n = 128
- * and d_c = 512, both run in one launch, so the absorption uses the CUs the
- * cache write leaves idle; otherwise the two calls run in sequence.  An 8-bit
- * cache returns MLA_ERR_WORKSPACE (its write needs mla_write_cache_ws).
+ * The decode step's cache write and query absorption in one call
+ * (openarchlab section 2 steps 1-2).  The result is that of
+ * mla_write_cache_ws(dims, h, w_dkr, positions, slot_mapping, n_write, pool,
+ * num_pages) followed by mla_absorb_q(dims, q, w_uk, q_positions, n_q,
+ * q_abs), with the same arguments, layouts and errors (the two are
+ * independent: the absorption does not read the pool).
+ *
+ * With bf16 operands on the MFMA paths, n_write and n_q in [1, 64], d_n = 128,
+ * d_c = 512, D a multiple of 64 up to 8192 and d_c + d_r a multiple of 64,
+ * both run in one launch, so the absorption uses the CUs the cache write
+ * leaves idle; otherwise the two calls run in sequence.  In the one launch
+ * the rows are written by a split-K product: each row is the same fp32 sum
+ * as mla_write_cache's, added in another order, then rounded once to bf16
+ * (so a value can differ from mla_write_cache's by one bf16 unit in the
+ * last place); the order is fixed, so the call is deterministic.  q_abs is
+ * bit-identical to mla_absorb_q's.
+ *
+ *   workspace  >= mla_write_absorb_workspace_size(dims, n_write) bytes, of
+ *              device memory that only this call uses.  Its first 256
+ *              bytes must be zero before the first call (a zero-filled
+ *              allocation); every call leaves them zero.  Calls that share
+ *              a workspace must not overlap (one stream, or ordered).
+ *              NULL is accepted when the size is 0.
  */
 int mla_write_absorb(const mla_dims_t* dims, const void* h, const void* w_dkr, const int32_t* positions,
                      const int64_t* slot_mapping, int32_t n_write, void* pool, int32_t num_pages, const void* q,
-                     const void* w_uk, const int32_t* q_positions, int32_t n_q, void* q_abs, hipStream_t stream);
+                     const void* w_uk, const int32_t* q_positions, int32_t n_q, void* q_abs, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace mla_decode needs for `batch` sequences of at most
  * max_seq_len tokens (0 on invalid arguments or when no device is present). */

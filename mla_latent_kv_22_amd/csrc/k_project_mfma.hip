@@ -424,22 +424,146 @@ __global__ void __launch_bounds__(256) k_absorb_mfma(AbsorbArgs a) {
 }
 
 // ---------------------------------------------------------------- write + absorption, one launch
-// The decode step's cache write (k_write_mfma<1, 16, 4, 2> tiles, 144
-// work-groups at 64 tokens) leaves most CUs idle for its whole duration, and
-// the absorption does not depend on it.  k_write_absorb runs both in one
-// grid of 1024-thread work-groups: the first ones are cache-write tiles, the
-// rest each take whole heads of the absorption (d_n = 128, d_c = 512, at
-// most 64 tokens).  For a head, sub-group s (threads 256 s .. +255, four
-// waves) computes latent columns 128 s .. +127 exactly as one k_absorb_mfma
+// A decode step's cache write and absorption each leave most CUs idle and do
+// not depend on each other.  k_write_absorb runs both in one grid of
+// 1024-thread work-groups: the first nfb * S are split-K tiles of the cache
+// write, the rest each take whole heads of the absorption (d_n = 128,
+// d_c = 512, at most 64 tokens).
+//
+// Cache write, split over the hidden axis: work-group (fb, s) computes
+// features 64 fb .. +63 against every token (at most 64) over hidden chunks
+// [s nchunk / S, (s + 1) nchunk / S) of 64.  The W and h rows of its chunks
+// arrive by direct-to-LDS loads in one batch (at most WS_MAXC chunks of
+// 128 rows x 128 bytes, 16-byte piece p of row r at slot p ^ (r % 8)), so a
+// work-group waits for memory once; a tile that covers the whole hidden axis
+// instead moves its bytes through one CU in several dependent rounds.  Wave w
+// computes features 16 (w % 4) .. +15 x tokens 16 (w / 4) .. +15 (16x16x32
+// MFMA, chunks in order) and stores that fp32 partial.  A device-scope
+// counter per feature block elects the block's last work-group to finish; it
+// adds the S partials in slice order (a fixed order: the rows do not depend
+// on which work-group finishes last), rotates the k_R pairs and stores the
+// bf16 rows to their slots, and returns the counter to zero.
+//
+// Absorption: for a head, sub-group s (threads 256 s .. +255, four waves)
+// computes latent columns 128 s .. +127 exactly as one k_absorb_mfma
 // work-group does (same operands, same k order, so the results are
 // bit-identical); the q_C block is staged once for the four, and each
 // sub-group's W_UK column block is overwritten by its output tile once every
 // wave has finished reading it.
 constexpr int WA_WBLK = 32768;                 // one W_UK column block: 128 rows x 256 bytes
 constexpr int WA_LDS = 4 * WA_WBLK + AB_T * 256;  // + the q_C block: 147456 bytes
-// cache-write tiles of 16 features x 16 WA_TB4 tokens, WA_NSL LDS slices per wave
-constexpr int WA_TB4 = 2, WA_NSL = 1, WA_KB = 3;
-static_assert(sizeof(WriteLds<WA_TB4, 16, WA_NSL>) <= (size_t)WA_LDS, "write tile fits the fused kernel's LDS");
+constexpr int WS_MAXC = 8;                     // hidden chunks of 64 per split-K tile (16 KiB of LDS each)
+constexpr int WS_MAXS = 16;                    // split-K slices
+constexpr int WS_PART = 64 * 64;               // floats of one tile's partial: [64 tokens][64 features]
+static_assert(WS_MAXC * 16384 <= WA_LDS, "split-K tile fits the fused kernel's LDS");
+
+// buffer resource word 3 for raw 32-bit accesses, and the sc1 cache-policy
+// bit of buffer loads and stores (device-coherent across the XCDs' L2 caches)
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCoherent = 16;
+
+struct WriteSplit {
+  int S, nfb;     // slices of the hidden axis, 64-feature blocks (R / 64)
+  int* counters;  // [nfb], zero between calls
+  float* part;    // [S][nfb][WS_PART]
+};
+
+__device__ __forceinline__ void write_split_tile(const WriteCacheArgs& a, const WriteSplit& ws, int fb, int s,
+                                                 char* smem) {
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int D = a.D, nchunk = D / 64;
+  const int c0 = s * nchunk / ws.S, nc = (s + 1) * nchunk / ws.S - c0;  // nc <= WS_MAXC
+  // wave w loads rows 8 w .. 8 w + 7 of every chunk: waves 0-7 W rows
+  // 64 fb + 8 w + l / 8, waves 8-15 h rows (tokens past the last repeat it;
+  // their products are not stored); lane l fills slot l % 8 with source piece
+  // (l % 8) ^ (row % 8)
+  {
+    const int row = 8 * w + (lane >> 3), piece = (lane & 7) ^ (row & 7);
+    const char* src = w < 8 ? (const char*)a.w_dkr + ((size_t)(64 * fb + row) * D + 64 * c0 + 8 * piece) * 2
+                            : (const char*)a.h + ((size_t)min(row - 64, a.n_tokens - 1) * D + 64 * c0 + 8 * piece) * 2;
+    const uint32_t lds = lds_addr_of(smem) + 1024 * w;
+#pragma unroll
+    for (int i = 0; i < WS_MAXC; ++i)
+      if (i < nc) dma16_v(src + 128 * i, lds + 16384 * i);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  asm volatile("" ::: "memory");
+  const int m = lane & 15, q = lane >> 4;
+  const int fw = w & 3, tw = w >> 2;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < WS_MAXC; ++i) {
+    if (i >= nc) break;
+    const char* cb = smem + 16384 * i;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int sl = (4 * kk + q) ^ (m & 7);
+      const u32x4 av = *(const u32x4*)(cb + (16 * fw + m) * 128 + 16 * sl);
+      const u32x4 bv = *(const u32x4*)(cb + (64 + 16 * tw + m) * 128 + 16 * sl);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
+    }
+  }
+  // D: lane holds token 16 tw + m, features 16 fw + 4 q + j.  The partial
+  // goes out as device-coherent stores (written through to the level every
+  // XCD reads), and every wave waits for them before the work-group counts
+  // its slice in: the reducer's device-coherent loads then see them.  No
+  // cache-wide write-back or invalidation is needed (nothing else of this
+  // exchange passes through the per-XCD L2 caches).
+  // (16-byte buffer accesses with the sc1 cache policy, the device-coherent
+  // form; the resource covers exactly the partials)
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      ws.part, (short)0, ws.S * ws.nfb * WS_PART * (int)sizeof(float), kBufferRsrcWord3);
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(u32x4, acc), prs,
+      (int)sizeof(float) * ((s * ws.nfb + fb) * WS_PART + (16 * tw + m) * 64 + 16 * fw + 4 * q), 0, kCoherent);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  if (tid == 0) {
+    const int last = atomicAdd(ws.counters + fb, 1) == ws.S - 1;
+    if (last) atomicExch(ws.counters + fb, 0);  // every slice has counted: ready for the next call
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const int t = tid >> 4, f4 = tid & 15;
+  if (t >= a.n_tokens) return;
+  const int pb = (int)sizeof(float) * (fb * WS_PART + t * 64 + 4 * f4);
+  // all WS_MAXS loads in flight at once: slices k >= S lie past the end of
+  // the resource, where buffer loads return zero (and their values are not used)
+  f32x4 pv[WS_MAXS];
+#pragma unroll
+  for (int k = 0; k < WS_MAXS; ++k)
+    pv[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          prs, pb + (int)sizeof(float) * k * ws.nfb * WS_PART, 0, kCoherent));
+  const long long sl = a.dense ? (long long)t : a.slots[t];
+  const int pos = a.positions[t];
+  f32x4 v = pv[0];
+#pragma unroll
+  for (int k = 1; k < WS_MAXS; ++k) {
+    const f32x4 sum = v + pv[k];
+    v = k < ws.S ? sum : v;
+  }
+  const long long slot = checked_slot(sl, a.num_pages, a.P, a.err);
+  if (slot < 0) return;
+  const int R = a.d_c + a.d_r, rf = 64 * fb + 4 * f4;
+  float o[4] = {v[0], v[1], v[2], v[3]};
+  if (rf >= a.d_c) {
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      float c, sn;
+      rope_cs_theta(pos, rope_inv_freq((rf - a.d_c) / 2 + pr, a.d_r, a.rope_base), c, sn);
+      const float x0 = o[2 * pr], x1 = o[2 * pr + 1];
+      o[2 * pr] = x0 * c - x1 * sn;
+      o[2 * pr + 1] = x0 * sn + x1 * c;
+    }
+  }
+  const uint32_t lo = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+  *(uint2*)((uint16_t*)a.pool + (size_t)slot * R + rf) = make_uint2(lo, hi);
+}
 
 __device__ __forceinline__ void absorb_head16(const AbsorbArgs& a, int h, char* smem) {
   constexpr int DN = 128, NP = AB_DR / 2;
@@ -544,14 +668,14 @@ __device__ __forceinline__ void absorb_head16(const AbsorbArgs& a, int h, char* 
   }
 }
 
-// Work-group x < n_wblocks: cache-write tile (x % (R / 16), x / (R / 16));
-// otherwise heads x - n_wblocks, x - n_wblocks + n_ablocks, ... of the absorption.
-__global__ void __launch_bounds__(1024, 1) k_write_absorb(WriteCacheArgs wa, AbsorbArgs aa, int n_wblocks, int n_ablocks) {
+// Work-group x < nfb S: split-K write tile (x % nfb, x / nfb); otherwise heads
+// x - nfb S, x - nfb S + n_ablocks, ... of the absorption.
+__global__ void __launch_bounds__(1024, 1) k_write_absorb(WriteCacheArgs wa, AbsorbArgs aa, WriteSplit ws,
+                                                          int n_ablocks) {
   __shared__ __attribute__((aligned(16))) char smem[WA_LDS];
-  const int x = blockIdx.x;
+  const int x = blockIdx.x, n_wblocks = ws.nfb * ws.S;
   if (x < n_wblocks) {
-    const int fb = (wa.d_c + wa.d_r) / 16;
-    write_tile<WA_TB4, 16, WA_KB, WA_NSL>(wa, x % fb, x / fb, *(WriteLds<WA_TB4, 16, WA_NSL>*)smem);
+    write_split_tile(wa, ws, x % ws.nfb, x / ws.nfb, smem);
     return;
   }
   for (int h = x - n_wblocks; h < aa.H; h += n_ablocks) {
@@ -562,18 +686,33 @@ __global__ void __launch_bounds__(1024, 1) k_write_absorb(WriteCacheArgs wa, Abs
 
 }  // namespace
 
-bool write_absorb_fused_supported(int n_write, int n_q, int D, int d_c, int d_r, int H, int d_n) {
-  return n_write >= 1 && n_write <= 64 && n_q >= 1 && n_q <= AB_T && write_mfma_supported(D, d_c, d_r) &&
-         absorb_mfma_supported(H, d_n, d_c, d_r) && d_n == 128 && d_c == 4 * AB_C;
+static int write_split_slices(int D) { return (D / 64 + WS_MAXC - 1) / WS_MAXC; }
+
+bool write_absorb_fused_supported(int n_write, int D, int d_c, int d_r) {
+  const int R = d_c + d_r;
+  return n_write >= 1 && n_write <= 64 && D % 64 == 0 && D >= 64 && write_split_slices(D) <= WS_MAXS && R % 64 == 0 &&
+         R / 64 <= 64 && d_c == 4 * AB_C && d_r % 2 == 0;
 }
 
-hipError_t write_absorb_mfma(const WriteCacheArgs& wa, const AbsorbArgs& aa, int cus, hipStream_t s) {
-  const int R = wa.d_c + wa.d_r;
-  const int n_wblocks = (R / 16) * ((wa.n_tokens + 16 * WA_TB4 - 1) / (16 * WA_TB4));
+bool write_absorb_absorb_supported(int n_q, int H, int d_n, int d_c, int d_r) {
+  return n_q >= 1 && n_q <= AB_T && absorb_mfma_supported(H, d_n, d_c, d_r) && d_n == 128 && d_c == 4 * AB_C;
+}
+
+size_t write_absorb_ws_bytes(int D, int d_c, int d_r) {
+  return 256 + (size_t)write_split_slices(D) * ((d_c + d_r) / 64) * WS_PART * sizeof(float);
+}
+
+hipError_t write_absorb_mfma(const WriteCacheArgs& wa, const AbsorbArgs& aa, void* workspace, int cus, hipStream_t s) {
+  WriteSplit ws;
+  ws.S = write_split_slices(wa.D);
+  ws.nfb = (wa.d_c + wa.d_r) / 64;
+  ws.counters = (int*)workspace;
+  ws.part = (float*)((char*)workspace + 256);
+  const int n_wblocks = ws.nfb * ws.S;
   int n_ablocks = cus - n_wblocks;
   if (n_ablocks > aa.H) n_ablocks = aa.H;
   if (n_ablocks < (aa.H + 1) / 2) n_ablocks = (aa.H + 1) / 2;  // at most two heads per work-group
-  hipLaunchKernelGGL(k_write_absorb, dim3(n_wblocks + n_ablocks), dim3(1024), 0, s, wa, aa, n_wblocks, n_ablocks);
+  hipLaunchKernelGGL(k_write_absorb, dim3(n_wblocks + n_ablocks), dim3(1024), 0, s, wa, aa, ws, n_ablocks);
   return hipGetLastError();
 }
 

@@ -346,25 +346,47 @@ int mla_absorb_q(const mla_dims_t* dims, const void* q, const void* w_uk, const 
   return launched(absorb_generic(a, dims->dtype == MLA_BF16, stream));
 }
 
+// the fused launch covers the dims' write (bf16, split-K tiles) for n_write rows
+static bool write_absorb_fused_write(const mla_dims_t* d, int n_write) {
+  return write_fast(d) && !fp8_cache(d) && d->dtype == MLA_BF16 &&
+         write_absorb_fused_supported(n_write, d->hidden, d->d_c, d->d_r);
+}
+
+size_t mla_write_absorb_workspace_size(const mla_dims_t* dims, int32_t n_write) {
+  if (check_dims(dims) != MLA_OK || n_write < 0) return 0;
+  // 256 bytes of counters first; the 8-bit staging of the sequential path
+  // starts behind them, so it never disturbs them
+  size_t need = 0;
+  if (write_absorb_fused_write(dims, n_write)) need = write_absorb_ws_bytes(dims->hidden, dims->d_c, dims->d_r);
+  const size_t staged = mla_write_cache_workspace_size(dims, n_write);
+  if (staged > 0 && 256 + staged > need) need = 256 + staged;
+  return need;
+}
+
 int mla_write_absorb(const mla_dims_t* dims, const void* h, const void* w_dkr, const int32_t* positions,
                      const int64_t* slot_mapping, int32_t n_write, void* pool, int32_t num_pages, const void* q,
-                     const void* w_uk, const int32_t* q_positions, int32_t n_q, void* q_abs, hipStream_t stream) {
+                     const void* w_uk, const int32_t* q_positions, int32_t n_q, void* q_abs, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (n_write < 0 || n_q < 0 || num_pages < 0) return MLA_ERR_ARG;
-  if (fp8_cache(dims) && n_write > 0) return MLA_ERR_WORKSPACE;  // the 8-bit write stages rows in a workspace
-  const bool fused = write_fast(dims) && absorb_fast(dims) &&
-                     write_absorb_fused_supported(n_write, n_q, dims->hidden, dims->d_c, dims->d_r,
-                                                  dims->num_heads, dims->qk_nope);
+  const size_t need = mla_write_absorb_workspace_size(dims, n_write);
+  const bool fused = write_absorb_fused_write(dims, n_write) && absorb_fast(dims) &&
+                     write_absorb_absorb_supported(n_q, dims->num_heads, dims->qk_nope, dims->d_c, dims->d_r);
   if (!fused) {
-    // the two calls in sequence (their own checks and paths)
-    st = mla_write_cache(dims, h, w_dkr, positions, slot_mapping, n_write, pool, num_pages, stream);
+    // the two calls in sequence (their own checks and paths); an 8-bit
+    // write stages its rows behind the counters
+    if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+    st = mla_write_cache_ws(dims, h, w_dkr, positions, slot_mapping, n_write, pool, num_pages,
+                            need > 0 ? (char*)workspace + 256 : nullptr, need > 0 ? workspace_bytes - 256 : 0,
+                            stream);
     if (st != MLA_OK) return st;
     return mla_absorb_q(dims, q, w_uk, q_positions, n_q, q_abs, stream);
   }
   if (!h || !w_dkr || !positions || !slot_mapping || !pool || !q || !w_uk || !q_positions || !q_abs)
     return MLA_ERR_NULL;
   if (num_pages < 1) return MLA_ERR_ARG;
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   int* err = device_error_word();
   const int cus = current_cus();
   if (!err || cus <= 0) return MLA_ERR_HIP;
@@ -372,7 +394,7 @@ int mla_write_absorb(const mla_dims_t* dims, const void* h, const void* w_dkr, c
                     dims->d_r, dims->page_size, dims->rope_base, 0, num_pages, err};
   AbsorbArgs aa{q, w_uk, q_positions, q_abs, n_q, dims->num_heads, dims->qk_nope, dims->d_c, dims->d_r,
                 dims->rope_base};
-  return launched(write_absorb_mfma(wa, aa, cus, stream));
+  return launched(write_absorb_mfma(wa, aa, workspace, cus, stream));
 }
 
 size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t max_seq_len) {

@@ -99,8 +99,12 @@ hipError_t absorb_mfma(const AbsorbArgs& a, hipStream_t s);
 // the decode step's cache write and absorption in one launch (at most 64
 // tokens each, d_n = 128, d_c = 512): bit-identical to write_cache_mfma then
 // absorb_mfma
-bool write_absorb_fused_supported(int n_write, int n_q, int D, int d_c, int d_r, int H, int d_n);
-hipError_t write_absorb_mfma(const WriteCacheArgs& wa, const AbsorbArgs& aa, int cus, hipStream_t s);
+// the fused cache write + absorption (k_write_absorb): its write part, its
+// absorption part, its workspace (counters, then split-K partials)
+bool write_absorb_fused_supported(int n_write, int D, int d_c, int d_r);
+bool write_absorb_absorb_supported(int n_q, int H, int d_n, int d_c, int d_r);
+size_t write_absorb_ws_bytes(int D, int d_c, int d_r);
+hipError_t write_absorb_mfma(const WriteCacheArgs& wa, const AbsorbArgs& aa, void* workspace, int cus, hipStream_t s);
 
 // MFMA decode kernels (bf16, latent width 512, rotary width 64)
 bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch);

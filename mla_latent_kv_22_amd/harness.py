@@ -61,6 +61,9 @@ class DecodeStep:
         # the cache write's workspace: 8-bit row staging and the split-K partials
         wws = mla.write_cache_workspace_size(self.d, int(inp["h"].shape[0]))
         self.write_ws = torch.empty(max(wws, 1), dtype=torch.uint8, device=device)
+        # mla_write_absorb's workspace: counters (zero before the first call) and partials
+        waws = mla.write_absorb_workspace_size(self.d, int(inp["h"].shape[0]))
+        self.wa_ws = torch.zeros(max(waws, 1), dtype=torch.uint8, device=device)
 
     def write(self, stream=None, pool=None):
         mla.write_cache(self.d, self.h, self.w_dkr, self.positions, self.slots, self.pool if pool is None else pool,
@@ -69,7 +72,7 @@ class DecodeStep:
     def write_absorb(self, stream=None, pool=None):
         """The cache write and the absorption in one call (mla_write_absorb)."""
         mla.write_absorb(self.d, self.h, self.w_dkr, self.positions, self.slots, self.pool if pool is None else pool,
-                         self.q, self.w_uk, self.q_positions, self.q_abs, stream)
+                         self.q, self.w_uk, self.q_positions, self.q_abs, self.wa_ws, stream)
 
     def absorb(self, stream=None):
         mla.absorb_q(self.d, self.q, self.w_uk, self.q_positions, self.q_abs, stream)
@@ -90,7 +93,7 @@ class DecodeStep:
             self.write(side_stream, pool)
             self.absorb(main)
             main.wait_stream(side_stream)
-        elif fused and not self.d.flags & mla.FLAG_FP8_CACHE:  # the 8-bit write needs its workspace
+        elif fused:
             self.write_absorb(main, pool)
         else:
             self.write(main, pool)

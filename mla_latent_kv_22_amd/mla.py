@@ -29,7 +29,8 @@ _SYMBOLS = ("mla_write_cache", "mla_write_cache_ws", "mla_write_cache_workspace_
             "mla_decode_workspace_size", "mla_decode", "mla_prefill_workspace_size", "mla_prefill",
             "mla_prefill_kv", "mla_cache_bytes", "mla_page_bytes", "mla_status_string", "mla_uses_fast_path",
             "mla_get_device_error", "mla_debug_build", "mla_decode_noalloc", "mla_project_q_workspace_size",
-            "mla_project_q", "mla_project_out_workspace_size", "mla_project_out", "mla_write_absorb")
+            "mla_project_q", "mla_project_out_workspace_size", "mla_project_out", "mla_write_absorb",
+            "mla_write_absorb_workspace_size")
 DEVERR_PAGE, DEVERR_SLOT, DEVERR_LENGTH = 1, 2, 4
 
 
@@ -100,7 +101,9 @@ def lib() -> ctypes.CDLL:
         L.mla_project_out_workspace_size.restype = sz
         L.mla_project_out.argtypes = [dp, vp, vp, i32, vp, vp, sz, vp]
         L.mla_debug_build.argtypes = []
-        L.mla_write_absorb.argtypes = [dp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, i32, vp, vp]
+        L.mla_write_absorb.argtypes = [dp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp]
+        L.mla_write_absorb_workspace_size.argtypes = [dp, i32]
+        L.mla_write_absorb_workspace_size.restype = sz
         for f in ("mla_write_cache", "mla_write_cache_ws", "mla_absorb_q", "mla_decode", "mla_decode_noalloc",
                   "mla_prefill",
                   "mla_prefill_kv", "mla_uses_fast_path", "mla_get_device_error", "mla_debug_build",
@@ -186,18 +189,26 @@ def absorb_q(d: Dims, q, w_uk, positions, q_abs, stream=None) -> None:
                               _ptr(q_abs, "q_abs", dt), _stream(stream)), "mla_absorb_q")
 
 
-def write_absorb(d: Dims, h, w_dkr, positions, slot_mapping, pool, q, w_uk, q_positions, q_abs,
+def write_absorb_workspace_size(d: Dims, n_write: int) -> int:
+    return int(lib().mla_write_absorb_workspace_size(ctypes.byref(d), int(n_write)))
+
+
+def write_absorb(d: Dims, h, w_dkr, positions, slot_mapping, pool, q, w_uk, q_positions, q_abs, workspace=None,
                  stream=None) -> None:
-    """mla_write_absorb: write_cache then absorb_q, in one launch where it applies."""
+    """mla_write_absorb: write_cache then absorb_q, in one launch where it
+    applies.  workspace: write_absorb_workspace_size bytes, zero-filled before
+    its first use (each call leaves its counters at zero)."""
     dt = _torch_dtype(d)
     n_w = 0 if h is None else int(h.shape[0])
     n_q = 0 if q is None else int(q.shape[0])
+    ws = None if workspace is None else _ptr(workspace, "workspace", torch.uint8)
     _check(lib().mla_write_absorb(ctypes.byref(d), _ptr(h, "h", dt), _ptr(w_dkr, "w_dkr", dt),
                                   _ptr(positions, "positions", torch.int32),
                                   _ptr(slot_mapping, "slot_mapping", torch.int64), n_w,
                                   _ptr(pool, "pool", _pool_dtype(d)), int(pool.shape[0]), _ptr(q, "q", dt),
                                   _ptr(w_uk, "w_uk", dt), _ptr(q_positions, "q_positions", torch.int32), n_q,
-                                  _ptr(q_abs, "q_abs", dt), _stream(stream)), "mla_write_absorb")
+                                  _ptr(q_abs, "q_abs", dt), ws, 0 if workspace is None else workspace.numel(),
+                                  _stream(stream)), "mla_write_absorb")
 
 
 def decode_workspace_size(d: Dims, batch: int, max_seq_len: int) -> int:

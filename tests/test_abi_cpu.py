@@ -196,16 +196,34 @@ def test_project_calls_check_arguments_before_the_device():
 def test_write_absorb_checks_arguments_before_the_device():
     L = mla.lib()
     d = _dims()
-    wa = lambda dims, h, nw, q, nq: L.mla_write_absorb(  # noqa: E731
-        ctypes.byref(dims), h, FAKE, FAKE, FAKE, nw, FAKE, 4, q, FAKE, FAKE, nq, FAKE, None)
-    assert wa(d, FAKE, 0, FAKE, 0) == 0                       # nothing to do
+    wa = lambda dims, h, nw, q, nq, ws=FAKE, wsb=1 << 30: L.mla_write_absorb(  # noqa: E731
+        ctypes.byref(dims), h, FAKE, FAKE, FAKE, nw, FAKE, 4, q, FAKE, FAKE, nq, FAKE, ws, wsb, None)
+    assert wa(d, FAKE, 0, FAKE, 0, None, 0) == 0              # nothing to do
     assert wa(d, FAKE, -1, FAKE, 4) == -7
     assert wa(d, FAKE, 4, FAKE, -2) == -7
     assert wa(d, None, 4, FAKE, 4) == -1                      # fused path: every pointer checked first
     assert wa(d, FAKE, 4, None, 4) == -1
+    assert wa(d, FAKE, 4, FAKE, 4, None, 0) == -4             # fused path: its counters and partials
+    need = mla.write_absorb_workspace_size(d, 4)
+    assert wa(d, FAKE, 4, FAKE, 4, FAKE, need - 1) == -4
     assert wa(_dims(d_c=3), FAKE, 4, FAKE, 4) == -2
-    assert wa(_dims(flags=mla.FLAG_FP8_CACHE), FAKE, 4, FAKE, 4) == -4  # the 8-bit write needs a workspace
-    assert wa(_dims(dtype="f32"), None, 4, FAKE, 4) == -1     # sequential path: mla_write_cache's check
+    assert wa(_dims(flags=mla.FLAG_FP8_CACHE), FAKE, 4, FAKE, 4, None, 0) == -4  # the 8-bit write stages its rows
+    assert wa(_dims(dtype="f32"), None, 4, FAKE, 4, None, 0) == -1  # sequential path: mla_write_cache's check
+
+
+def test_write_absorb_workspace_size_formula():
+    # 256 bytes of counters, then one fp32 partial of 64 x 64 per split-K
+    # tile: ceil(D / 64 / 8) slices x (d_c + d_r) / 64 feature blocks
+    d = _dims()
+    assert mla.write_absorb_workspace_size(d, 64) == 256 + 14 * 9 * 64 * 64 * 4
+    assert mla.write_absorb_workspace_size(d, 1) == 256 + 14 * 9 * 64 * 64 * 4
+    assert mla.write_absorb_workspace_size(_dims(hidden=2048), 16) == 256 + 4 * 9 * 64 * 64 * 4
+    assert mla.write_absorb_workspace_size(_dims(hidden=1000), 16) == 0   # D not a multiple of 64: two calls
+    assert mla.write_absorb_workspace_size(d, 0) == 0                     # nothing to write
+    assert mla.write_absorb_workspace_size(d, 65) == 0                    # beyond a decode batch: two calls
+    assert mla.write_absorb_workspace_size(_dims(dtype="f32"), 64) == 0
+    assert mla.write_absorb_workspace_size(_dims(flags=mla.FLAG_FP8_CACHE), 64) == 256 + 64 * 576 * 2
+    assert mla.write_absorb_workspace_size(d, -1) == 0
 
 
 def test_binding_rejects_host_tensors():
