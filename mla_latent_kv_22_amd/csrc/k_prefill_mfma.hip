@@ -52,31 +52,50 @@ constexpr int PD = 128;  // d_n = d_v
 constexpr int PDR = 64;  // d_R
 
 // ---------------------------------------------------------------- up-projection
-constexpr int XT = 128;                     // tokens per work-group
-constexpr int XK = 64;                      // latent columns per k-chunk (128-byte rows)
-constexpr int XSTAGE = (XT + PD) * XK * 2;  // 32 KiB: 128 latent rows, then 128 weight rows
+// One work-group per (128 key tokens, head): K_C and V together, a
+// [128 x 512] . [512 x 256] product whose 256 weight rows are W_UK,h then
+// W_UV,h, so each latent row fetched serves both.  32-wide k chunks of the 128
+// latent rows (gathered through the block table) and the 256 weight rows
+// stream into a three-stage LDS ring by direct-to-LDS loads, two chunks
+// ahead, one barrier per chunk; two work-groups share a CU.  Wave (wo, wt) =
+// (w / 2, w % 2) computes outputs of W block wo (K_C or V) for tokens
+// 64 wt .. +63: 4 x 2 MFMA blocks, so a k step reads 6 fragments for 8 MFMAs.
+// (One work-group per K_C or V with 32 x 128 wave tiles read 5 fragments per
+// 4 MFMAs, and the LDS port, shared with the loads, set its pace: 0.80 ms
+// for the V3 prefill's 16,384 keys.)
+constexpr int XT = 128;                      // tokens per work-group
+constexpr int XW = 2 * PD;                   // weight rows: W_UK,h then W_UV,h
+constexpr int XK = 32;                       // latent columns per k-chunk (64-byte rows)
+constexpr int XNS = 3;                       // stages
+constexpr int XSTAGE = (XT + XW) * XK * 2;   // 24 KiB: 128 latent rows, then 256 weight rows
+constexpr int XLPW = (XT + XW) / 16 / 4;     // loads per wave per stage (6)
 
-// LDS stage row r (128 bytes): 16-byte chunk c at slot c ^ ((r >> 1) & 7).
-__device__ __forceinline__ int xslot(int r, int c) { return c ^ ((r >> 1) & 7); }
+// LDS stage row r (64 bytes): 16-byte piece c at slot c ^ ((r >> 2) & 3)
+// (the 16 rows of a quarter-wave's fragment reads cover all 64 banks).
+__device__ __forceinline__ int xslot(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 __global__ void __launch_bounds__(256, 2) k_prefill_proj(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * XSTAGE];
-  const int n0 = blockIdx.x * XT, h = blockIdx.y, which = blockIdx.z;  // 0: K_C, 1: V
+  __shared__ __attribute__((aligned(16))) char smem[XNS * XSTAGE];
+  const int n0 = blockIdx.x * XT, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
+  const int wo = w >> 1, wt = w & 1;
   const int N = a.total_kv, R = a.d_c + a.d_r;  // every key token: cached prefix and new
-  const char* __restrict__ Wh = (const char*)(which ? a.w_uv : a.w_uk) + (size_t)h * PD * a.d_c * 2;
+  const char* __restrict__ Wk = (const char*)a.w_uk + (size_t)h * PD * a.d_c * 2;
+  const char* __restrict__ Wv = (const char*)a.w_uv + (size_t)h * PD * a.d_c * 2;
   const uint32_t lds0 = lds_addr_of(smem);
 
-  // loads: instruction k (0..31) of a stage fills LDS bytes [1024 k, +1024):
-  // rows 8 (k % 16) + lane / 8 of the latent block (k < 16) or of the weight
-  // block (k >= 16), slot lane % 8.  Wave w issues k = w + 4 i.
-  const char* crow[4];
-  uint32_t cchunk[4], woff[4];
+  // loads: instruction k (0..23) of a stage fills LDS bytes [1024 k, +1024):
+  // rows 16 k' + lane / 4 (k' = k for the latent block, k < 8; k' = k - 8 of
+  // the weight block: W_UK,h rows for k' < 8, W_UV,h rows after), slot
+  // lane % 4 holding source piece slot ^ ((row >> 2) & 3).  Wave w issues
+  // k = w + 4 i (i < 6): latent rows for i < 2, W_UK,h for i < 4, W_UV,h after.
+  const char* crow[2];
+  uint32_t cchunk[2], woff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 8 * ((w + 4 * i) & 15) + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * (w + 4 * i) + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
     const int n = min(n0 + r, N - 1);
     const int s = seq_of(a.cu_kv, a.num_seqs, n);
     // clamped so that the block-table read stays in row s (max_kv_len <= capacity)
@@ -84,69 +103,84 @@ __global__ void __launch_bounds__(256, 2) k_prefill_proj(PrefillArgs a) {
     const int page = checked_page(a.block_table[(size_t)s * a.max_pages_per_seq + t / a.P], a.num_pages, a.err);
     crow[i] = (const char*)a.pool + ((size_t)page * a.P + t % a.P) * (size_t)R * 2;
     cchunk[i] = 16u * c;
+    // weight rows of loads i + 2 and i + 4: row r of W_UK,h, then of W_UV,h
+    // (r % 128 = r, (r + 128) >> 2 & 3 = r >> 2 & 3: the same slot)
     woff[i] = (uint32_t)(r * a.d_c * 2 + 16 * c);
   }
   auto issue = [&](int kc, int st) {
     const uint32_t base = lds0 + st * XSTAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16_v(crow[i] + 128 * kc + cchunk[i], base + 1024 * (w + 4 * i));
+    for (int i = 0; i < 2; ++i) dma16_v(crow[i] + 64 * kc + cchunk[i], base + 1024 * (w + 4 * i));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16<0>(Wh + 128 * kc, woff[i], base + 1024 * (16 + w + 4 * i));
+    for (int i = 0; i < 2; ++i) dma16<0>(Wk + 64 * kc, woff[i], base + XT * XK * 2 + 1024 * (w + 4 * i));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16<0>(Wv + 64 * kc, woff[i], base + XT * XK * 2 + 1024 * (8 + w + 4 * i));
   };
 
-  f32x16 acc[4];
+  f32x16 acc[4][2];  // [output block jt][token block tb]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) acc[jt][tb] = f32x16{};
   const int nk = a.d_c / XK;
-  issue(0, 0);
+#pragma unroll
+  for (int c = 0; c < XNS - 1; ++c)
+    if (c < nk) issue(c, c);
   for (int kc = 0; kc < nk; ++kc) {
-    if (kc + 1 < nk) {
-      issue(kc + 1, (kc + 1) & 1);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    __builtin_amdgcn_s_barrier();
+    // chunk kc has landed once at most the next chunk's loads remain
+    if (kc + 1 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_vm(XLPW));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();  // chunk kc in LDS; chunk kc-1's stage no longer read
     asm volatile("" ::: "memory");
-    const char* st = smem + (kc & 1) * XSTAGE;
-    const int ra = 32 * w + r32;  // B column: token
+    if (kc + XNS - 1 < nk) issue(kc + XNS - 1, (kc + XNS - 1) % XNS);
+    const char* st = smem + (kc % XNS) * XSTAGE;
 #pragma unroll
     for (int ks = 0; ks < XK / 16; ++ks) {
       const int c = 2 * ks + g;
-      const u32x4 av = *(const u32x4*)(st + ra * 128 + 16 * xslot(ra, c));
+      u32x4 bt[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int rt = 64 * wt + 32 * tb + r32;  // B column: token
+        bt[tb] = *(const u32x4*)(st + rt * (XK * 2) + 16 * xslot(rt, c));
+      }
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
-        const int rb = 32 * jt + r32;  // A row: output j (weight row)
-        const u32x4 bv = *(const u32x4*)(st + XT * 128 + rb * 128 + 16 * xslot(rb, c));
-        acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bv), as_bf16x8(av), acc[jt], 0, 0, 0);
+        const int rw = PD * wo + 32 * jt + r32;  // A row: weight row (output)
+        const u32x4 aw = *(const u32x4*)(st + XT * XK * 2 + rw * (XK * 2) + 16 * xslot(rw, c));
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          acc[jt][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aw), as_bf16x8(bt[tb]), acc[jt][tb], 0, 0, 0);
       }
     }
-    __syncthreads();  // the stage is free for the load two chunks on
   }
+  __syncthreads();  // every wave is done with the stages: the epilogue reuses them
 
-  // The products are D^T: lane holds token 32 w + lane % 32 and outputs
-  // j = 32 jt + 8 (e/4) + 4 g + e % 4, four consecutive j per e/4, stored as
-  // one 8-byte bf16 group.  Staged as bf16 [token][128], 16-byte slot
-  // (j / 8) ^ (token % 16), then written in whole 256-byte rows.
+  // The products are D^T: lane holds token 64 wt + 32 tb + lane % 32 and
+  // outputs j = 32 jt + 8 (e/4) + 4 g + e % 4 of block wo, four consecutive j
+  // per e/4, stored as one 8-byte bf16 group.  Staged as bf16
+  // [wo][token][128], 16-byte slot (j / 8) ^ (token % 16), then written in
+  // whole 256-byte rows.
   uint16_t* ot = (uint16_t*)smem;
-  {
-    const int tk = 32 * w + r32;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int tk = 64 * wt + 32 * tb + r32;
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
       for (int eg = 0; eg < 4; ++eg) {
         const int j0 = 32 * jt + 8 * eg + 4 * g;
-        const u32x2 v = {pack_bf16x2(acc[jt][4 * eg], acc[jt][4 * eg + 1]),
-                         pack_bf16x2(acc[jt][4 * eg + 2], acc[jt][4 * eg + 3])};
-        *(u32x2*)(ot + tk * PD + 8 * ((j0 >> 3) ^ (tk & 15)) + (j0 & 7)) = v;
+        const u32x2 v = {pack_bf16x2(acc[jt][tb][4 * eg], acc[jt][tb][4 * eg + 1]),
+                         pack_bf16x2(acc[jt][tb][4 * eg + 2], acc[jt][tb][4 * eg + 3])};
+        *(u32x2*)(ot + (wo * XT + tk) * PD + 8 * ((j0 >> 3) ^ (tk & 15)) + (j0 & 7)) = v;
       }
   }
   __syncthreads();
-  uint16_t* dst = (uint16_t*)(which ? a.ws_v : a.ws_k) + ((size_t)h * N + n0) * PD;
 #pragma unroll
-  for (int i = 0; i < XT * 16 / 256; ++i) {
-    const int u = i * 256 + tid, tk = u >> 4, c = u & 15;
-    if (n0 + tk < N) *(u32x4*)(dst + (size_t)tk * PD + 8 * c) = *(const u32x4*)(ot + tk * PD + 8 * (c ^ (tk & 15)));
+  for (int i = 0; i < 2 * XT * 16 / 256; ++i) {
+    const int u = i * 256 + tid, wb = u / (XT * 16), tk = (u >> 4) % XT, c = u & 15;
+    uint16_t* dst = (uint16_t*)(wb ? a.ws_v : a.ws_k) + ((size_t)h * N + n0) * PD;
+    if (n0 + tk < N)
+      *(u32x4*)(dst + (size_t)tk * PD + 8 * c) = *(const u32x4*)(ot + (wb * XT + tk) * PD + 8 * (c ^ (tk & 15)));
   }
 }
 
@@ -471,7 +505,7 @@ bool prefill_mfma_supported(int d_n, int d_v, int d_r, int d_c, int P) {
 
 hipError_t prefill_mfma(const PrefillArgs& a, hipStream_t s) {
   if (a.total == 0 || a.num_seqs == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_prefill_proj, dim3((a.total_kv + XT - 1) / XT, a.H, 2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_prefill_proj, dim3((a.total_kv + XT - 1) / XT, a.H), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.max_seq_len + AQ - 1) / AQ;
