@@ -579,6 +579,270 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
 }
 
 // ============================================================================
+// At most 16 heads (V2-Lite has 16): k_split16.  A 32-head MFMA block would
+// be half padding, and the work per token is small, so the layout changes:
+//   * 16-wide MFMAs: scores S^T[16 tokens][16 heads] with 16x16x32 (18 k
+//     steps over the 576-wide row), the latent update O^T[16 features][16
+//     heads] += C^T[16 features][16 tokens] P^T[16 tokens][16 heads] with
+//     16x16x16.  The score accumulator leaves lane l holding tokens
+//     4 (l / 16) .. +3 of head l % 16, which is exactly the lane's share of
+//     the P^T operand, so the numerators go from the accumulator to the
+//     latent MFMA in registers;
+//   * token-parallel waves: wave w takes the item's 16-token tiles w, w + 4,
+//     ... through a private two-stage ring (18 direct-to-LDS loads a tile),
+//     with its own reference maximum, sum and 512 x 16 accumulator; no
+//     barrier in the loop;
+//   * at the item's end the four waves merge in LDS (each scaled by
+//     2^(m_w - m*)) into one partial, in the layout the combine reads.
+// Tile layout in a stage: column group cg (64 features, 128 bytes per row)
+// of 16 rows at 2048 cg, 16-byte piece c of row r at slot c ^ ((r / 2) % 8):
+// the score fragment reads (16 rows, one piece each) cover all 64 banks.
+constexpr int T16 = 16;                        // tokens per tile
+constexpr int T16_BYTES = T16 * RW * 2;        // 18432
+constexpr int T16_LOADS = T16_BYTES / 1024;    // 18 wave-wide loads a tile
+constexpr int T16_WAVE = 2 * T16_BYTES;        // two stages per wave
+constexpr int T16_LDS = 4 * T16_WAVE;          // 147456
+static_assert(PLAN_INTS * 4 <= T16_WAVE, "planner arrays fit in one wave's stages");
+static_assert(4 * 16 * DC * 4 + 4 * 16 * 2 * 4 <= T16_LDS, "merge buffers fit");
+
+__device__ __forceinline__ int s16sw(int r) { return (r >> 1) & 7; }
+
+__global__ void __launch_bounds__(256, 1) k_split16(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[T16_LDS];
+  int* s_len = (int*)(smem + 3 * T16_WAVE);  // wave 3's stages, before its first load
+  int* s_items = s_len + (kMaxDecodeBatch + 1);
+  int* red = s_items + (kMaxDecodeBatch + 1);
+
+  const int cap = a.len_cap;
+  const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
+                                           a.ovh_tokens, s_len, s_items, red, a.err, a.max_items);
+  const int n_items = plan.n_items;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i <= a.batch; i += blockDim.x) a.plan[i] = s_items[i];
+    for (int i = threadIdx.x; i < a.batch; i += blockDim.x) a.plan[a.batch + 1 + i] = s_len[i];
+    if (threadIdx.x == 0) a.plan[2 * a.batch + 1] = plan.chunk;
+  }
+  const int G = gridDim.x;
+  const int rounds = (int)blockIdx.x < n_items ? (n_items - 1 - (int)blockIdx.x) / G + 1 : 0;
+  int d_item = 0, d_b = 0, d_t0 = 0, d_t1 = 0;
+  if (lane < rounds) {
+    const int idx = blockIdx.x + lane * G;
+    const int item = ((n_items & 7) == 0 && (G & 7) == 0) ? (idx & 7) * (n_items >> 3) + (idx >> 3) : idx;
+    const int b = item_seq(s_items, a.batch, item);
+    d_item = item;
+    d_b = b;
+    d_t0 = (item - s_items[b]) * plan.chunk;
+    d_t1 = min(s_len[b], d_t0 + plan.chunk);
+  }
+  __syncthreads();  // the planner arrays are not read after this point
+
+  const int hl = lane & 15, q4 = lane >> 4;  // head; token quad / k group
+  const bool hvalid = hl < a.H;
+  const int P = a.P;
+  const uint32_t page_bytes = (uint32_t)(P * RW * 2);
+  const char* __restrict__ pool = (const char*)a.pool;
+  char* wst = smem + w * T16_WAVE;  // this wave's two stages
+  const uint32_t lds_w = lds_addr_of(wst);
+  // load d of a tile: rows 8 (d % 2) + lane / 8 of column group d / 2, slot
+  // lane % 8 holding source piece slot ^ (row / 2 % 8); the column offset
+  // 128 (d / 2) goes into the scalar base
+  uint32_t ld_off[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int row = 8 * hf + (lane >> 3);
+    ld_off[hf] = (uint32_t)(row * (RW * 2) + 16 * ((lane & 7) ^ s16sw(row)));
+  }
+  // score A operand (token row hl, piece 4 (ks % 2) + q4 of group ks / 2)
+  const int sc_row = 128 * hl;
+  // transpose read for feature block fb: source lane l (in its 16-lane group
+  // q4) gives row 4 q4 + (l % 16) / 4, 8 bytes at features 16 fb + 4 (l % 4):
+  // piece 2 (fb % 4) + (l / 2) % 2 of group fb / 4, half l % 2
+  int tr_off[4];
+  {
+    const int row = 4 * q4 + (hl >> 2);
+#pragma unroll
+    for (int f4 = 0; f4 < 4; ++f4) tr_off[f4] = row * 128 + 16 * ((2 * f4 + ((hl >> 1) & 1)) ^ s16sw(row)) + 8 * (hl & 1);
+  }
+  const float sl2 = a.scale_log2;
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int item = __builtin_amdgcn_readlane(d_item, rd);
+    const int b = __builtin_amdgcn_readlane(d_b, rd);
+    const int t0 = __builtin_amdgcn_readlane(d_t0, rd);
+    const int t1 = __builtin_amdgcn_readlane(d_t1, rd);
+    const __attribute__((address_space(4))) int32_t* btb =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_table + (size_t)b * a.max_pages_per_seq);
+    const int ntiles = (t1 - t0 + T16 - 1) / T16;
+    const int nmine = w < ntiles ? (ntiles - 1 - w) / 4 + 1 : 0;  // tiles w, w + 4, ...
+    auto tile_src = [&](int j) {  // first row of tile j (P % 16 == 0: a tile lies in one page)
+      const int tok = t0 + T16 * j;
+      const int page = checked_page(btb[tok / P], a.num_pages, a.err);
+      return pool + (size_t)(uint32_t)page * page_bytes + (uint32_t)(tok % P) * (RW * 2);
+    };
+    auto issue = [&](int j, int st) {
+      const char* src = tile_src(j);
+      const int nv = min(T16, t1 - (t0 + T16 * j));
+      const uint32_t dst = lds_w + st * T16_BYTES;
+      if (nv == T16) {
+#pragma unroll
+        for (int d = 0; d < T16_LOADS; ++d) dma16<0>(src + 128 * (d >> 1), ld_off[d & 1], dst + 1024 * d);
+      } else {
+        // ragged tail: rows past the last token repeat it (their p is 0)
+#pragma unroll
+        for (int d = 0; d < T16_LOADS; ++d) {
+          const int row = 8 * (d & 1) + (lane >> 3), rr = min(row, nv - 1);
+          const uint32_t off = (uint32_t)(rr * (RW * 2) + 16 * ((lane & 7) ^ s16sw(row)));
+          dma16<0>(src + 128 * (d >> 1), off, dst + 1024 * d);
+        }
+      }
+    };
+
+    // query fragments (B operand of S^T = K Q^T): head hl, features
+    // 32 ks + 8 q4 .. +7; heads past H read head 0 (their results are not stored)
+    u32x4 qf[RW / 32];
+    {
+      const char* qb = (const char*)a.q_abs + (size_t)b * a.H * (RW * 2);
+      uint32_t qo = (uint32_t)((hvalid ? hl : 0) * (RW * 2) + 16 * q4);
+      asm volatile("" : "+v"(qo));
+#pragma unroll
+      for (int ks = 0; ks < RW / 32; ++ks) qf[ks] = *(const u32x4*)(qb + qo + 64 * ks);
+    }
+    if (nmine > 0) issue(w, 0);
+    if (nmine > 1) issue(w + 4, 1);
+
+    f32x4 acc[DC / 16];
+#pragma unroll
+    for (int i = 0; i < DC / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, lsum = 0.f;
+    for (int i = 0; i < nmine; ++i) {
+      const int j = w + 4 * i;
+      if (i + 1 < nmine) __builtin_amdgcn_s_waitcnt(waitcnt_vm(T16_LOADS));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      asm volatile("" ::: "memory");
+      const char* st = wst + (i & 1) * T16_BYTES;
+      // scores, K fragments three steps ahead
+      constexpr int PF = 3;
+      auto kfrag = [&](int ks) {
+        return *(const u32x4*)(st + 2048 * (ks >> 1) + sc_row + 16 * ((4 * (ks & 1) + q4) ^ s16sw(hl)));
+      };
+      u32x4 kf[PF];
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) kf[ks] = kfrag(ks);
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < RW / 32; ++ks) {
+        const u32x4 cur = kf[ks % PF];
+        if (ks + PF < RW / 32) kf[ks % PF] = kfrag(ks + PF);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur), as_bf16x8(qf[ks]), sc, 0, 0, 0);
+      }
+      // sc[e]: token t0 + 16 j + 4 q4 + e against head hl
+      const int tok = t0 + T16 * j + 4 * q4;
+      if (i == 0) {
+        // this wave's reference maximum: the largest score of its first tile
+        float mt = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (tok + e < t1) mt = fmaxf(mt, sc[e]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        m_ref = mt * sl2;
+      }
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], sl2, -m_ref));
+        if (tok + e >= t1) pv[e] = 0.f;
+      }
+      const uint32_t p01 = pack_bf16x2(pv[0], pv[1]), p23 = pack_bf16x2(pv[2], pv[3]);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p01), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                             lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p23), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                             lsum, false);
+      const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+      // latent: O^T[16 fb + ..][hl] += C^T[features][4 q4 ..] P^T, transpose
+      // reads two blocks ahead
+      auto cfrag = [&](int fb) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + 2048 * (fb >> 2) + tr_off[fb & 3]));
+      };
+      s16x4 cf[2];
+      cf[0] = cfrag(0);
+      cf[1] = cfrag(1);
+#pragma unroll
+      for (int fb = 0; fb < DC / 16; ++fb) {
+        const s16x4 cur = cf[fb & 1];
+        if (fb + 2 < DC / 16) cf[fb & 1] = cfrag(fb + 2);
+        acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur, pb, acc[fb], 0, 0, 0);
+      }
+      // the stage is read: tile i + 2 goes into it
+      if (i + 2 < nmine) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this stage's reads have returned
+        issue(j + 8, i & 1);
+      }
+    }
+
+    // merge the four waves: m* = max m_w, L = sum 2^(m_w - m*) l_w,
+    // acc = sum 2^(m_w - m*) acc_w.  A wave without tiles has m_w = -inf.
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    // a score more than kHeadroom (log2) above a wave's reference makes its
+    // sum at least 2^kHeadroom (or inf / NaN): the partial is flagged and the
+    // combine recomputes it exactly
+    const float ovf = (nmine > 0 && !(lsum < 0x1p100f)) ? 1.f : 0.f;
+    float* s_acc = (float*)smem;                         // [4 waves][16 heads][512]
+    float* s_ml = (float*)(smem + 4 * 16 * DC * 4);      // [4 waves][16 heads][2]
+    __syncthreads();  // every wave is done with its stages
+    if (q4 == 0) {
+      s_ml[(w * 16 + hl) * 2 + 0] = nmine > 0 ? m_ref : -INFINITY;
+      s_ml[(w * 16 + hl) * 2 + 1] = ovf > 0.f ? INFINITY : lsum;
+    }
+    __syncthreads();
+    float mstar = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) mstar = fmaxf(mstar, s_ml[(v * 16 + hl) * 2]);
+    const float sw = nmine > 0 ? __builtin_amdgcn_exp2f(m_ref - mstar) : 0.f;
+    // acc[fb]: features 16 fb + 4 q4 + e of head hl
+#pragma unroll
+    for (int fb = 0; fb < DC / 16; ++fb)
+      *(f32x4*)(s_acc + (w * 16 + hl) * DC + 16 * fb + 4 * q4) = acc[fb] * sw;
+    __syncthreads();
+    // sum the four copies in wave order: thread t takes head t / 16 and
+    // features 4 (t % 16) + 64 k, k < 8
+    {
+      const int h = threadIdx.x >> 4, c4 = threadIdx.x & 15;
+      if (h < a.H) {
+        float* pa = a.part_acc + ((size_t)item * a.H + h) * DC;
+#pragma unroll
+        for (int k = 0; k < DC / 64; ++k) {
+          const int f = 4 * c4 + 64 * k;
+          f32x4 v = *(const f32x4*)(s_acc + h * DC + f);
+#pragma unroll
+          for (int u = 1; u < 4; ++u) v += *(const f32x4*)(s_acc + (u * 16 + h) * DC + f);
+          *(f32x4*)(pa + f) = v;
+        }
+        if (c4 == 0) {
+          float ms = -INFINITY, L = 0.f;
+          bool flag = false;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ms = fmaxf(ms, s_ml[(u * 16 + h) * 2]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float mu = s_ml[(u * 16 + h) * 2], lu = s_ml[(u * 16 + h) * 2 + 1];
+            if (mu == -INFINITY) continue;
+            if (!(lu < INFINITY)) flag = true;
+            L += __builtin_amdgcn_exp2f(mu - ms) * lu;
+          }
+          a.part_ml[((size_t)item * a.H + h) * 2 + 0] = flag ? INFINITY : ms;
+          a.part_ml[((size_t)item * a.H + h) * 2 + 1] = L;
+        }
+      }
+    }
+    // the next round's loads reuse the stages and the merge buffers
+    __syncthreads();
+  }
+}
+
+// ============================================================================
 // 8-bit cache (MLA_FLAG_FP8_CACHE: E4M3 codes, one float32 power-of-two scale
 // per row).  Same plan, item loop, ring of four stages and step order as
 // k_split; what changes is the tile and how its operands are read:
@@ -1305,7 +1569,10 @@ hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s) {
     }
   } else {
     switch (split_waves(a.H)) {
-      case 1: hipLaunchKernelGGL((k_split<4, true>), g1, dim3(256), 0, s, a); break;
+      case 1:
+        if (a.H <= 16) hipLaunchKernelGGL(k_split16, g1, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_split<4, true>), g1, dim3(256), 0, s, a);
+        break;
       case 2: hipLaunchKernelGGL(k_split<2>, g1, dim3(128), 0, s, a); break;
       default: hipLaunchKernelGGL(k_split<4>, g1, dim3(256), 0, s, a); break;
     }

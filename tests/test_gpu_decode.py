@@ -163,10 +163,12 @@ def test_decode_v2lite(flags):
 
 @pytest.mark.parametrize("lens", [[1, 2, 31, 32, 33, 63, 64, 65], [0, 257, 300, 1000, 5, 4097, 128, 96]],
                          ids=["short", "mixed_with_empty"])
-@pytest.mark.parametrize("heads", [128, 16, 40])
+@pytest.mark.parametrize("heads", [128, 16, 40, 24, 8, 1])
 def test_decode_ragged_edges(lens, heads):
-    """Lengths around tile (32) and page (64) boundaries, an empty sequence,
-    head counts that fill 4, 1 and 2 waves; random page permutation."""
+    """Lengths around tile (32 and 16) and page (64) boundaries, an empty
+    sequence, head counts for each split kernel (4, 2 and 1 head blocks of 32,
+    and the 16-wide few-heads kernel at 16, 8 and 1 heads, whose padding heads
+    are not stored); random page permutation."""
     need_gpu()
     _case(f"decode ragged edges lens={lens} H={heads}")
     cfg = I.scaled(I.RAGGED, hidden=512, num_heads=heads, batch=len(lens), seq_len=max(lens), min_seq_len=1)
@@ -283,9 +285,10 @@ def test_decode_ragged_paged_full_size():
     _check(cfg, inp, st, seqs)
 
 
+@pytest.mark.parametrize("heads", [128, 16])
 @pytest.mark.parametrize("flags,amp", [(0, 40.0), (mla.FLAG_GENERIC, 40.0), (0, 13.0), (0, 17.0)],
                          ids=["mfma_huge", "generic_huge", "mfma_below_bound", "mfma_above_bound"])
-def test_decode_score_spike_far_above_first_tile(flags, amp):
+def test_decode_score_spike_far_above_first_tile(flags, amp, heads):
     """One row of sequence 1 aligned with head 0's absorbed query and scaled so
     its score exceeds the rest of its work item by about 7 amp in log2 units:
     amp 40 (~277) overflows the numerators and the MFMA split pass must hand
@@ -294,8 +297,8 @@ def test_decode_score_spike_far_above_first_tile(flags, amp):
     (~118) crosses it and is flagged through the numerator sum.  The output
     for head 0 is then W_UV,0 c_spike in every case."""
     need_gpu()
-    _case(f"score spike flags={flags} amp={amp}")
-    cfg = I.scaled(I.RAGGED, hidden=512, batch=3, seq_len=2100, min_seq_len=1)
+    _case(f"score spike flags={flags} amp={amp} H={heads}")
+    cfg = I.scaled(I.RAGGED, hidden=512, num_heads=heads, batch=3, seq_len=2100, min_seq_len=1)
     inp = I.make(cfg, 21, lengths=[700, 2100, 64])
     q = O.from_storage(inp["q"], "bf16")
     qa = O.absorb_query(q, O.from_storage(inp["w_uk"], "bf16"), inp["q_positions"], cfg.qk_nope, cfg.rope_base)
