@@ -171,7 +171,7 @@ int decode_launch(const mla_dims_t* dims, const void* q_abs, const void* pool, i
   a.len_cap = max_seq_len;
   a.slots = L.slots;
   a.max_items = L.max_items;
-  a.min_chunk = 256;
+  a.min_chunk = decode_fast(dims, batch) ? 256 : 32;  // the plain kernels work a token at a time per lane
   // partial (m, l, acc) written and read back, in cache-row equivalents
   a.ovh_tokens = (int)((2.0 * dims->num_heads * (dims->d_c + 2) * 4.0) /
                        ((double)(dims->d_c + dims->d_r) * cache_elem_bytes(dims)));
