@@ -124,3 +124,29 @@ def test_write_absorb_empty_parts():
     mla.write_absorb(b.d, b.h, b.w_dkr, b.positions, b.slots, b.pool, None, b.w_uk, b.q_positions, b.q_abs, b.wa_ws)
     torch.cuda.synchronize()
     assert np.array_equal(harness.to_host_bits(a.pool), harness.to_host_bits(b.pool))
+
+
+def test_write_absorb_different_row_and_query_counts():
+    """The cache write and the absorption take their own token counts: 5 rows
+    written, 3 queries absorbed (and the reverse), on the one-launch path."""
+    need_gpu()
+    print("[case] write_absorb 5 rows / 3 queries", flush=True)
+    cfg = I.scaled(I.V3, hidden=1024, batch=5, seq_len=80, paged=True)
+    inp = I.make(cfg, 9)
+    for nw, nq in ((5, 3), (2, 5)):
+        a = harness.DecodeStep(cfg, inp)
+        b = harness.DecodeStep(cfg, inp)
+        mla.write_cache(a.d, a.h[:nw], a.w_dkr, a.positions[:nw], a.slots[:nw], a.pool)
+        mla.absorb_q(a.d, a.q[:nq], a.w_uk, a.q_positions[:nq], a.q_abs[:nq])
+        mla.write_absorb(b.d, b.h[:nw], b.w_dkr, b.positions[:nw], b.slots[:nw], b.pool, b.q[:nq], b.w_uk,
+                         b.q_positions[:nq], b.q_abs[:nq], b.wa_ws)
+        torch.cuda.synchronize()
+        # rows past nq were never written (torch.empty)
+        assert np.array_equal(harness.to_host_bits(a.q_abs)[:nq], harness.to_host_bits(b.q_abs)[:nq])
+        pa, pb = harness.to_host_bits(a.pool), harness.to_host_bits(b.pool)
+        R = cfg.row_width
+        dist = _bf16_ulp_distance(pa.reshape(-1, R), pb.reshape(-1, R))
+        assert dist.max() <= 1
+        untouched = np.ones(pa.reshape(-1, R).shape[0], dtype=bool)
+        untouched[inp["slots"][:nw]] = False
+        assert np.array_equal(pa.reshape(-1, R)[untouched], pb.reshape(-1, R)[untouched])
