@@ -1312,7 +1312,8 @@ __device__ __noinline__ void recompute_partial(const void* __restrict__ pool, co
                                                const uint16_t* __restrict__ qa, float* __restrict__ pa,
                                                float* __restrict__ pml, int P, float scale_log2, int t0, int t1,
                                                float* scratch, int* red, int f8, int num_pages, int* err) {
-  // blockDim.x in {256, 512}: thread tid keeps latent columns tid (+ blockDim.x)
+  // blockDim.x in {256, 512, 1024}: thread tid keeps latent columns tid and
+  // tid + blockDim.x, those below d_c
   const int nth = blockDim.x;
   float* q = scratch;          // 576
   float* p = scratch + RW;     // blockDim.x
@@ -1350,11 +1351,11 @@ __device__ __noinline__ void recompute_partial(const void* __restrict__ pool, co
       const int tt = tb + k;
       const float pk = p[k];
       l += pk;  // every thread keeps the full sum
-      acc0 += pk * val(tt, c0);
+      if (c0 < DC) acc0 += pk * val(tt, c0);
       if (c1 < DC) acc1 += pk * val(tt, c1);
     }
   }
-  pa[c0] = acc0;
+  if (c0 < DC) pa[c0] = acc0;
   if (c1 < DC) pa[c1] = acc1;
   if (tid == 0) {
     pml[0] = m;
@@ -1533,6 +1534,249 @@ __global__ void __launch_bounds__(64 * CNW, 4) k_combine(DecodeArgs a) {
   }
 }
 
+
+// --------------------------------------------------------------------------
+// combine, wide form for d_v = 128: grid (H, ceil(batch / 32)), 1024 threads
+// (16 waves), one work-group per CU.  Work-group (h, sequences b0 .. b0+31):
+//   - W_UV,h (128 rows x 1 KiB) goes to LDS by direct loads, 8 rows a wave;
+//     row r keeps its 16-byte chunk c in slot c ^ (r % 32).
+//   - Wave w owns latent columns 32 w .. 32 w + 31, one 32-wide k-step of the
+//     16x16x32 product.  Its lane (r, q) = (lane % 16, lane / 16) merges
+//     columns 32 w + 4 q .. +3 and 32 w + 16 + 4 q .. +3 of sequences r and
+//     16 + r over the items in index order (groups of four items, requested
+//     together; a later group rescales the earlier ones).  Those eight
+//     columns are its A fragment of each 16-sequence block: the k order
+//     inside the step is permuted (the B fragments follow it), so that the
+//     four lanes of a sequence read 64 contiguous bytes of a partial in one
+//     instruction.  Every partial of the work-group is requested before the
+//     first wait; the items' (m, L) pairs come through LDS.
+//   - D_w[s][v] = sum over the wave's 32 columns k of lat[s][k] W_UV[h][v][k],
+//     lat as bf16 hi + lo (the pair carries the fp32 value to ~2^-17): two
+//     16-sequence blocks x eight 16-wide v blocks, 32 MFMAs a wave.
+//   - The 16 partial products meet in LDS (over the W_UV buffer), half of v
+//     at a time, and each output pair is the sum over w = 0 .. 15 in order.
+constexpr int WCB = 32;       // sequences per wide combine work-group
+constexpr int WNI = 4;        // items requested per sequence and group
+constexpr int WRED_LD = 68;   // floats per reduction row (64 + 4: the four row groups of a D fragment hit other banks)
+constexpr int WLDS = 16 * WCB * WRED_LD * 4;  // 139264 bytes: reduction rows; W_UV,h in the first 128 KiB
+static_assert(128 * DC * 2 <= WLDS, "W_UV,h fits under the reduction rows");
+constexpr int WSCR = RW + 1024;  // floats of scratch for recompute_partial
+// buffer resource word 3 for raw 32-bit accesses
+constexpr int kRawBufferWord3 = 0x00020000;
+__global__ void __launch_bounds__(1024) k_combine_wide(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[WLDS];
+  __shared__ __attribute__((aligned(16))) float scr[WSCR];
+  __shared__ __attribute__((aligned(16))) f32x2 s_ml[WNI][WCB];  // (m, L) of item j0 + jj of each sequence
+  __shared__ int red[16];
+
+  const int h = blockIdx.x, b0 = blockIdx.y * WCB;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r16 = lane & 15;
+  const int nb = min(WCB, a.batch - b0);
+  const float* __restrict__ pml = a.part_ml;
+
+  // items it0[sb] .. it1[sb] - 1 of this lane's sequences b0 + 16 sb + r16 (none past the batch)
+  int it0[2], it1[2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    it0[sb] = a.plan[b0 + min(16 * sb + r16, nb)];
+    it1[sb] = a.plan[b0 + min(16 * sb + r16 + 1, nb)];
+  }
+  // threads 0 .. 127 fetch the (m, L) pairs: sequence tid / 4, item j0 + tid % 4
+  const int mseq = min(tid >> 2, nb);
+  int mit0 = a.plan[b0 + mseq], mit1 = a.plan[b0 + min(mseq + 1, nb)];
+  // the plan arrives before the direct loads are issued
+  asm volatile("" ::"v"(it0[0]), "v"(it1[0]), "v"(it0[1]), "v"(it1[1]), "v"(mit0), "v"(mit1));
+  int nmax = max(it1[0] - it0[0], it1[1] - it0[1]);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o));
+  nmax = __builtin_amdgcn_readfirstlane(nmax);
+
+  // W_UV,h rows 8 w .. 8 w + 7 to LDS: lane l fills slot l of row r from chunk l ^ (r % 32)
+  {
+    const char* wbase = (const char*)a.w_uv + (size_t)h * 128 * DC * 2;
+    const uint32_t lds0 = lds_addr_of(smem);
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int r = 8 * w + rr;
+      dma16_v(wbase + (size_t)r * DC * 2 + ((lane ^ (r & 31)) << 4), lds0 + r * DC * 2);
+    }
+  }
+
+  // The partials through buffer resources (32-bit offsets; the host takes this
+  // kernel only when both buffers are below 2 GiB): an absent item's loads
+  // get an offset past the end and return zeros.
+  const __amdgpu_buffer_rsrc_t acc_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.part_acc, (short)0, (int)((size_t)a.max_items * a.H * DC * sizeof(float)), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t ml_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)pml, (short)0, (int)((size_t)a.max_items * a.H * 2 * sizeof(float)), kRawBufferWord3);
+  // merge items it0 + j0 .. +3 (those below it1) of both sequences into the
+  // running (v, m, L):
+  //   m = max(m, m_i);  v = v 2^(m_old - m) + sum_i 2^(m_i - m) acc_i;  L likewise.
+  // FIRST: nothing merged yet (v and L are written, not read).
+  auto merge_group = [&](auto first, int j0, f32x4(&v)[2][2], float(&m)[2], float(&l)[2], int& flagged) {
+    constexpr bool FIRST = decltype(first)::value;
+    f32x4 ai[2][WNI][2];
+#pragma unroll
+    for (int jj = 0; jj < WNI; ++jj)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int i = it0[sb] + j0 + jj;
+        const int off_acc = i < it1[sb] ? 4 * (DC * (i * a.H + h) + 32 * w + 4 * q) : (int)0x80000000;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          ai[sb][jj][u] =
+              __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(acc_rs, off_acc + 64 * u, 0, 0));
+      }
+    // (m, L) after the partials: its wait then covers every load of the group
+    if (tid < WNI * WCB) {
+      const int i = mit0 + j0 + (tid & 3);
+      const bool ok = i < mit1;
+      const f32x2 ml = __builtin_bit_cast(
+          f32x2, __builtin_amdgcn_raw_buffer_load_b64(ml_rs, ok ? 8 * (i * a.H + h) : (int)0x80000000, 0, 0));
+      s_ml[tid & 3][tid >> 2] = f32x2{ok ? ml[0] : -INFINITY, ml[1]};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      float mi[WNI], li[WNI];
+#pragma unroll
+      for (int jj = 0; jj < WNI; ++jj) {
+        const f32x2 ml = s_ml[jj][16 * sb + r16];
+        mi[jj] = ml[0];
+        li[jj] = ml[1];
+      }
+      float mn = FIRST ? -INFINITY : m[sb];
+#pragma unroll
+      for (int jj = 0; jj < WNI; ++jj) {
+        flagged |= mi[jj] == INFINITY;
+        mn = fmaxf(mn, mi[jj]);
+      }
+      // weights 2^(m_i - mn): 0 for absent items; all 0 while nothing is merged
+      const bool any = mn != -INFINITY;
+      float wgt[WNI];
+#pragma unroll
+      for (int jj = 0; jj < WNI; ++jj) wgt[jj] = any ? exp2f(mi[jj] - mn) : 0.f;
+      if constexpr (FIRST) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) v[sb][u] = wgt[0] * ai[sb][0][u];
+        l[sb] = wgt[0] * li[0];
+      } else {
+        const float sc = any ? exp2f(m[sb] - mn) : 0.f;  // 0 while m = -inf
+#pragma unroll
+        for (int u = 0; u < 2; ++u) v[sb][u] = sc * v[sb][u] + wgt[0] * ai[sb][0][u];
+        l[sb] = sc * l[sb] + wgt[0] * li[0];
+      }
+#pragma unroll
+      for (int jj = 1; jj < WNI; ++jj) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) v[sb][u] += wgt[jj] * ai[sb][jj][u];
+        l[sb] += wgt[jj] * li[jj];
+      }
+      m[sb] = mn;
+    }
+    __syncthreads();  // s_ml is read: the next group may overwrite it
+  };
+  auto merge_all = [&](f32x4(&v)[2][2], float(&m)[2], float(&l)[2]) {
+    int flagged = 0;
+    merge_group(std::true_type{}, 0, v, m, l, flagged);
+    for (int j0 = WNI; j0 < nmax; j0 += WNI)  // more than four items: later groups in order
+      merge_group(std::false_type{}, j0, v, m, l, flagged);
+    return flagged;
+  };
+
+  f32x4 v[2][2];
+  float mrun[2], lrun[2];
+  if (__syncthreads_or(merge_all(v, mrun, lrun))) {
+    // a flagged partial (m = +inf): recompute it exactly, then merge again
+    const int chunk = a.plan[2 * a.batch + 1];
+    for (int b = 0; b < nb; ++b) {
+      const int i0 = a.plan[b0 + b], i1 = a.plan[b0 + b + 1];
+      const int len = a.plan[a.batch + 1 + b0 + b];
+      for (int i = i0; i < i1; ++i) {
+        const size_t ih = (size_t)i * a.H + h;
+        if (pml[ih * 2] != INFINITY) continue;  // same value in every thread
+        const int t0 = (i - i0) * chunk;
+        const int t1 = min(len, t0 + chunk);
+        recompute_partial(a.pool, a.block_table + (size_t)(b0 + b) * a.max_pages_per_seq,
+                          (const uint16_t*)a.q_abs + ((size_t)(b0 + b) * a.H + h) * RW, a.part_acc + ih * DC,
+                          a.part_ml + ih * 2, a.P, a.scale_log2, t0, t1, scr, red, a.fp8, a.num_pages, a.err);
+      }
+    }
+    __syncthreads();
+    // (the load offsets are formed again here rather than kept from the first merge)
+    asm volatile("" : "+v"(it0[0]), "+v"(it1[0]), "+v"(it0[1]), "+v"(it1[1]), "+v"(mit0), "+v"(mit1));
+    merge_all(v, mrun, lrun);  // recomputed partials are finite
+  }
+
+  // lat = v / L as bf16 hi + lo: the A fragments (row = sequence r16 of block
+  // sb; its eight k slots hold columns 32 w + 4 q .. +3, 32 w + 16 + 4 q .. +3)
+  u32x4 ahi[2], alo[2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const float il = lrun[sb] > 0.f ? 1.f / lrun[sb] : 0.f;
+    const int seq = 16 * sb + r16;
+    if (w == 0 && q == 0 && seq < nb && a.lse)
+      a.lse[(size_t)(b0 + seq) * a.H + h] = lrun[sb] > 0.f ? (mrun[sb] + log2f(lrun[sb])) * kLn2 : -INFINITY;
+    const f32x4 x0 = v[sb][0] * il, x1 = v[sb][1] * il;
+    const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t hp = pack_bf16x2(x[e], x[e + 1]);
+      hw[e >> 1] = hp;
+      lw[e >> 1] = pack_bf16x2(x[e] - __uint_as_float(hp << 16), x[e + 1] - __uint_as_float(hp & 0xffff0000u));
+    }
+    ahi[sb] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+    alo[sb] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's W_UV rows have landed
+  __syncthreads();                            // and every other wave's
+
+  // D_w: B = W_UV^T fragment (column v = 16 vb + lane % 16, the same eight
+  // columns as the A slots): 8 bytes from chunk 4 w + q / 2 and 8 from chunk
+  // 4 w + 2 + q / 2 of row 16 vb + lane % 16, half q % 2 of each
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int vb = 0; vb < 8; ++vb) {
+    const int row = 16 * vb + r16;
+    const char* rp = smem + row * DC * 2 + 8 * (q & 1);
+    const uint2 b0w = *(const uint2*)(rp + (((4 * w + (q >> 1)) ^ (row & 31)) << 4));
+    const uint2 b1w = *(const uint2*)(rp + (((4 * w + 2 + (q >> 1)) ^ (row & 31)) << 4));
+    const u32x4 bw = u32x4{b0w.x, b0w.y, b1w.x, b1w.y};
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      acc[sb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi[sb]), as_bf16x8(bw),
+                                                            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      acc[sb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(alo[sb]), as_bf16x8(bw), acc[sb][vb], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // W_UV reads done: the buffer takes the partial products
+
+  // D rows: sequence 16 sb + 4 q + j, column v = 16 vb + lane % 16
+  float* qs = (float*)smem;  // [w][seq][WRED_LD], v of the current half
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int vl = 0; vl < 4; ++vl)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qs[(w * WCB + 16 * sb + 4 * q + j) * WRED_LD + 16 * vl + r16] = acc[sb][4 * half + vl][j];
+    __syncthreads();
+    {
+      const int seq = tid >> 5, v2 = 2 * (tid & 31);
+      f32x2 o = *(const f32x2*)(qs + seq * WRED_LD + v2);
+#pragma unroll
+      for (int k = 1; k < 16; ++k) o += *(const f32x2*)(qs + (k * WCB + seq) * WRED_LD + v2);
+      if (seq < nb)
+        *(uint32_t*)((uint16_t*)a.out + ((size_t)(b0 + seq) * a.H + h) * 128 + 64 * half + v2) = pack_bf16x2(o[0], o[1]);
+    }
+    if (half == 0) __syncthreads();
+  }
+}
+
 }  // namespace
 
 bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch) {
@@ -1579,7 +1823,10 @@ hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((long long)a.H * ((a.batch + 15) / 16) >= 2LL * a.slots)
+  if (a.d_v == 128 && (long long)a.H * ((a.batch + WCB - 1) / WCB) >= a.slots &&
+      (long long)a.max_items * a.H * DC * (long long)sizeof(float) < (1LL << 31))
+    hipLaunchKernelGGL(k_combine_wide, dim3(a.H, (a.batch + WCB - 1) / WCB), dim3(1024), 0, s, a);
+  else if ((long long)a.H * ((a.batch + 15) / 16) >= 2LL * a.slots)
     hipLaunchKernelGGL((k_combine<16, 2>), dim3(a.H, (a.batch + 15) / 16), dim3(64 * CNW), 0, s, a);
   else
     hipLaunchKernelGGL((k_combine<4, 8>), dim3(a.H, (a.batch + 3) / 4), dim3(64 * CNW), 0, s, a);

@@ -209,6 +209,34 @@ def test_decode_max_batch(heads):
     assert np.all(np.isneginf(lse[z]))
 
 
+def test_decode_wide_combine_many_items():
+    """H = 128 with more than 32 sequences takes the combine form with 32
+    sequences per work-group: one long sequence split into dozens of items
+    (merged four at a time, the later groups rescaling the earlier ones),
+    empty and one-token sequences, lengths around tile and page boundaries, and
+    a ragged last block of 8 sequences (40 in all)."""
+    need_gpu()
+    _case("decode wide combine, many items")
+    lens = [5000, 0, 1, 31, 32, 33, 64, 65, 2047, 0] + list(np.random.default_rng(31).integers(0, 300, size=30))
+    cfg = I.scaled(I.RAGGED, hidden=512, num_heads=128, batch=len(lens), seq_len=max(lens), min_seq_len=1)
+    inp = I.make(cfg, 32, lengths=lens)
+    st = _run_step(cfg, inp)
+    assert mla.uses_fast_path(st.d, mla.OP_DECODE) == 1
+    lens = np.array(lens, dtype=np.int32)
+    nz = [b for b in range(len(lens)) if lens[b] > 0]
+    _check(cfg, inp, st, nz[:8] + nz[-4:])
+    out = harness.to_host_bits(st.out)
+    for b in np.flatnonzero(lens == 0):
+        assert np.all(out[b].astype(np.uint16) == 0)
+        assert np.all(np.isneginf(st.lse.cpu().numpy()[b]))
+    # the same bits on a second run
+    o1, l1 = out.copy(), st.lse.cpu().numpy().copy()
+    st.attend()
+    torch.cuda.synchronize()
+    assert np.array_equal(harness.to_host_bits(st.out), o1)
+    assert np.array_equal(st.lse.cpu().numpy(), l1)
+
+
 @pytest.mark.parametrize("flags", [0, mla.FLAG_GENERIC], ids=["mfma", "generic"])
 def test_page_permutation_bit_invariance_and_determinism(flags):
     need_gpu()
@@ -310,3 +338,25 @@ def test_decode_score_spike_far_above_first_tile(flags, amp, heads):
     inp["rows"] = rows
     st = _run_step(cfg, inp, flags)
     _check(cfg, inp, st, [0, 1, 2], spike=True)
+
+
+@pytest.mark.parametrize("amp", [40.0, 17.0], ids=["huge", "above_bound"])
+def test_decode_score_spike_wide_combine(amp):
+    """The spike case of the test above with 40 sequences at H = 128, so that
+    the combine with 32 sequences per work-group recomputes the flagged
+    (item, head) and merges the long sequence's many items again."""
+    need_gpu()
+    _case(f"score spike wide combine amp={amp}")
+    lens = [700, 2100, 64] + [64 + 3 * k for k in range(37)]
+    cfg = I.scaled(I.RAGGED, hidden=512, num_heads=128, batch=len(lens), seq_len=2100, min_seq_len=1)
+    inp = I.make(cfg, 21, lengths=lens)
+    q = O.from_storage(inp["q"], "bf16")
+    qa = O.absorb_query(q, O.from_storage(inp["w_uk"], "bf16"), inp["q_positions"], cfg.qk_nope, cfg.rope_base)
+    spike = np.where(qa[1, 0] >= 0, amp, -amp).astype(np.float32)
+    t_spike = 1000
+    P = cfg.page_size
+    rows = inp["rows"].copy()
+    rows[inp["block_table"][1, t_spike // P], t_spike % P] = I.f32_to_bf16_bits(spike)
+    inp["rows"] = rows
+    st = _run_step(cfg, inp)
+    _check(cfg, inp, st, [0, 1, 2, 39], spike=True)
