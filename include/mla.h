@@ -240,6 +240,9 @@ size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t 
  * 2^100 (larger ones are detected and the affected partial is recomputed
  * exactly), so cached values must stay below 2^28 in magnitude for the fp32
  * latent sums to stay finite.
+ * Precision: on the fast path each split's latent sums (fp32 inside the
+ * split) are stored as bf16 (round to nearest even) between the two passes;
+ * the merge itself, the (max, sum) pairs and the W_UV product stay fp32.
  */
 int mla_decode(const mla_dims_t* dims, const void* q_abs, const void* pool, int32_t num_pages,
                const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,

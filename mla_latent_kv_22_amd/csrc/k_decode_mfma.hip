@@ -13,10 +13,13 @@
 // rescales the accumulator (the merge stays exact: every partial carries its
 // own reference); a score more than 2^100 above the reference could overflow,
 // so such an (item, head) -- detected from its sum of numerators -- is
-// flagged and recomputed exactly by the combine.
-// Pass 2 (combine): per (head, 16 sequences): LSE-merge of the items in a
-// fixed order, the merged latent split into bf16 hi + lo parts, and W_UV
-// applied with MFMA (so the fp32 latent reaches the product intact to ~2^-17).
+// flagged and recomputed exactly by the combine.  A partial leaves as its
+// (m, l) pair in fp32 and its 512 latent sums rounded to bf16 (same exponent
+// range as fp32, relative rounding 2^-9; half the bytes of fp32 sums).
+// Pass 2 (combine): per (head, 16 or 32 sequences): LSE-merge of the items in
+// a fixed order in fp32, the merged latent split into bf16 hi + lo parts, and
+// W_UV applied with MFMA (the fp32 merged latent reaches the product intact
+// to ~2^-17).
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -567,11 +570,12 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
       for (int hb = 0; hb < S::HB; ++hb) {
         const int h = 32 * hb + hl;
         if (h >= a.H) continue;
-        float* pa = a.part_acc + ((size_t)item * a.H + h) * DC + 32 * (S::FBW * w + fbl) + 4 * g;
+        uint16_t* pa = a.part_lat + ((size_t)item * a.H + h) * DC + 32 * (S::FBW * w + fbl) + 4 * g;
         const f32x16& v = acc[fbl * S::HB + hb];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *(f32x4*)(pa + 8 * q4) = f32x4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+          *(uint2*)(pa + 8 * q4) =
+              make_uint2(pack_bf16x2(v[4 * q4], v[4 * q4 + 1]), pack_bf16x2(v[4 * q4 + 2], v[4 * q4 + 3]));
       }
     // the next round's query loads and tiles reuse LDS and registers
     __syncthreads();
@@ -811,14 +815,14 @@ __global__ void __launch_bounds__(256, 1) k_split16(DecodeArgs a) {
     {
       const int h = threadIdx.x >> 4, c4 = threadIdx.x & 15;
       if (h < a.H) {
-        float* pa = a.part_acc + ((size_t)item * a.H + h) * DC;
+        uint16_t* pa = a.part_lat + ((size_t)item * a.H + h) * DC;
 #pragma unroll
         for (int k = 0; k < DC / 64; ++k) {
           const int f = 4 * c4 + 64 * k;
           f32x4 v = *(const f32x4*)(s_acc + h * DC + f);
 #pragma unroll
           for (int u = 1; u < 4; ++u) v += *(const f32x4*)(s_acc + (u * 16 + h) * DC + f);
-          *(f32x4*)(pa + f) = v;
+          *(uint2*)(pa + f) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
         if (c4 == 0) {
           float ms = -INFINITY, L = 0.f;
@@ -1292,24 +1296,26 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
       for (int hb = 0; hb < S::HB; ++hb) {
         const int h = 32 * hb + hl;
         if (h >= a.H) continue;
-        float* pa = a.part_acc + ((size_t)item * a.H + h) * DC + 32 * (S::FBW * w + fbl) + 4 * g;
+        uint16_t* pa = a.part_lat + ((size_t)item * a.H + h) * DC + 32 * (S::FBW * w + fbl) + 4 * g;
         const f32x16& v = acc[fbl * S::HB + hb];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *(f32x4*)(pa + 8 * q4) = f32x4{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+          *(uint2*)(pa + 8 * q4) =
+              make_uint2(pack_bf16x2(v[4 * q4], v[4 * q4 + 1]), pack_bf16x2(v[4 * q4 + 2], v[4 * q4 + 3]));
       }
     __syncthreads();
   }
 }
 
 // --------------------------------------------------------------------------
-// Exact two-pass partial (m, l, acc) of one (item, head) in fp32, used only for
-// partials the split pass flagged.  scratch: >= 576 + 256 floats of LDS.
+// Exact two-pass partial (m, l, acc) of one (item, head) in fp32, stored as
+// the split pass stores it (latent sums as bf16), used only for partials the
+// split pass flagged.  scratch: >= 576 + 256 floats of LDS.
 // The arguments are plain values (no pointer to the kernel's argument block,
 // which would force that block into scratch memory in the caller).
 // f8: the pool is 8-bit (row values E4M3(code) * row scale).
 __device__ __noinline__ void recompute_partial(const void* __restrict__ pool, const int32_t* __restrict__ bt,
-                                               const uint16_t* __restrict__ qa, float* __restrict__ pa,
+                                               const uint16_t* __restrict__ qa, uint16_t* __restrict__ pa,
                                                float* __restrict__ pml, int P, float scale_log2, int t0, int t1,
                                                float* scratch, int* red, int f8, int num_pages, int* err) {
   // blockDim.x in {256, 512, 1024}: thread tid keeps latent columns tid and
@@ -1355,8 +1361,8 @@ __device__ __noinline__ void recompute_partial(const void* __restrict__ pool, co
       if (c1 < DC) acc1 += pk * val(tt, c1);
     }
   }
-  if (c0 < DC) pa[c0] = acc0;
-  if (c1 < DC) pa[c1] = acc1;
+  if (c0 < DC) pa[c0] = f32_to_bf16(acc0);
+  if (c1 < DC) pa[c1] = f32_to_bf16(acc1);
   if (tid == 0) {
     pml[0] = m;
     pml[1] = l;
@@ -1387,7 +1393,7 @@ __global__ void __launch_bounds__(64 * CNW, 4) k_combine(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nb = min(CB, a.batch - b0);
   const float* __restrict__ pml = a.part_ml;
-  const float* __restrict__ pacc = a.part_acc;
+  const uint16_t* __restrict__ plat = a.part_lat;
 
   // the plan the split pass published
   if (tid <= nb) s_items[tid] = a.plan[b0 + tid];
@@ -1431,7 +1437,9 @@ __global__ void __launch_bounds__(64 * CNW, 4) k_combine(DecodeArgs a) {
           const float2 ml = ok ? *(const float2*)(pml + 2 * ih) : make_float2(-INFINITY, 0.f);
           mi[k][jj] = ml.x;
           li[k][jj] = ml.y;
-          ai[k][jj] = ok ? *(const f32x4*)(pacc + DC * ih + 4 * cq) : f32x4{0.f, 0.f, 0.f, 0.f};
+          const uint2 pb = ok ? *(const uint2*)(plat + DC * ih + 4 * cq) : make_uint2(0u, 0u);
+          ai[k][jj] = f32x4{__uint_as_float(pb.x << 16), __uint_as_float(pb.x & 0xffff0000u),
+                            __uint_as_float(pb.y << 16), __uint_as_float(pb.y & 0xffff0000u)};
         }
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
@@ -1464,7 +1472,7 @@ __global__ void __launch_bounds__(64 * CNW, 4) k_combine(DecodeArgs a) {
         const int t1 = min(s_len[bl], t0 + s_chunk);
         const size_t ih = (size_t)i * a.H + h;
         recompute_partial(a.pool, a.block_table + (size_t)b * a.max_pages_per_seq,
-                          (const uint16_t*)a.q_abs + ((size_t)b * a.H + h) * RW, a.part_acc + ih * DC,
+                          (const uint16_t*)a.q_abs + ((size_t)b * a.H + h) * RW, a.part_lat + ih * DC,
                           a.part_ml + ih * 2, a.P, a.scale_log2, t0, t1, (float*)lat_hi, red, a.fp8, a.num_pages,
                           a.err);
       }
@@ -1542,14 +1550,13 @@ __global__ void __launch_bounds__(64 * CNW, 4) k_combine(DecodeArgs a) {
 //     row r keeps its 16-byte chunk c in slot c ^ (r % 32).
 //   - Wave w owns latent columns 32 w .. 32 w + 31, one 32-wide k-step of the
 //     16x16x32 product.  Its lane (r, q) = (lane % 16, lane / 16) merges
-//     columns 32 w + 4 q .. +3 and 32 w + 16 + 4 q .. +3 of sequences r and
-//     16 + r over the items in index order (groups of four items, requested
-//     together; a later group rescales the earlier ones).  Those eight
-//     columns are its A fragment of each 16-sequence block: the k order
-//     inside the step is permuted (the B fragments follow it), so that the
-//     four lanes of a sequence read 64 contiguous bytes of a partial in one
-//     instruction.  Every partial of the work-group is requested before the
-//     first wait; the items' (m, L) pairs come through LDS.
+//     columns 32 w + 8 q .. +7 of sequences r and 16 + r over the items in
+//     index order (groups of four items, requested together; a later group
+//     rescales the earlier ones).  Those eight columns are its A fragment of
+//     each 16-sequence block, and one 16-byte load of a bf16 partial: the
+//     four lanes of a sequence read 64 contiguous bytes.  Every partial of
+//     the work-group is requested before the first wait; the items' (m, L)
+//     pairs come through LDS.
 //   - D_w[s][v] = sum over the wave's 32 columns k of lat[s][k] W_UV[h][v][k],
 //     lat as bf16 hi + lo (the pair carries the fp32 value to ~2^-17): two
 //     16-sequence blocks x eight 16-wide v blocks, 32 MFMAs a wave.
@@ -1606,8 +1613,8 @@ __global__ void __launch_bounds__(1024) k_combine_wide(DecodeArgs a) {
   // The partials through buffer resources (32-bit offsets; the host takes this
   // kernel only when both buffers are below 2 GiB): an absent item's loads
   // get an offset past the end and return zeros.
-  const __amdgpu_buffer_rsrc_t acc_rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)a.part_acc, (short)0, (int)((size_t)a.max_items * a.H * DC * sizeof(float)), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t lat_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.part_lat, (short)0, (int)((size_t)a.max_items * a.H * DC * sizeof(uint16_t)), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t ml_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)pml, (short)0, (int)((size_t)a.max_items * a.H * 2 * sizeof(float)), kRawBufferWord3);
   // merge items it0 + j0 .. +3 (those below it1) of both sequences into the
@@ -1616,18 +1623,21 @@ __global__ void __launch_bounds__(1024) k_combine_wide(DecodeArgs a) {
   // FIRST: nothing merged yet (v and L are written, not read).
   auto merge_group = [&](auto first, int j0, f32x4(&v)[2][2], float(&m)[2], float(&l)[2], int& flagged) {
     constexpr bool FIRST = decltype(first)::value;
-    f32x4 ai[2][WNI][2];
+    u32x4 ai[2][WNI];  // eight bf16 latent sums: columns 32 w + 8 q .. +7
 #pragma unroll
     for (int jj = 0; jj < WNI; ++jj)
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         const int i = it0[sb] + j0 + jj;
-        const int off_acc = i < it1[sb] ? 4 * (DC * (i * a.H + h) + 32 * w + 4 * q) : (int)0x80000000;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          ai[sb][jj][u] =
-              __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(acc_rs, off_acc + 64 * u, 0, 0));
+        const int off_lat = i < it1[sb] ? 2 * (DC * (i * a.H + h) + 32 * w + 8 * q) : (int)0x80000000;
+        ai[sb][jj] = __builtin_amdgcn_raw_buffer_load_b128(lat_rs, off_lat, 0, 0);
       }
+    // columns 4 u .. 4 u + 3 of the eight as fp32
+    auto part = [&](int sb, int jj, int u) {
+      const uint32_t x0 = ai[sb][jj][2 * u], x1 = ai[sb][jj][2 * u + 1];
+      return f32x4{__uint_as_float(x0 << 16), __uint_as_float(x0 & 0xffff0000u), __uint_as_float(x1 << 16),
+                   __uint_as_float(x1 & 0xffff0000u)};
+    };
     // (m, L) after the partials: its wait then covers every load of the group
     if (tid < WNI * WCB) {
       const int i = mit0 + j0 + (tid & 3);
@@ -1659,18 +1669,18 @@ __global__ void __launch_bounds__(1024) k_combine_wide(DecodeArgs a) {
       for (int jj = 0; jj < WNI; ++jj) wgt[jj] = any ? exp2f(mi[jj] - mn) : 0.f;
       if constexpr (FIRST) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) v[sb][u] = wgt[0] * ai[sb][0][u];
+        for (int u = 0; u < 2; ++u) v[sb][u] = wgt[0] * part(sb, 0, u);
         l[sb] = wgt[0] * li[0];
       } else {
         const float sc = any ? exp2f(m[sb] - mn) : 0.f;  // 0 while m = -inf
 #pragma unroll
-        for (int u = 0; u < 2; ++u) v[sb][u] = sc * v[sb][u] + wgt[0] * ai[sb][0][u];
+        for (int u = 0; u < 2; ++u) v[sb][u] = sc * v[sb][u] + wgt[0] * part(sb, 0, u);
         l[sb] = sc * l[sb] + wgt[0] * li[0];
       }
 #pragma unroll
       for (int jj = 1; jj < WNI; ++jj) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) v[sb][u] += wgt[jj] * ai[sb][jj][u];
+        for (int u = 0; u < 2; ++u) v[sb][u] += wgt[jj] * part(sb, jj, u);
         l[sb] += wgt[jj] * li[jj];
       }
       m[sb] = mn;
@@ -1699,7 +1709,7 @@ __global__ void __launch_bounds__(1024) k_combine_wide(DecodeArgs a) {
         const int t0 = (i - i0) * chunk;
         const int t1 = min(len, t0 + chunk);
         recompute_partial(a.pool, a.block_table + (size_t)(b0 + b) * a.max_pages_per_seq,
-                          (const uint16_t*)a.q_abs + ((size_t)(b0 + b) * a.H + h) * RW, a.part_acc + ih * DC,
+                          (const uint16_t*)a.q_abs + ((size_t)(b0 + b) * a.H + h) * RW, a.part_lat + ih * DC,
                           a.part_ml + ih * 2, a.P, a.scale_log2, t0, t1, scr, red, a.fp8, a.num_pages, a.err);
       }
     }
@@ -1710,7 +1720,7 @@ __global__ void __launch_bounds__(1024) k_combine_wide(DecodeArgs a) {
   }
 
   // lat = v / L as bf16 hi + lo: the A fragments (row = sequence r16 of block
-  // sb; its eight k slots hold columns 32 w + 4 q .. +3, 32 w + 16 + 4 q .. +3)
+  // sb; its eight k slots hold columns 32 w + 8 q .. +7)
   u32x4 ahi[2], alo[2];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
@@ -1734,16 +1744,12 @@ __global__ void __launch_bounds__(1024) k_combine_wide(DecodeArgs a) {
   __syncthreads();                            // and every other wave's
 
   // D_w: B = W_UV^T fragment (column v = 16 vb + lane % 16, the same eight
-  // columns as the A slots): 8 bytes from chunk 4 w + q / 2 and 8 from chunk
-  // 4 w + 2 + q / 2 of row 16 vb + lane % 16, half q % 2 of each
+  // columns as the A slots): chunk 4 w + q of row 16 vb + lane % 16
   f32x4 acc[2][8];
 #pragma unroll
   for (int vb = 0; vb < 8; ++vb) {
     const int row = 16 * vb + r16;
-    const char* rp = smem + row * DC * 2 + 8 * (q & 1);
-    const uint2 b0w = *(const uint2*)(rp + (((4 * w + (q >> 1)) ^ (row & 31)) << 4));
-    const uint2 b1w = *(const uint2*)(rp + (((4 * w + 2 + (q >> 1)) ^ (row & 31)) << 4));
-    const u32x4 bw = u32x4{b0w.x, b0w.y, b1w.x, b1w.y};
+    const u32x4 bw = *(const u32x4*)(smem + row * DC * 2 + (((4 * w + q) ^ (row & 31)) << 4));
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       acc[sb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi[sb]), as_bf16x8(bw),
@@ -1824,7 +1830,7 @@ hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.d_v == 128 && (long long)a.H * ((a.batch + WCB - 1) / WCB) >= a.slots &&
-      (long long)a.max_items * a.H * DC * (long long)sizeof(float) < (1LL << 31))
+      (long long)a.max_items * a.H * DC * (long long)sizeof(uint16_t) < (1LL << 31))
     hipLaunchKernelGGL(k_combine_wide, dim3(a.H, (a.batch + WCB - 1) / WCB), dim3(1024), 0, s, a);
   else if ((long long)a.H * ((a.batch + 15) / 16) >= 2LL * a.slots)
     hipLaunchKernelGGL((k_combine<16, 2>), dim3(a.H, (a.batch + 15) / 16), dim3(64 * CNW), 0, s, a);

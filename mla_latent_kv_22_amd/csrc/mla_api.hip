@@ -88,6 +88,9 @@ bool decode_fast(const mla_dims_t* d, int batch) {
          decode_mfma_supported(d->num_heads, d->d_c, d->d_r, d->v_head, d->page_size, batch);
 }
 
+// Bytes per partial latent sum: bf16 on the MFMA path, fp32 on the plain one.
+size_t partial_elem_bytes(const mla_dims_t* d, int batch) { return decode_fast(d, batch) ? 2 : sizeof(float); }
+
 struct DecodeLayout {
   int slots, max_items;
   size_t acc_bytes, ml_bytes, plan_bytes;
@@ -103,7 +106,7 @@ bool decode_layout(const mla_dims_t* d, int batch, int max_seq_len, DecodeLayout
   const long long by_len = ((long long)batch * max_seq_len + kMaxChunk - 1) / kMaxChunk;
   const long long base = (long long)kMaxChunksPerSlot * L.slots;
   L.max_items = (int)((by_len > base ? by_len : base) + batch);
-  L.acc_bytes = (size_t)L.max_items * d->num_heads * d->d_c * sizeof(float);
+  L.acc_bytes = (size_t)L.max_items * d->num_heads * d->d_c * partial_elem_bytes(d, batch);
   L.acc_bytes = (L.acc_bytes + 255) & ~(size_t)255;
   L.ml_bytes = (size_t)L.max_items * d->num_heads * 2 * sizeof(float);
   L.ml_bytes = (L.ml_bytes + 255) & ~(size_t)255;
@@ -159,6 +162,7 @@ int decode_launch(const mla_dims_t* dims, const void* q_abs, const void* pool, i
   a.out = out;
   a.lse = lse;
   a.part_acc = (float*)ws;
+  a.part_lat = (uint16_t*)ws;
   a.part_ml = (float*)(ws + L.acc_bytes);
   a.plan = (int*)(ws + L.acc_bytes + L.ml_bytes);
   a.batch = batch;
@@ -173,7 +177,7 @@ int decode_launch(const mla_dims_t* dims, const void* q_abs, const void* pool, i
   a.max_items = L.max_items;
   a.min_chunk = decode_fast(dims, batch) ? 256 : 32;  // the plain kernels work a token at a time per lane
   // partial (m, l, acc) written and read back, in cache-row equivalents
-  a.ovh_tokens = (int)((2.0 * dims->num_heads * (dims->d_c + 2) * 4.0) /
+  a.ovh_tokens = (int)((2.0 * dims->num_heads * (dims->d_c * (double)partial_elem_bytes(dims, batch) + 8.0)) /
                        ((double)(dims->d_c + dims->d_r) * cache_elem_bytes(dims)));
   a.scale_log2 = dims->softmax_scale * kLog2e;
   a.fp8 = fp8_cache(dims) ? 1 : 0;
@@ -211,7 +215,7 @@ char* scratch_address() {
 // see make_decode_plan) does not fit.
 int decode_layout_in(const mla_dims_t* d, int batch, int max_seq_len, size_t bytes, DecodeLayout& L) {
   if (!decode_layout(d, batch, max_seq_len, L)) return MLA_ERR_HIP;
-  const size_t per_item = (size_t)d->num_heads * ((size_t)d->d_c + 2) * sizeof(float);
+  const size_t per_item = (size_t)d->num_heads * ((size_t)d->d_c * partial_elem_bytes(d, batch) + 2 * sizeof(float));
   const size_t fixed = L.plan_bytes + 512;  // plan, and the 256-byte roundings of the two arrays
   if (bytes <= fixed) return MLA_ERR_WORKSPACE;
   const long long cap = (long long)((bytes - fixed) / per_item);
@@ -220,7 +224,7 @@ int decode_layout_in(const mla_dims_t* d, int batch, int max_seq_len, size_t byt
   if (need > cap) return MLA_ERR_WORKSPACE;
   if (cap < L.max_items) {
     L.max_items = (int)cap;
-    L.acc_bytes = ((size_t)L.max_items * d->num_heads * d->d_c * sizeof(float) + 255) & ~(size_t)255;
+    L.acc_bytes = ((size_t)L.max_items * d->num_heads * d->d_c * partial_elem_bytes(d, batch) + 255) & ~(size_t)255;
     L.ml_bytes = ((size_t)L.max_items * d->num_heads * 2 * sizeof(float) + 255) & ~(size_t)255;
   }
   return L.total() <= bytes ? MLA_OK : MLA_ERR_WORKSPACE;

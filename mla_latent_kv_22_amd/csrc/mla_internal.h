@@ -47,7 +47,8 @@ struct DecodeArgs {
   const void* w_uv;
   void* out;
   float* lse;
-  float* part_acc;  // [max_items, H, d_c]
+  float* part_acc;  // [max_items, H, d_c] fp32 (plain kernels)
+  uint16_t* part_lat;  // [max_items, H, d_c] bf16, the same buffer (MFMA kernels)
   float* part_ml;   // [max_items, H, 2]  (reference max in log2 units, sum)
   int* plan;        // [2 batch + 2]: first item per sequence (batch + 1), lengths, chunk
   int batch, H, d_c, d_r, d_v, P, max_pages_per_seq;
