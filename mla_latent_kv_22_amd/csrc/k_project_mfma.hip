@@ -668,17 +668,18 @@ __device__ __forceinline__ void absorb_head16(const AbsorbArgs& a, int h, char* 
   }
 }
 
-// Work-group x < nfb S: split-K write tile (x % nfb, x / nfb); otherwise heads
-// x - nfb S, x - nfb S + n_ablocks, ... of the absorption.
+// Work-group roles as wa_role (mla_checks.h) deals them: split-K write
+// tiles grouped by XCD, then absorption heads rank, rank + n_ablocks, ...
 __global__ void __launch_bounds__(1024, 1) k_write_absorb(WriteCacheArgs wa, AbsorbArgs aa, WriteSplit ws,
                                                           int n_ablocks) {
   __shared__ __attribute__((aligned(16))) char smem[WA_LDS];
-  const int x = blockIdx.x, n_wblocks = ws.nfb * ws.S;
-  if (x < n_wblocks) {
-    write_split_tile(wa, ws, x % ws.nfb, x / ws.nfb, smem);
+  const WaRole role = wa_role(blockIdx.x, ws.S, ws.nfb);
+  if (role.write) {
+    write_split_tile(wa, ws, role.fb, role.s, smem);
     return;
   }
-  for (int h = x - n_wblocks; h < aa.H; h += n_ablocks) {
+  const int rank = role.rank;
+  for (int h = rank; h < aa.H; h += n_ablocks) {
     absorb_head16(aa, h, smem);
     __syncthreads();  // the next head reuses the LDS
   }
@@ -712,7 +713,8 @@ hipError_t write_absorb_mfma(const WriteCacheArgs& wa, const AbsorbArgs& aa, voi
   int n_ablocks = cus - n_wblocks;
   if (n_ablocks > aa.H) n_ablocks = aa.H;
   if (n_ablocks < (aa.H + 1) / 2) n_ablocks = (aa.H + 1) / 2;  // at most two heads per work-group
-  hipLaunchKernelGGL(k_write_absorb, dim3(n_wblocks + n_ablocks), dim3(1024), 0, s, wa, aa, ws, n_ablocks);
+  const int grid = wa_grid(ws.S, ws.nfb, n_ablocks);
+  hipLaunchKernelGGL(k_write_absorb, dim3(grid), dim3(1024), 0, s, wa, aa, ws, n_ablocks);
   return hipGetLastError();
 }
 

@@ -97,4 +97,49 @@ MLA_HD int key_position(int n, int seq_start, int max_kv_len, int* err) {
   return clamp_report<CHECK>(n - seq_start, 0, max_kv_len - 1, err);
 }
 
+// Block map of the fused cache write + absorption launch (k_write_absorb).
+// Work-group x runs on XCD x % 8.  The S split-K slices of the hidden axis
+// are dealt to the XCDs in turn (slice s on XCD s % 8), and the first
+// nfb * (slices of XCD c) work-groups of XCD c are the write tiles of its
+// slices, so the nfb tiles that read the same h columns share one L2.  Every
+// other work-group is an absorption work-group; its rank counts the
+// absorption work-groups below it.
+MLA_HD int wa_xcd_slices(int c, int S) { return c < S ? (S - 1 - c) / 8 + 1 : 0; }
+
+struct WaRole {
+  bool write;
+  int fb, s;  // write tile: feature block, slice
+  int rank;   // absorption work-group: heads rank, rank + n_ablocks, ...
+};
+MLA_HD WaRole wa_role(int x, int S, int nfb) {
+  WaRole r{false, 0, 0, 0};
+  const int c = x & 7, j = x >> 3;
+  if (j < nfb * wa_xcd_slices(c, S)) {
+    r.write = true;
+    r.fb = j % nfb;
+    r.s = c + 8 * (j / nfb);
+    return r;
+  }
+  for (int cc = 0; cc < 8; ++cc) {
+    const int below = x > cc ? (x - cc + 7) / 8 : 0;  // work-groups x' < x on XCD cc
+    const int w = nfb * wa_xcd_slices(cc, S);
+    r.rank += below > w ? below - w : 0;
+  }
+  return r;
+}
+
+// Grid of the launch: at least nfb * S write tiles plus n_ablocks (>= 1)
+// absorption work-groups, and far enough for the last write tile of every
+// XCD (the j-th work-group of XCD c is 8 j + c).  n_ablocks becomes the
+// grid's absorption work-group count.
+MLA_HD int wa_grid(int S, int nfb, int& n_ablocks) {
+  int grid = nfb * S + n_ablocks;
+  for (int c = 0; c < 8; ++c) {
+    const int tiles = nfb * wa_xcd_slices(c, S);
+    if (tiles > 0 && grid < 8 * (tiles - 1) + c + 1) grid = 8 * (tiles - 1) + c + 1;
+  }
+  n_ablocks = grid - nfb * S;
+  return grid;
+}
+
 }  // namespace mla

@@ -23,3 +23,21 @@ def test_check_predicates_on_host(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
     v, n = r.stdout.split()[1], r.stdout.split()[3]
     assert int(v) == 0 and int(n) > 1_000_000, r.stdout
+
+
+BLOCKMAP = os.path.join(ROOT, "tests", "host", "blockmap_driver.cpp")
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_write_absorb_block_map_on_host(tmp_path):
+    """The fused write + absorption launch deals its work-groups to roles by
+    XCD (mla_checks.h wa_role / wa_grid): every write tile, absorption rank
+    and head exactly once, at most two heads per work-group, for every grid
+    the host can form."""
+    exe = str(tmp_path / "blockmap")
+    r = subprocess.run(["g++", "-O2", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", BLOCKMAP, "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert int(r.stdout.split()[1]) == 0 and int(r.stdout.split()[3]) > 100_000, r.stdout
