@@ -1783,6 +1783,159 @@ __global__ void __launch_bounds__(1024) k_combine_wide(DecodeArgs a) {
   }
 }
 
+// --------------------------------------------------------------------------
+// combine, one work-group per (head, sequence), for launches with few such
+// pairs (H * batch <= 2 CUs, d_v = 128; the few-heads shapes): 256 threads.
+//   - Each thread requests its half row of W_UV,h at once, straight into
+//     registers (row t / 2, columns 256 (t % 2) .. +255: 32 16-byte loads,
+//     issued after the partial loads so that the merge waits only for those).
+//   - Wave s merges items it0 + s, it0 + s + 4, ... of the sequence in that
+//     order; lane l holds latent columns 8 l .. 8 l + 7 (one 16-byte load of
+//     a bf16 partial per item) and the running (m, L) of its set.  The four
+//     sets then meet in LDS in set order (a fixed order: the result does not
+//     depend on page placement).
+//   - o[v] = sum_c W_UV[h][v][c] lat[c] in fp32 on the VALU: each thread its
+//     half row against the merged latent in LDS, the two halves added by the
+//     pair of lanes.  (One sequence per work-group: an MFMA block would be
+//     1/16 used.)
+constexpr int SNT = 256;  // threads per work-group
+__global__ void __launch_bounds__(SNT) k_combine_seq(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) float s_v[4][DC];  // per-set partial sums, then the merged latent
+  __shared__ float s_m[4], s_l[4];
+  __shared__ __attribute__((aligned(16))) float scr[RW + SNT];  // recompute_partial scratch
+  __shared__ int red[16];
+  const int h = blockIdx.x % a.H, b = blockIdx.x / a.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int set = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int it0 = a.plan[b], it1 = a.plan[b + 1];
+  const uint16_t* __restrict__ plat = a.part_lat;
+  const float* __restrict__ pml = a.part_ml;
+
+  // items i0, i0 + 4, i0 + 8, i0 + 12 of this wave's set (those below it1)
+  auto load_group = [&](int i0, u32x4 (&pv)[4], f32x2 (&ml)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = i0 + 4 * k;
+      const bool ok = i < it1;
+      const size_t ih = (size_t)(ok ? i : it0) * a.H + h;
+      pv[k] = ok ? *(const u32x4*)(plat + ih * DC + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
+      ml[k] = ok ? *(const f32x2*)(pml + 2 * ih) : f32x2{-INFINITY, 0.f};
+    }
+  };
+  // into the running (v, m, L) in item order; flagged: some m_i = +inf
+  auto merge_group = [&](const u32x4 (&pv)[4], const f32x2 (&ml)[4], f32x4 (&v)[2], float& m, float& l) {
+    int flagged = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      flagged |= ml[k][0] == INFINITY;
+      const float mn = fmaxf(m, ml[k][0]);
+      if (mn == -INFINITY) continue;  // nothing merged yet and an absent item
+      const float sc = exp2f(m - mn), wg = exp2f(ml[k][0] - mn);  // 0 for m = -inf
+      const f32x4 x0 = f32x4{__uint_as_float(pv[k][0] << 16), __uint_as_float(pv[k][0] & 0xffff0000u),
+                             __uint_as_float(pv[k][1] << 16), __uint_as_float(pv[k][1] & 0xffff0000u)};
+      const f32x4 x1 = f32x4{__uint_as_float(pv[k][2] << 16), __uint_as_float(pv[k][2] & 0xffff0000u),
+                             __uint_as_float(pv[k][3] << 16), __uint_as_float(pv[k][3] & 0xffff0000u)};
+      v[0] = sc * v[0] + wg * x0;
+      v[1] = sc * v[1] + wg * x1;
+      l = sc * l + wg * ml[k][1];
+      m = mn;
+    }
+    return flagged;
+  };
+  auto merge_rest = [&](int first, f32x4 (&v)[2], float& m, float& l) {
+    int flagged = 0;
+    for (int i0 = first; i0 < it1; i0 += 16) {
+      u32x4 pv[4];
+      f32x2 ml[4];
+      load_group(i0, pv, ml);
+      flagged |= merge_group(pv, ml, v, m, l);
+    }
+    return flagged;
+  };
+
+  f32x4 v[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  float m = -INFINITY, l = 0.f;
+  u32x4 wrow[32];
+  int flagged;
+  {
+    // the first group of partials, then this thread's W_UV,h half row: the
+    // merge of the group waits for its own loads only (in-order counting)
+    u32x4 pv[4];
+    f32x2 ml[4];
+    load_group(it0 + set, pv, ml);
+    const uint16_t* wp = (const uint16_t*)a.w_uv + ((size_t)h * 128 + (tid >> 1)) * DC + 256 * (tid & 1);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) wrow[k] = *(const u32x4*)(wp + 8 * k);
+    flagged = merge_group(pv, ml, v, m, l);
+    flagged |= merge_rest(it0 + set + 16, v, m, l);
+  }
+  if (__syncthreads_or(flagged)) {
+    // a flagged partial (m = +inf): recompute it exactly, then merge again
+    const int chunk = a.plan[2 * a.batch + 1];
+    const int len = a.plan[a.batch + 1 + b];
+    for (int i = it0; i < it1; ++i) {
+      const size_t ih = (size_t)i * a.H + h;
+      if (pml[ih * 2] != INFINITY) continue;  // same value in every thread
+      const int t0 = (i - it0) * chunk;
+      const int t1 = min(len, t0 + chunk);
+      recompute_partial(a.pool, a.block_table + (size_t)b * a.max_pages_per_seq,
+                        (const uint16_t*)a.q_abs + ((size_t)b * a.H + h) * RW, a.part_lat + ih * DC,
+                        a.part_ml + ih * 2, a.P, a.scale_log2, t0, t1, scr, red, a.fp8, a.num_pages, a.err);
+    }
+    __syncthreads();
+    // merge again (recomputed partials are finite)
+    v[0] = v[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+    merge_rest(it0 + set, v, m, l);
+  }
+  *(f32x4*)(&s_v[set][8 * lane]) = v[0];
+  *(f32x4*)(&s_v[set][8 * lane + 4]) = v[1];
+  if (lane == 0) {
+    s_m[set] = m;
+    s_l[set] = l;
+  }
+  __syncthreads();
+  // the four sets in order: lat[c] = sum_s 2^(m_s - M) v_s[c] / L
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) M = fmaxf(M, s_m[k]);
+  float wk[4], L = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    wk[k] = M == -INFINITY ? 0.f : exp2f(s_m[k] - M);
+    L += wk[k] * s_l[k];
+  }
+  const float il = L > 0.f ? 1.f / L : 0.f;
+  float lat[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = tid + SNT * u;
+    float x = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x += wk[k] * s_v[k][c];
+    lat[u] = x * il;
+  }
+  if (tid == 0 && a.lse) a.lse[(size_t)b * a.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  __syncthreads();  // every set sum is read: row 0 of s_v takes the merged latent
+#pragma unroll
+  for (int u = 0; u < 2; ++u) s_v[0][tid + SNT * u] = lat[u];
+  __syncthreads();
+  const float* lv = &s_v[0][256 * (tid & 1)];
+  float o = 0.f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const f32x4 l0 = *(const f32x4*)(lv + 8 * k), l1 = *(const f32x4*)(lv + 8 * k + 4);
+    const u32x4 wv = wrow[k];
+    o += __uint_as_float(wv[0] << 16) * l0[0] + __uint_as_float(wv[0] & 0xffff0000u) * l0[1] +
+         __uint_as_float(wv[1] << 16) * l0[2] + __uint_as_float(wv[1] & 0xffff0000u) * l0[3] +
+         __uint_as_float(wv[2] << 16) * l1[0] + __uint_as_float(wv[2] & 0xffff0000u) * l1[1] +
+         __uint_as_float(wv[3] << 16) * l1[2] + __uint_as_float(wv[3] & 0xffff0000u) * l1[3];
+  }
+  o += __shfl_xor(o, 1);
+  if ((tid & 1) == 0) ((uint16_t*)a.out)[((size_t)b * a.H + h) * 128 + (tid >> 1)] = f32_to_bf16(o);
+}
+
 }  // namespace
 
 bool decode_mfma_supported(int H, int d_c, int d_r, int d_v, int P, int batch) {
@@ -1832,6 +1985,8 @@ hipError_t decode_mfma(const DecodeArgs& a, hipStream_t s) {
   if (a.d_v == 128 && (long long)a.H * ((a.batch + WCB - 1) / WCB) >= a.slots &&
       (long long)a.max_items * a.H * DC * (long long)sizeof(uint16_t) < (1LL << 31))
     hipLaunchKernelGGL(k_combine_wide, dim3(a.H, (a.batch + WCB - 1) / WCB), dim3(1024), 0, s, a);
+  else if (a.d_v == 128 && (long long)a.H * a.batch <= 2LL * a.slots)
+    hipLaunchKernelGGL(k_combine_seq, dim3(a.H * a.batch), dim3(SNT), 0, s, a);
   else if ((long long)a.H * ((a.batch + 15) / 16) >= 2LL * a.slots)
     hipLaunchKernelGGL((k_combine<16, 2>), dim3(a.H, (a.batch + 15) / 16), dim3(64 * CNW), 0, s, a);
   else
