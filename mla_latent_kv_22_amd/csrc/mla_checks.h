@@ -97,6 +97,62 @@ MLA_HD int key_position(int n, int seq_start, int max_kv_len, int* err) {
   return clamp_report<CHECK>(n - seq_start, 0, max_kv_len - 1, err);
 }
 
+// Tokens per work item of the decode's split pass.  items(ch) must return
+// the item count at chunk ch: the sum over sequences of ceil(len / ch).  Work
+// item i runs in round i / slots of its work-group, so a plan costs
+//   rounds * chunk  (tokens of the busiest work-group)  +  items * ovh / slots
+// (the partial results written and merged, in cache-row equivalents).
+// Candidates:
+//   - chunk = total / (k slots) for k = 1, 2, 4 (rounded up to 32): the k = 1
+//     plan always fits the partial buffers (items <= slots + batch);
+//   - when the best of those leaves the busiest work-group more than 5% (and
+//     a tile) above the mean, for r = 2 .. 4 rounds the chunk that makes the
+//     items fit r * slots: estimated as total / (r slots - batch / 2) (each
+//     sequence's last item is on average half a chunk short) and raised at
+//     most three times by the ratio of items to r * slots.
+// Every chunk is a multiple of 32 in [min_chunk, max_chunk], and no plan with
+// more than max_items items is taken.  The result depends only on the
+// arguments and items(), so every work-group computes the same plan.
+template <class Items>
+MLA_HD int choose_chunk(long long total, int batch, int slots, int min_chunk, int max_chunk, int ovh_tokens,
+                        int max_items, Items items) {
+  int best_chunk = 0;
+  long long best_cost = -1, best_work = 0;
+  auto round32 = [&](long long c) {
+    c = ((c + 31) / 32) * 32;
+    return (int)(c < min_chunk ? min_chunk : (c > max_chunk ? max_chunk : c));
+  };
+  auto consider = [&](int ch, long long it, bool always) {
+    if (!always && it > max_items) return;
+    const long long rounds = (it + slots - 1) / slots;
+    const long long cost = rounds * ch + (it * ovh_tokens) / slots;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_chunk = ch;
+      best_work = rounds * ch;
+    }
+  };
+  for (int k = 1; k <= 4; k <<= 1) {
+    const int ch = round32((total + (long long)k * slots - 1) / ((long long)k * slots));
+    consider(ch, items(ch), k == 1);
+  }
+  const long long mean = (total + slots - 1) / slots;
+  if (best_work > mean + mean / 20 + 32) {
+    for (int r = 2; r <= 4; ++r) {
+      const long long cap = (long long)r * slots;
+      const long long den = cap - batch / 2 > cap / 2 ? cap - batch / 2 : cap / 2;
+      int ch = round32((total + den - 1) / den);
+      long long it = items(ch);
+      for (int t = 0; t < 3 && it > cap && ch < max_chunk; ++t) {
+        ch = round32(((long long)ch * it + cap - 1) / cap);
+        it = items(ch);
+      }
+      if (it <= cap) consider(ch, it, false);
+    }
+  }
+  return best_chunk;
+}
+
 // Block map of the fused cache write + absorption launch (k_write_absorb).
 // Work-group x runs on XCD x % 8.  The S split-K slices of the hidden axis
 // are dealt to the XCDs in turn (slice s on XCD s % 8), and the first

@@ -174,24 +174,14 @@ __device__ inline DecodePlan make_decode_plan(const int32_t* __restrict__ seq_le
       part += L;
     }
     const long long total = wave_sum_ll(part);
-    int best_chunk = 0;
-    long long best_cost = -1;
-    for (int k = 1; k <= 4; k <<= 1) {
-      const long long denom = (long long)k * slots;
-      long long chl = (total + denom - 1) / denom;
-      chl = ((chl + 31) / 32) * 32;
-      int ch = (int)(chl < min_chunk ? min_chunk : (chl > max_chunk ? max_chunk : chl));
-      long long it = 0;
-      for (int b = lane; b < batch; b += 64) it += (s_len[b] + ch - 1) / ch;  // this lane's own entries
-      it = wave_sum_ll(it);
-      if (k > 1 && it > max_items) continue;
-      const long long rounds = (it + slots - 1) / slots;
-      const long long cost = rounds * ch + (it * ovh_tokens) / slots;
-      if (best_cost < 0 || cost < best_cost) {
-        best_cost = cost;
-        best_chunk = ch;
-      }
-    }
+    // items at chunk ch: this lane's own entries, summed over the wave
+    // (the lengths were written above by the same lanes)
+    const int best_chunk =
+        choose_chunk(total, batch, slots, min_chunk, max_chunk, ovh_tokens, max_items, [&](int ch) {
+          long long it = 0;
+          for (int b = lane; b < batch; b += 64) it += (s_len[b] + ch - 1) / ch;
+          return wave_sum_ll(it);
+        });
     // exclusive prefix of item counts: lane l owns the contiguous run of
     // sequences [l per, l per + per); LDS operations of one wave complete in
     // order, so the lengths written above are visible here
