@@ -357,7 +357,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split(DecodeArgs a) {
 
   const int cap = a.len_cap;
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
-                                           a.ovh_tokens, s_len, s_items, red, a.err, a.max_items);
+                                           a.ovh_tokens, a.round_ovh_tokens, s_len, s_items, red, a.err, a.max_items);
   const int n_items = plan.n_items;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // work-group 0 publishes the plan for the combine pass:
@@ -619,7 +619,7 @@ __global__ void __launch_bounds__(256, 1) k_split16(DecodeArgs a) {
 
   const int cap = a.len_cap;
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
-                                           a.ovh_tokens, s_len, s_items, red, a.err, a.max_items);
+                                           a.ovh_tokens, a.round_ovh_tokens, s_len, s_items, red, a.err, a.max_items);
   const int n_items = plan.n_items;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (blockIdx.x == 0) {
@@ -1085,7 +1085,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_split8(DecodeArgs a) {
 
   const int cap = a.len_cap;
   const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk,
-                                           a.ovh_tokens, s_len, s_items, red, a.err, a.max_items);
+                                           a.ovh_tokens, a.round_ovh_tokens, s_len, s_items, red, a.err, a.max_items);
   const int n_items = plan.n_items;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (blockIdx.x == 0) {

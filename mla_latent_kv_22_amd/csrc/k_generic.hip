@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(64) k_decode_split(DecodeArgs a) {
   const RowT** rows = (const RowT**)(acc + a.d_c + (a.d_c & 1));  // 8-byte aligned: all sizes above are ints
 
   const int cap = a.len_cap;
-  const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk, a.ovh_tokens,
+  const DecodePlan plan = make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk, a.ovh_tokens, a.round_ovh_tokens,
                                            s_len, s_items, red, a.err, a.max_items);
   const int item = blockIdx.x;
   if (item >= plan.n_items) return;
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(128) k_decode_combine(DecodeArgs a) {
   float* stat = lat + a.d_c;  // m*, 1/L
 
   const int cap = a.len_cap;
-  make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk, a.ovh_tokens, s_len, s_items, red, a.err, a.max_items);
+  make_decode_plan(a.seq_lens, a.batch, cap, a.slots, a.min_chunk, kMaxChunk, a.ovh_tokens, a.round_ovh_tokens, s_len, s_items, red, a.err, a.max_items);
   const int b = blockIdx.x, h = blockIdx.y;
   const int i0 = s_items[b], i1 = s_items[b + 1];
   T* out = (T*)a.out + ((size_t)b * a.H + h) * a.d_v;

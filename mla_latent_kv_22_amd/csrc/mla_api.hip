@@ -179,6 +179,11 @@ int decode_launch(const mla_dims_t* dims, const void* q_abs, const void* pool, i
   // partial (m, l, acc) written and read back, in cache-row equivalents
   a.ovh_tokens = (int)((2.0 * dims->num_heads * (dims->d_c * (double)partial_elem_bytes(dims, batch) + 8.0)) /
                        ((double)(dims->d_c + dims->d_r) * cache_elem_bytes(dims)));
+  // a round of items: the query fragments of its item (H rows' worth) and
+  // the chip-wide pipeline fill and partial stores every work-group meets at
+  // once, measured at about 20-30 us per extra round on 128 long ragged
+  // sequences at H = 128 (some 500-700 rows of streaming per CU)
+  a.round_ovh_tokens = dims->num_heads + 512;
   a.scale_log2 = dims->softmax_scale * kLog2e;
   a.fp8 = fp8_cache(dims) ? 1 : 0;
   a.num_pages = num_pages;

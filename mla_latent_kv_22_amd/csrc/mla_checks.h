@@ -100,13 +100,17 @@ MLA_HD int key_position(int n, int seq_start, int max_kv_len, int* err) {
 // Tokens per work item of the decode's split pass.  items(ch) must return
 // the item count at chunk ch: the sum over sequences of ceil(len / ch).  Work
 // item i runs in round i / slots of its work-group, so a plan costs
-//   rounds * chunk  (tokens of the busiest work-group)  +  items * ovh / slots
-// (the partial results written and merged, in cache-row equivalents).
+//   rounds * (chunk + round_ovh)  +  items * ovh / slots
+// in cache-row equivalents: the tokens of the busiest work-group, what a
+// round costs besides its tokens (the item's query fragments and pipeline
+// fill, which every work-group meets at the same time), and the partial
+// results written and merged.
 // Candidates:
 //   - chunk = total / (k slots) for k = 1, 2, 4 (rounded up to 32): the k = 1
 //     plan always fits the partial buffers (items <= slots + batch);
 //   - when the best of those leaves the busiest work-group more than 5% (and
-//     a tile) above the mean, for r = 2 .. 4 rounds the chunk that makes the
+//     a tile) above the mean and the batch has at most 2 slots sequences
+//     (long contexts, not many short ones), for r = 2 .. 4 rounds the chunk that makes the
 //     items fit r * slots: estimated as total / (r slots - batch / 2) (each
 //     sequence's last item is on average half a chunk short) and raised at
 //     most three times by the ratio of items to r * slots.
@@ -115,7 +119,7 @@ MLA_HD int key_position(int n, int seq_start, int max_kv_len, int* err) {
 // arguments and items(), so every work-group computes the same plan.
 template <class Items>
 MLA_HD int choose_chunk(long long total, int batch, int slots, int min_chunk, int max_chunk, int ovh_tokens,
-                        int max_items, Items items) {
+                        int round_ovh, int max_items, Items items) {
   int best_chunk = 0;
   long long best_cost = -1, best_work = 0;
   auto round32 = [&](long long c) {
@@ -125,7 +129,7 @@ MLA_HD int choose_chunk(long long total, int batch, int slots, int min_chunk, in
   auto consider = [&](int ch, long long it, bool always) {
     if (!always && it > max_items) return;
     const long long rounds = (it + slots - 1) / slots;
-    const long long cost = rounds * ch + (it * ovh_tokens) / slots;
+    const long long cost = rounds * (ch + round_ovh) + (it * ovh_tokens) / slots;
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
       best_chunk = ch;
@@ -137,7 +141,7 @@ MLA_HD int choose_chunk(long long total, int batch, int slots, int min_chunk, in
     consider(ch, items(ch), k == 1);
   }
   const long long mean = (total + slots - 1) / slots;
-  if (best_work > mean + mean / 20 + 32) {
+  if (best_work > mean + mean / 20 + 32 && batch <= 2 * slots) {
     for (int r = 2; r <= 4; ++r) {
       const long long cap = (long long)r * slots;
       const long long den = cap - batch / 2 > cap / 2 ? cap - batch / 2 : cap / 2;

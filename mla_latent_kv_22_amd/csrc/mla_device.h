@@ -163,7 +163,8 @@ __device__ __forceinline__ long long wave_sum_ll(long long v) {
 }
 
 __device__ inline DecodePlan make_decode_plan(const int32_t* __restrict__ seq_lens, int batch, int cap,
-                                              int slots, int min_chunk, int max_chunk, int ovh_tokens, int* s_len,
+                                              int slots, int min_chunk, int max_chunk, int ovh_tokens, int round_ovh,
+                                              int* s_len,
                                               int* s_items, int* red, int* err, int max_items) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -177,7 +178,7 @@ __device__ inline DecodePlan make_decode_plan(const int32_t* __restrict__ seq_le
     // items at chunk ch: this lane's own entries, summed over the wave
     // (the lengths were written above by the same lanes)
     const int best_chunk =
-        choose_chunk(total, batch, slots, min_chunk, max_chunk, ovh_tokens, max_items, [&](int ch) {
+        choose_chunk(total, batch, slots, min_chunk, max_chunk, ovh_tokens, round_ovh, max_items, [&](int ch) {
           long long it = 0;
           for (int b = lane; b < batch; b += 64) it += (s_len[b] + ch - 1) / ch;
           return wave_sum_ll(it);

@@ -56,6 +56,7 @@ struct DecodeArgs {
   int slots;        // concurrent work-groups the split kernel can hold
   int max_items;    // capacity of the partial buffers
   int min_chunk, ovh_tokens;
+  int round_ovh_tokens;  // planner: what a round costs besides its tokens, in cache rows
   float scale_log2; // softmax_scale * log2(e)
   int fp8;          // 1: 8-bit pool (E4M3 rows + float32 row scales per page)
   int num_pages;

@@ -5,7 +5,7 @@
 // every chosen chunk must be a multiple of 32 within [min_chunk, max_chunk],
 // give at most max_items items, and cost no more under the planner's cost
 // model than the best of the three k-candidates alone.  Prints "violations N
-// cases M".  Mode "plan SLOTS MIN OVH": reads lengths from stdin and prints
+// cases M".  Mode "plan SLOTS MIN OVH ROVH": reads lengths from stdin and prints
 // "chunk items rounds" for them.
 #include <stdio.h>
 #include <string.h>
@@ -24,7 +24,7 @@ static long long items_of(const std::vector<int>& L, int ch) {
 }
 
 // the k-candidates alone (chunk = total / (k slots), k = 1, 2, 4)
-static long long base_cost(const std::vector<int>& L, long long total, int slots, int mn, int mx, int ovh,
+static long long base_cost(const std::vector<int>& L, long long total, int slots, int mn, int mx, int ovh, int rovh,
                            int max_items) {
   long long best = -1;
   for (int k = 1; k <= 4; k <<= 1) {
@@ -33,7 +33,7 @@ static long long base_cost(const std::vector<int>& L, long long total, int slots
     const int ch = (int)(c < mn ? mn : (c > mx ? mx : c));
     const long long it = items_of(L, ch);
     if (k > 1 && it > max_items) continue;
-    const long long cost = (it + slots - 1) / slots * ch + it * ovh / slots;
+    const long long cost = (it + slots - 1) / slots * (ch + rovh) + it * ovh / slots;
     if (best < 0 || cost < best) best = cost;
   }
   return best;
@@ -41,8 +41,8 @@ static long long base_cost(const std::vector<int>& L, long long total, int slots
 
 int main(int argc, char** argv) {
   const int kMaxChunk = 8192;
-  if (argc >= 5 && !strcmp(argv[1], "plan")) {
-    const int slots = atoi(argv[2]), mn = atoi(argv[3]), ovh = atoi(argv[4]);
+  if (argc >= 6 && !strcmp(argv[1], "plan")) {
+    const int slots = atoi(argv[2]), mn = atoi(argv[3]), ovh = atoi(argv[4]), rovh = atoi(argv[5]);
     std::vector<int> L;
     long long total = 0;
     int v;
@@ -53,7 +53,7 @@ int main(int argc, char** argv) {
     const int B = (int)L.size();
     const long long by_len = (total + kMaxChunk - 1) / kMaxChunk;
     const int max_items = (int)((by_len > 4LL * slots ? by_len : 4LL * slots) + B);
-    const int ch = choose_chunk(total, B, slots, mn, kMaxChunk, ovh, max_items,
+    const int ch = choose_chunk(total, B, slots, mn, kMaxChunk, ovh, rovh, max_items,
                                 [&](int c) { return items_of(L, c); });
     const long long it = items_of(L, ch);
     printf("%d %lld %lld\n", ch, it, (it + slots - 1) / slots);
@@ -89,19 +89,20 @@ int main(int argc, char** argv) {
           for (int l : L) total += l;
           for (int mn : {32, 256})
             for (int ovh : {0, 229, 457})
+              for (int rovh : {0, 640})
               for (int small = 0; small < 2; ++small) {
                 const long long by_len = (total + kMaxChunk - 1) / kMaxChunk;
                 // the workspace's item capacity, or the smallest a no-alloc layout allows
                 const long long base = by_len > 4LL * slots ? by_len : 4LL * slots;
                 const long long need = (by_len > slots ? by_len : slots) + B;
                 const int max_items = (int)(small ? need : base + B);
-                const int ch = choose_chunk(total, B, slots, mn, kMaxChunk, ovh, max_items,
+                const int ch = choose_chunk(total, B, slots, mn, kMaxChunk, ovh, rovh, max_items,
                                             [&](int c) { return items_of(L, c); });
                 const long long it = items_of(L, ch);
                 expect(ch % 32 == 0 && ch >= mn && ch <= kMaxChunk, "chunk range", B, slots);
                 expect(it <= max_items, "items within capacity", B, slots);
-                const long long cost = (it + slots - 1) / slots * ch + it * ovh / slots;
-                expect(cost <= base_cost(L, total, slots, mn, kMaxChunk, ovh, max_items), "no worse than k-candidates",
+                const long long cost = (it + slots - 1) / slots * (ch + rovh) + it * ovh / slots;
+                expect(cost <= base_cost(L, total, slots, mn, kMaxChunk, ovh, rovh, max_items), "no worse than k-candidates",
                        B, slots);
               }
         }

@@ -67,15 +67,20 @@ def test_decode_chunk_choice_on_host(tmp_path):
 @pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
 def test_decode_chunk_choice_ragged_v3(tmp_path):
     """On the seeded paged ragged workload (B=128, lengths U{512..32768}, 256
-    CUs, 256-token minimum chunk, the bf16 partial overhead) the busiest
-    work-group gets at most 9312 tokens: chunk total/(4 CUs) rounded up would
-    leave 55 work-groups with a fifth round (5 x 2144 = 10720)."""
+    CUs, 256-token minimum chunk, the bf16 partial overhead, a round costing
+    H + 512 rows besides its tokens) the plan takes two rounds of at most
+    4864 tokens: chunk total/(4 CUs) rounded up would leave 55 work-groups
+    with a fifth round (5 x 2144 = 10720 tokens)."""
     import numpy as np
     from mla_latent_kv_22_amd import inputs as I
     lens = I.seq_lengths(I.RAGGED, np.random.default_rng(0))
     ovh = int(2 * 128 * (512 * 2 + 8) / (576 * 2))
-    r = subprocess.run([_build_plan(tmp_path), "plan", "256", "256", str(ovh)], input=" ".join(map(str, lens)),
-                       capture_output=True, text=True, timeout=60)
+    r = subprocess.run([_build_plan(tmp_path), "plan", "256", "256", str(ovh), str(128 + 512)],
+                       input=" ".join(map(str, lens)), capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
     ch, items, rounds = map(int, r.stdout.split())
-    assert ch % 32 == 0 and rounds * ch <= 9312, r.stdout
+    assert ch % 32 == 0 and rounds == 2 and rounds * ch <= 9728, r.stdout
+    # the uniform V3 batch keeps its exact one-round plan
+    r = subprocess.run([_build_plan(tmp_path), "plan", "256", "256", str(ovh), str(128 + 512)],
+                       input=" ".join(["8192"] * 64), capture_output=True, text=True, timeout=60)
+    assert r.stdout.split() == ["2048", "256", "1"], r.stdout
