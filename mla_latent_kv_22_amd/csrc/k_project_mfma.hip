@@ -629,22 +629,26 @@ __device__ __forceinline__ void absorb_head16(const AbsorbArgs& a, int h, char* 
   const int g = lane >> 5, r = lane & 31;
   const int grp = lane >> 4, jl = lane & 15;
   const int tcol = 32 * ws + 16 * (grp & 1) + 4 * (jl & 3);
+  // k-steps outer: each W_UK^T fragment (two transpose reads) serves both
+  // 32-token blocks, and the unrolled loop lets the LDS reads run ahead of
+  // the MFMAs (same operands and k order as before, so the same bits)
   f32x16 acc[AB_T / 32];
 #pragma unroll
-  for (int tb = 0; tb < AB_T / 32; ++tb) {
-    const int trow = 32 * tb + r;
-    acc[tb] = f32x16{};
-#pragma unroll 2
-    for (int ks = 0; ks < DN / 16; ++ks) {
-      const int pc = 2 * ks + g;
+  for (int tb = 0; tb < AB_T / 32; ++tb) acc[tb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < DN / 16; ++ks) {
+    const int pc = 2 * ks + g;
+    const int k0 = 16 * ks + 8 * g;
+    const int j1 = k0 + (jl >> 2), j2 = j1 + 4;
+    const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(wtile + j1 * 256 + 16 * ((tcol >> 3) ^ (2 * (j1 & 3))) + 2 * (tcol & 7)));
+    const s16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(wtile + j2 * 256 + 16 * ((tcol >> 3) ^ (2 * (j2 & 3))) + 2 * (tcol & 7)));
+    const s16x8 bv = s16x8{b1[0], b1[1], b1[2], b1[3], b2[0], b2[1], b2[2], b2[3]};
+#pragma unroll
+    for (int tb = 0; tb < AB_T / 32; ++tb) {
+      const int trow = 32 * tb + r;
       const u32x4 av = *(const u32x4*)(qtile + trow * 256 + 16 * (pc ^ (trow & 7)));
-      const int k0 = 16 * ks + 8 * g;
-      const int j1 = k0 + (jl >> 2), j2 = j1 + 4;
-      const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(wtile + j1 * 256 + 16 * ((tcol >> 3) ^ (2 * (j1 & 3))) + 2 * (tcol & 7)));
-      const s16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(wtile + j2 * 256 + 16 * ((tcol >> 3) ^ (2 * (j2 & 3))) + 2 * (tcol & 7)));
-      const s16x8 bv = s16x8{b1[0], b1[1], b1[2], b1[3], b2[0], b2[1], b2[2], b2[3]};
       acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), __builtin_bit_cast(bf16x8, bv), acc[tb], 0, 0,
                                                         0);
     }
